@@ -1,0 +1,220 @@
+"""Python front end of the CPU oracle (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` use
+this module. It loads ``liboracle.so`` built from ``speed3r_oracle.c`` with plain gcc (no HIP),
+and shares nothing with the GPU library.
+
+Inputs are torch or numpy arrays of bf16 values; they are upcast exactly to float32 before the
+call, and every computation inside runs in float64 (see the C file for the step-by-step
+definition and the pages it follows).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+import time
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "speed3r_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_dbl = ctypes.c_double
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        L.s3r_oracle_pool.argtypes = [_i64, _i32, _i32, _i32, _f32p, _i64, _i64, _f64p]
+        L.s3r_oracle_pool.restype = None
+        L.s3r_oracle_cmp_row.argtypes = [_i64, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f64p,
+                                         _f64p, _i32, _i64, _f64p, _f64p, _f64p]
+        L.s3r_oracle_cmp_row.restype = None
+        L.s3r_oracle_topk.argtypes = [_f32p, _i64, _i32, _i32p]
+        L.s3r_oracle_topk.restype = _i32
+        L.s3r_oracle_sel_row.argtypes = [_i64, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p,
+                                         _i64, _i64, _f32p, _i64, _i64, _i32, _i64, _i32p, _i32,
+                                         _f64p]
+        L.s3r_oracle_sel_row.restype = None
+        L.s3r_oracle_dense_rows.argtypes = [_i64, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p,
+                                            _i64, _i64, _f32p, _i64, _i64, _i32, _i64, _i64,
+                                            _f64p]
+        L.s3r_oracle_dense_rows.restype = None
+        L.s3r_oracle_forward_rows.argtypes = [
+            _i64, _i32, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p, _i64, _i64, _f32p,
+            _i64, _i64, _f64p, _f64p, _f32p, _i64, _i64, _i32p, _i64p,
+            ctypes.c_void_p, _f64p, _f64p, _f32p, _i32p, _f64p, _f64p]
+        L.s3r_oracle_forward_rows.restype = None
+        L.s3r_oracle_num_threads.argtypes = []
+        L.s3r_oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().s3r_oracle_num_threads())
+
+
+def _f32(x) -> np.ndarray:
+    """Exact float32 copy of a [T, H, D] bf16/float tensor (torch or numpy), contiguous."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float32).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def n_blocks(T: int, B: int) -> int:
+    return -(-T // B)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def pool(x, B: int) -> np.ndarray:
+    """Block means of a [T, H, D] tensor -> [H, Nb, D] float64."""
+    a = _f32(x)
+    T, H, D = a.shape
+    out = np.empty((H, n_blocks(T, B), D), np.float64)
+    lib().s3r_oracle_pool(T, H, D, B, a, H * D, D, out)
+    return out
+
+
+def cmp_row(q, kc: np.ndarray, vc: np.ndarray, B: int, h: int, i: int,
+            scale: Optional[float] = None):
+    """Compression branch of one (head, query block): returns (lse [n], ocmp [n, D],
+    score [Nb]) in float64."""
+    a = _f32(q)
+    T, H, D = a.shape
+    Nb = n_blocks(T, B)
+    n = min(T, (i + 1) * B) - i * B
+    lse = np.empty(B, np.float64)
+    oc = np.empty((B, D), np.float64)
+    sc = np.empty(Nb, np.float64)
+    lib().s3r_oracle_cmp_row(T, H, D, B, default_scale(D) if scale is None else scale, a,
+                             H * D, D, np.ascontiguousarray(kc), np.ascontiguousarray(vc), h, i,
+                             lse, oc, sc)
+    return lse[:n], oc[:n], sc
+
+
+def topk(score_row, k: int) -> np.ndarray:
+    """Top-k block indices of one float32 score row (value desc, index asc), ascending."""
+    s = np.ascontiguousarray(np.asarray(score_row, dtype=np.float32))
+    out = np.empty(max(1, min(k, s.size)), np.int32)
+    n = lib().s3r_oracle_topk(s, s.size, k, out)
+    return out[:n]
+
+
+def sel_row(q, k, v, B: int, h: int, i: int, sel: Sequence[int],
+            scale: Optional[float] = None) -> np.ndarray:
+    """Selection branch of one (head, query block) over the listed key blocks -> [n, D]."""
+    a, b, c = _f32(q), _f32(k), _f32(v)
+    T, H, D = a.shape
+    n = min(T, (i + 1) * B) - i * B
+    s = np.ascontiguousarray(np.asarray(sel, dtype=np.int32))
+    out = np.empty((B, D), np.float64)
+    lib().s3r_oracle_sel_row(T, H, D, B, default_scale(D) if scale is None else scale,
+                             a, H * D, D, b, H * D, D, c, H * D, D, h, i, s, s.size, out)
+    return out[:n]
+
+
+def dense_rows(q, k, v, h: int, t0: int, nt: int, scale: Optional[float] = None) -> np.ndarray:
+    """Plain softmax attention of queries t0..t0+nt-1 of head h over all keys -> [nt, D]."""
+    a, b, c = _f32(q), _f32(k), _f32(v)
+    T, H, D = a.shape
+    out = np.empty((nt, D), np.float64)
+    lib().s3r_oracle_dense_rows(T, H, D, default_scale(D) if scale is None else scale, a, H * D,
+                                D, b, H * D, D, c, H * D, D, h, t0, nt, out)
+    return out
+
+
+def forward_rows(q, k, v, gates, B: int, topk_: int, rows_h: Sequence[int],
+                 rows_i: Sequence[int], kc: Optional[np.ndarray] = None,
+                 vc: Optional[np.ndarray] = None, sel_in: Optional[np.ndarray] = None,
+                 scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Whole forward pass for the listed (head, query block) rows.
+
+    Returns per-row arrays: lse [R, B], ocmp [R, B, D], score [R, Nb] (float32), sel
+    [R, k_eff], osel [R, B, D], out [R, B, D]; rows of a short last block are valid for their
+    first n_i entries only. ``kc``/``vc`` may be passed in to reuse a pooling.
+    """
+    a, b, c = _f32(q), _f32(k), _f32(v)
+    T, H, D = a.shape
+    Nb = n_blocks(T, B)
+    k_eff = min(topk_, Nb)
+    if kc is None:
+        kc = pool(b, B)
+    if vc is None:
+        vc = pool(c, B)
+    g = _f32(gates)
+    gate_st = 0 if g.ndim == 2 else H * 2
+    rh = np.ascontiguousarray(np.asarray(rows_h, dtype=np.int32))
+    ri = np.ascontiguousarray(np.asarray(rows_i, dtype=np.int64))
+    R = rh.size
+    res = {
+        "lse": np.zeros((R, B), np.float64), "ocmp": np.zeros((R, B, D), np.float64),
+        "score": np.zeros((R, Nb), np.float32), "sel": np.zeros((R, k_eff), np.int32),
+        "osel": np.zeros((R, B, D), np.float64), "out": np.zeros((R, B, D), np.float64),
+    }
+    sel_ptr = None
+    if sel_in is not None:
+        sel_in = np.ascontiguousarray(np.asarray(sel_in, dtype=np.int32).reshape(R, k_eff))
+        sel_ptr = sel_in.ctypes.data
+    lib().s3r_oracle_forward_rows(
+        T, H, D, B, topk_, default_scale(D) if scale is None else scale, a, H * D, D, b, H * D,
+        D, c, H * D, D, np.ascontiguousarray(kc), np.ascontiguousarray(vc), g.reshape(-1),
+        gate_st, R, rh, ri, sel_ptr, res["lse"], res["ocmp"], res["score"], res["sel"],
+        res["osel"], res["out"])
+    return res
+
+
+def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = None):
+    """Forward pass over every row, reassembled into token-major tensors:
+    out/ocmp/osel [T, H, D], lse [H, T], score [H, Nb, Nb] float32, sel [H, Nb, k_eff]."""
+    a = _f32(q)
+    T, H, D = a.shape
+    Nb = n_blocks(T, B)
+    rows_h = np.repeat(np.arange(H), Nb)
+    rows_i = np.tile(np.arange(Nb), H)
+    r = forward_rows(q, k, v, gates, B, topk_, rows_h, rows_i, scale=scale)
+    k_eff = r["sel"].shape[1]
+    full = {}
+    for name in ("ocmp", "osel", "out"):
+        x = r[name].reshape(H, Nb * B, D)[:, :T]          # [H, T, D]
+        full[name] = np.ascontiguousarray(x.transpose(1, 0, 2))
+    full["lse"] = r["lse"].reshape(H, Nb * B)[:, :T]
+    full["score"] = r["score"].reshape(H, Nb, Nb)
+    full["sel"] = r["sel"].reshape(H, Nb, k_eff)
+    return full
+
+
+def timed(fn, *args, **kw):
+    t0 = time.perf_counter()
+    r = fn(*args, **kw)
+    return r, time.perf_counter() - t0

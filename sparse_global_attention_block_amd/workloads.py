@@ -1,0 +1,140 @@
+"""Named workloads and seeded synthetic inputs for the sparse global attention path.
+
+This module only draws random numbers and lays them out as tensors. It holds none of the
+attention arithmetic, so the HIP library and the CPU oracle can both be fed from it.
+
+Shapes follow the multi-view transformer setting that Speed3R accelerates (project README,
+"Overview"; gist.science summary, "Technische samenvatting"): every view of a 518x518 image
+cut into 14x14 patches contributes a 37x37 grid (1369 tokens) plus 5 special tokens (one
+camera token and four register tokens), all views are concatenated along the token axis, and
+global attention runs over the whole sequence with 16 heads of width 64.
+
+Generators:
+  * ``iid``: q, k, v ~ N(0, 1) * ``iid_scale`` independently.
+  * ``structured``: x[t, h, :] = N(0, I_64) + alpha * e_view(t) @ W_h, with one 8-dim view
+    embedding e_v ~ N(0, I_8) per view and per-head projections W ~ N(0, 1/8) of shape [8, 64].
+    q and k share the projection (so tokens of the same view attract each other), v has its
+    own. Optionally the k and v rows of each view's 5 special tokens are multiplied by
+    ``special_mult`` to create heavy-hitter keys.
+  * Gates: sigmoid(N(0, 1)) per head and branch, shape [H, 2] (column 0 weights the
+    compression branch, column 1 the selection branch).
+
+Everything is drawn in float32 with a ``torch.Generator`` seeded per tensor, then rounded once
+to bfloat16 (round to nearest even). Both sides of a parity check consume the same bfloat16
+values: the GPU path directly, the oracle after an exact upcast to float.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+D_HEAD = 64
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    views: int
+    tokens_per_view: int
+    special: int          # special tokens at the start of each view
+    H: int
+    block: int
+    topk: int
+    gen: str              # "iid" or "structured"
+    seed: int
+    iid_scale: float = 1.0
+    alpha: float = 0.5
+    special_mult: float = 1.0
+    D: int = D_HEAD
+
+    @property
+    def T(self) -> int:
+        return self.views * self.tokens_per_view
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.T // self.block)
+
+    @property
+    def k_eff(self) -> int:
+        return min(self.topk, self.n_blocks)
+
+    def describe(self) -> Dict:
+        return {
+            "workload": self.name, "views": self.views, "tokens_per_view": self.tokens_per_view,
+            "T": self.T, "H": self.H, "D": self.D, "block": self.block, "topk": self.topk,
+            "generator": self.gen, "seed": self.seed,
+            **({"iid_scale": self.iid_scale} if self.gen == "iid" else
+               {"alpha": self.alpha, "special_tokens": self.special,
+                "special_kv_mult": self.special_mult}),
+        }
+
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
+    # 4 views of a 16x16 grid, iid N(0,1)/8 inputs, block 16, top-8.
+    Workload("tiny", 4, 256, 0, 4, 16, 8, "iid", seed=0, iid_scale=1.0 / 8.0),
+    # same, k = all 64 blocks (selection branch then equals dense attention)
+    Workload("tiny_all", 4, 256, 0, 4, 16, 64, "iid", seed=0, iid_scale=1.0 / 8.0),
+    # same shape with the structured generator, so that top-k has clear winners
+    Workload("tiny_s", 4, 256, 0, 4, 16, 8, "structured", seed=1),
+    # 8 views of the full per-view shape (used for quick parity at the real block size)
+    Workload("v8", 8, 1374, 5, 16, 64, 16, "structured", seed=8, special_mult=3.0),
+    Workload("v32", 32, 1374, 5, 16, 64, 16, "structured", seed=32),
+    Workload("v100", 100, 1374, 5, 16, 64, 16, "structured", seed=100, special_mult=3.0),
+    Workload("v1000_k16", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000, special_mult=3.0),
+    Workload("v1000_k32", 1000, 1374, 5, 16, 64, 32, "structured", seed=1000, special_mult=3.0),
+]}
+
+
+def _gen(seed: int, stream: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1009 + stream)
+    return g
+
+
+def _randn(shape, seed, stream, device, std=1.0):
+    return torch.randn(shape, generator=_gen(seed, stream, device), device=device,
+                       dtype=torch.float32) * std
+
+
+def make_inputs(w: Workload, device="cpu", T: Optional[int] = None,
+                views: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Return q, k, v as contiguous [T, H, 64] bfloat16 tensors and gates [H, 2] float32.
+
+    ``views`` (or ``T``) overrides the length of the sequence while keeping the recipe, which
+    is how tests build small instances of a large workload.
+    """
+    nv = views if views is not None else w.views
+    TT = T if T is not None else nv * w.tokens_per_view
+    nv = max(1, -(-TT // w.tokens_per_view))
+    H, D = w.H, w.D
+    dev = torch.device(device)
+    out = {}
+    if w.gen == "iid":
+        for i, name in enumerate(("q", "k", "v")):
+            x = _randn((TT, H, D), w.seed, i, dev, w.iid_scale)
+            out[name] = x.to(torch.bfloat16)
+    elif w.gen == "structured":
+        e = _randn((nv, 8), w.seed, 10, dev)                         # view embeddings
+        w_qk = _randn((H, 8, D), w.seed, 11, dev, math.sqrt(1.0 / 8.0))
+        w_v = _randn((H, 8, D), w.seed, 12, dev, math.sqrt(1.0 / 8.0))
+        view_of_t = torch.div(torch.arange(TT, device=dev), w.tokens_per_view,
+                              rounding_mode="floor")
+        emb_qk = torch.einsum("ve,hed->vhd", e, w_qk)                # [views, H, D]
+        emb_v = torch.einsum("ve,hed->vhd", e, w_v)
+        pos = torch.arange(TT, device=dev) % w.tokens_per_view
+        special = (pos < w.special) if w.special > 0 else None
+        for i, name in enumerate(("q", "k", "v")):
+            x = _randn((TT, H, D), w.seed, i, dev)
+            x.add_((emb_v if name == "v" else emb_qk)[view_of_t], alpha=w.alpha)
+            if name in ("k", "v") and special is not None and w.special_mult != 1.0:
+                x[special] *= w.special_mult
+            out[name] = x.to(torch.bfloat16)
+            del x
+    else:
+        raise ValueError(f"unknown generator {w.gen!r}")
+    out["gates"] = torch.sigmoid(_randn((H, 2), w.seed, 7, dev))
+    return out

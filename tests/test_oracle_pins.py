@@ -1,0 +1,277 @@
+"""Pins of the CPU oracle against facts fixed by the mathematics (no GPU).
+
+The pages print no numeric example of the method, so the oracle is pinned by a hand-derived
+worked example (tests/golden), by special cases that reduce to textbook attention (computed
+here with torch's CPU scaled_dot_product_attention / softmax in float64), by invariants of
+the definition, and by brute force on tiny inputs. Each test names the slip it would catch.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as O
+from sparse_global_attention_block_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_tensor(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+def sdpa(q, k, v, scale, mask=None):
+    """Textbook softmax attention, [T, H, D] float tensors, float64, via torch."""
+    qh, kh, vh = (x.double().permute(1, 0, 2) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qh.unsqueeze(0), kh.unsqueeze(0), vh.unsqueeze(0),
+                                       attn_mask=mask, scale=scale)[0]
+    return o.permute(1, 0, 2).numpy()
+
+
+def s(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+# ----------------------------------------------------------------------------- worked example
+def test_worked_example_closed_forms():
+    """Hand-derived example (golden/worked_example.md): catches any slip in pooling, scale,
+    softmax, score summation, top-k direction, block-to-token mapping and gating."""
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    T, H, D, B = ex["T"], ex["H"], ex["D"], ex["B"]
+    q = np.array(ex["q"], np.float32).reshape(T, H, D)
+    k = np.array(ex["k"], np.float32).reshape(T, H, D)
+    v = np.array(ex["v"], np.float32).reshape(T, H, D)
+    g = np.array(ex["gates"], np.float32).reshape(H, 2)
+    r = O.forward_all(q, k, v, g, B, ex["topk"], scale=ex["scale"])
+    kc = O.pool(k, B)
+    vc = O.pool(v, B)
+    np.testing.assert_array_equal(kc[0], [[2, 0], [0, 2]])
+    np.testing.assert_array_equal(vc[0], [[2, 0], [0, 2]])
+    e = math.e
+    lse = [math.log(e ** 2 + 1)] * 3 + [math.log(1 + e)]
+    ocmp = [(2 * s(2), 2 * s(-2)), (2 * s(2), 2 * s(-2)), (2 * s(-2), 2 * s(2)),
+            (2 * s(-1), 2 * s(1))]
+    score = [(2 * s(2), 2 * s(-2)), (s(-2) + s(-1), s(2) + s(1))]
+    osel = [(1 + 2 * s(2), 0), (1 + 2 * s(2), 0), (0, 4 * s(-2)), (0, 4 * s(-1))]
+    out = [tuple(0.25 * a + 0.75 * b for a, b in zip(x, y)) for x, y in zip(ocmp, osel)]
+    np.testing.assert_allclose(r["lse"][0], lse, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["ocmp"][:, 0], ocmp, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["score"][0], np.array(score, np.float32), rtol=0, atol=0)
+    np.testing.assert_array_equal(r["sel"][0], [[0], [1]])
+    np.testing.assert_allclose(r["osel"][:, 0], osel, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["out"][:, 0], out, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- pooling
+def test_pool_identical_keys_exact_including_short_last_block():
+    """A block of identical keys pools to exactly that key; the short last block (4 of 16
+    tokens) must be divided by its own length, not by B."""
+    T, H, D, B = 100, 3, 64, 16
+    base = bf16_tensor((7, H, D), 1).float()
+    x = base[torch.arange(T) // B]
+    kc = O.pool(x, B)
+    for j in range(7):
+        np.testing.assert_array_equal(kc[:, j], base[j].double().numpy())
+
+
+def test_pool_block1_is_identity_and_translation():
+    T, H, D = 37, 2, 64
+    x = bf16_tensor((T, H, D), 2).float()
+    np.testing.assert_array_equal(O.pool(x, 1), x.double().permute(1, 0, 2).numpy())
+    c = 0.5
+    a = O.pool(x, 8)
+    b = O.pool(x + c, 8)
+    np.testing.assert_allclose(b, a + c, rtol=0, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- compression
+@pytest.mark.parametrize("T", [40, 33])
+def test_block1_compression_is_dense_attention(T):
+    """With B = 1 every token is its own coarse token: LSE, O_cmp and the score matrix must be
+    textbook attention's log-sum-exp, output and probability matrix."""
+    H, D = 2, 64
+    q, k, v = (bf16_tensor((T, H, D), 10 + i, 0.5) for i in range(3))
+    g = torch.tensor([[1.0, 0.0]] * H)
+    r = O.forward_all(q, k, v, g, 1, 4)
+    scale = 1 / 8
+    logits = torch.einsum("thd,uhd->htu", q.double(), k.double()) * scale
+    np.testing.assert_allclose(r["lse"], torch.logsumexp(logits, -1).numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["ocmp"], sdpa(q, k, v, scale), atol=1e-12)
+    np.testing.assert_allclose(r["score"], torch.softmax(logits, -1).float().numpy(),
+                               rtol=1e-6, atol=1e-7)
+
+
+def test_compression_is_attention_over_block_means():
+    """General B (ragged tail): O_cmp is softmax attention over numpy block means."""
+    T, H, D, B = 90, 2, 64, 16
+    q, k, v = (bf16_tensor((T, H, D), 20 + i, 0.7) for i in range(3))
+    Nb = -(-T // B)
+    def means(x):
+        a = x.double().numpy()
+        return np.stack([a[j * B:min(T, (j + 1) * B)].mean(0) for j in range(Nb)])  # [Nb,H,D]
+    kc, vc = means(k), means(v)
+    r = O.forward_all(q, k, v, torch.ones(H, 2), B, 2)
+    ref = sdpa(q, torch.from_numpy(kc), torch.from_numpy(vc), 1 / 8)
+    np.testing.assert_allclose(r["ocmp"], ref, atol=1e-12)
+
+
+def test_softmax_rows_and_score_rows_sum():
+    """Probabilities of a query sum to one; summed over a block's n_i queries the score row
+    must therefore sum to n_i (64 ... 64, then 26 for the ragged last block)."""
+    T, H, D, B = 8 * 64 + 26, 2, 64, 64
+    q, k, v = (bf16_tensor((T, H, D), 30 + i) for i in range(3))
+    r = O.forward_all(q, k, v, torch.ones(H, 2), B, 3)
+    n = np.array([64] * 8 + [26], np.float64)
+    np.testing.assert_allclose(r["score"].astype(np.float64).sum(-1), np.tile(n, (H, 1)),
+                               rtol=2e-6)
+    assert (r["score"] >= 0).all()
+
+
+def test_identical_keys_give_uniform_attention():
+    """All keys equal -> every coarse logit equal -> P uniform 1/Nb, O_cmp = mean of Vc."""
+    T, H, D, B = 96, 1, 64, 16
+    q = bf16_tensor((T, H, D), 40)
+    k = bf16_tensor((1, H, D), 41).expand(T, H, D).contiguous()
+    v = bf16_tensor((T, H, D), 42)
+    r = O.forward_all(q, k, v, torch.ones(H, 2), B, 2)
+    vc = O.pool(v, B)
+    np.testing.assert_allclose(r["ocmp"][:, 0], np.tile(vc[0].mean(0), (T, 1)), atol=1e-13)
+    np.testing.assert_allclose(r["score"][0], np.full((6, 6), 16 / 6, np.float32), rtol=1e-6)
+
+
+def test_key_block_permutation_permutes_scores():
+    """Moving whole key/value blocks moves the score columns and the chosen indices with
+    them (catches a score column written to the wrong block)."""
+    T, H, D, B = 128, 2, 64, 16
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=T)
+    perm = np.array([3, 0, 7, 5, 1, 6, 2, 4])
+    tok = torch.from_numpy((perm[:, None] * B + np.arange(B)[None]).reshape(-1))
+    a = O.forward_all(x["q"], x["k"], x["v"], x["gates"], B, 3)
+    b = O.forward_all(x["q"], x["k"][tok], x["v"][tok], x["gates"], B, 3)
+    np.testing.assert_allclose(b["score"], a["score"][:, :, perm], rtol=1e-5, atol=1e-6)
+    inv = np.argsort(perm)
+    mapped = np.sort(inv[a["sel"]], axis=-1)
+    np.testing.assert_array_equal(b["sel"], mapped)
+    np.testing.assert_allclose(b["osel"], a["osel"], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- top-k
+def brute_topk(row, k):
+    idx = np.lexsort((np.arange(row.size), -row.astype(np.float64)))
+    return np.sort(idx[:min(k, row.size)])
+
+
+@pytest.mark.parametrize("levels", [None, 3, 1])
+def test_topk_brute_force_with_ties(levels):
+    rng = np.random.default_rng(5)
+    for n in (1, 7, 64, 300, 2047):
+        for k in (1, 8, 16, 32, n, n + 3):
+            row = rng.random(n).astype(np.float32)
+            if levels is not None:
+                row = (np.floor(row * levels) / max(levels, 1)).astype(np.float32)
+            np.testing.assert_array_equal(O.topk(row, k), brute_topk(row, k))
+
+
+def test_topk_all_equal_takes_smallest_indices():
+    np.testing.assert_array_equal(O.topk(np.full(50, 0.25, np.float32), 8), np.arange(8))
+
+
+def test_heavy_hitter_block_is_always_selected():
+    """A key block whose keys are a large multiple of the mean query must win top-1 on every
+    row (catches selecting the smallest scores)."""
+    T, H, D, B = 256, 2, 64, 16
+    q = bf16_tensor((T, H, D), 50).float() + 0.5
+    k = bf16_tensor((T, H, D), 51).float()
+    hot = 11
+    k[hot * B:(hot + 1) * B] = 4.0 * q.mean(0, keepdim=True)
+    v = bf16_tensor((T, H, D), 52).float()
+    r = O.forward_all(q, k, v, torch.ones(H, 2), B, 1)
+    assert (r["sel"][..., 0] == hot).all()
+
+
+# ----------------------------------------------------------------------------- selection
+@pytest.mark.parametrize("name", ["tiny_all"])
+def test_all_blocks_selected_is_dense_attention(name):
+    """k = all blocks: the selection branch must equal dense attention (the contract's own
+    brute-force check), here against torch's SDPA in float64."""
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    r = O.forward_all(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk)
+    np.testing.assert_allclose(r["osel"], sdpa(x["q"], x["k"], x["v"], 1 / 8), atol=1e-12)
+    np.testing.assert_allclose(O.dense_rows(x["q"], x["k"], x["v"], 1, 100, 20),
+                               sdpa(x["q"], x["k"], x["v"], 1 / 8)[100:120, 1], atol=1e-12)
+
+
+def test_selection_equals_masked_attention():
+    """For any selection, O_sel is SDPA with a boolean mask that admits exactly the tokens of
+    the chosen blocks (catches block/token index slips and duplicate handling)."""
+    T, H, D, B, k = 100, 2, 64, 16, 3
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=T)
+    r = O.forward_all(x["q"], x["k"], x["v"], x["gates"], B, k)
+    Nb = -(-T // B)
+    blk = torch.arange(T) // B
+    for h in range(H):
+        mask = torch.zeros(T, T, dtype=torch.bool)
+        for i in range(Nb):
+            rows = blk == i
+            cols = torch.isin(blk, torch.from_numpy(r["sel"][h, i].astype(np.int64)))
+            mask[rows.nonzero()[:, None, 0], cols.nonzero()[None, :, 0]] = True
+        ref = sdpa(x["q"][:, h:h + 1], x["k"][:, h:h + 1], x["v"][:, h:h + 1], 1 / 8,
+                   mask=mask.unsqueeze(0))
+        np.testing.assert_allclose(r["osel"][:, h], ref[:, 0], atol=1e-12)
+    # a duplicated index in an externally supplied list counts once
+    sel = np.array([[2, 2, 5]], np.int32)
+    a = O.forward_rows(x["q"], x["k"], x["v"], x["gates"], B, 3, [0], [1], sel_in=sel)
+    b = O.sel_row(x["q"], x["k"], x["v"], B, 0, 1, [2, 5])
+    np.testing.assert_allclose(a["osel"][0], b, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- gating, linearity
+def test_gates_isolate_branches_and_value_linearity():
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=200)
+    B, k = 16, 4
+    a = O.forward_all(x["q"], x["k"], x["v"], torch.tensor([[1.0, 0.0]] * w.H), B, k)
+    np.testing.assert_allclose(a["out"], a["ocmp"], atol=0)
+    b = O.forward_all(x["q"], x["k"], x["v"], torch.tensor([[0.0, 1.0]] * w.H), B, k)
+    np.testing.assert_allclose(b["out"], b["osel"], atol=0)
+    # outputs are linear in V (the selection depends on q and k only)
+    v2 = bf16_tensor(tuple(x["v"].shape), 60)
+    g = x["gates"]
+    r1 = O.forward_all(x["q"], x["k"], x["v"], g, B, k)
+    r2 = O.forward_all(x["q"], x["k"], v2, g, B, k)
+    r12 = O.forward_all(x["q"], x["k"], x["v"].float() + v2.float(), g, B, k)
+    np.testing.assert_array_equal(r12["sel"], r1["sel"])
+    np.testing.assert_allclose(r12["out"], r1["out"] + r2["out"], atol=1e-12)
+
+
+def test_per_token_gates():
+    """Per-token gates [T, H, 2] are read per token (the per-token gating reading)."""
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=64)
+    gt = torch.rand(64, w.H, 2, generator=torch.Generator().manual_seed(3))
+    r = O.forward_all(x["q"], x["k"], x["v"], gt, 16, 2)
+    ref = gt[..., :1].double().numpy() * r["ocmp"] + gt[..., 1:].double().numpy() * r["osel"]
+    np.testing.assert_allclose(r["out"], ref, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- workload facts
+def test_tiny_iid_has_no_clear_topk_rows_but_tiny_s_does():
+    """The iid N(0,1)/8 workload makes every block score ~n/Nb, so no row has a top-k gap
+    above 1e-3 and index parity is vacuous there; the structured tiny_s workload fixes that."""
+    def gap_fraction(name):
+        w = W.WORKLOADS[name]
+        x = W.make_inputs(w)
+        r = O.forward_all(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk)
+        sc = -np.sort(-r["score"].astype(np.float64), axis=-1)
+        gap = sc[..., w.topk - 1] - sc[..., w.topk]
+        return (gap > 1e-3).mean()
+    assert gap_fraction("tiny") == 0.0
+    assert gap_fraction("tiny_s") > 0.5
