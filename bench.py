@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse global attention forward pass on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic tokens: block pooling
+(+ packing of the raw keys/values), compressed LSE, compressed output + block scores, top-k
+selection, selection attention + gated combine. Inputs are generated on the GPU and resident
+in HBM before timing starts. The dense attention comparator is timed separately at the same
+shape. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v1000_k16]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_global_attention_block_amd import speed3r as S  # noqa: E402
+from sparse_global_attention_block_amd import workloads as W  # noqa: E402
+
+METRIC = "sparse global-attn fwd tokens/s at 1000 views; MFMA/HBM roofline %; x vs dense"
+PEAK_BF16 = 2.5e15       # dense MFMA, bf16/fp16 (MI355X)
+PEAK_HBM = 8.0e12        # bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w: W.Workload, T: int, Nb: int):
+    """Per-launch algorithmic flops / bytes of each kernel (per-unit figures times units)."""
+    H, D, B, k = w.H, w.D, w.block, w.k_eff
+    th = T * H
+    sel_keys = sum(min(T, (j + 1) * B) - j * B for j in range(min(k, Nb)))  # ~ k*B
+    return {
+        # reads k and v once (2 x 128 B per token-head), writes 12 KB per 32 pooled tokens
+        "pool": {"bytes": th * 256 + H * math.ceil(Nb / 32) * 12288, "bound": "hbm"},
+        # reads k and v, writes them back as packed tiles
+        "pack": {"bytes": th * 256 * 2, "bound": "hbm"},
+        # logits q.Kc over all coarse tokens: 2*D flops per (token, head, block)
+        "cmp_lse": {"flops": 2 * D * th * Nb, "bound": "mfma"},
+        # logits + P.Vc: 4*D flops per (token, head, block)
+        "cmp_fused": {"flops": 4 * D * th * Nb, "bound": "mfma"},
+        # reads the score matrix once (4 B per (head, query block, key block))
+        "topk": {"bytes": 4 * H * Nb * Nb, "bound": "hbm"},
+        # q.k and p.v over the k*B selected tokens: 4*D flops per (token, head, key)
+        "sel": {"flops": 4 * D * th * sel_keys, "bound": "mfma"},
+    }
+
+
+def timed_stages(st: "S.Stages", reps: int):
+    """Runs the hot path stage by stage with HIP events between stages (on the stream the
+    library launches on) and returns the mean duration of each stage in ms."""
+    names = ["pool", "cmp_lse", "cmp_fused", "topk", "sel"]
+    fns = [st.run_pool, st.run_lse, st.run_fused, st.run_topk, st.run_sel]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        ev[r][0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[r][i + 1].record()
+    torch.cuda.synchronize()
+    out = {n: sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
+           for i, n in enumerate(names)}
+    return out
+
+
+def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
+    """Times the float64 CPU oracle on one head: pooling over all tokens plus n_rows sampled
+    query blocks, and checks the GPU rows against it. The full-job time is extrapolated as
+    H * (pool + Nb * mean row time)."""
+    import numpy as np
+    from oracle import oracle as O
+
+    T, H = x["q"].shape[0], w.H
+    Nb = -(-T // w.block)
+    h = 0
+    rng = np.random.default_rng(seed)
+    rows = sorted(set([0, Nb - 1] + [int(r) for r in rng.integers(0, Nb, n_rows - 2)]))
+    hq, hk, hv = (x[n][:, h:h + 1].contiguous().cpu() for n in ("q", "k", "v"))
+    hg = x["gates"][h:h + 1].cpu()
+    t0 = time.perf_counter()
+    kc, vc = O.pool(hk, w.block), O.pool(hv, w.block)
+    t_pool = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32), rows,
+                       kc=kc, vc=vc)
+    t_rows = time.perf_counter() - t0
+    per_row = t_rows / len(rows)
+    t_full = H * (t_pool + Nb * per_row)
+    # parity of the sampled rows
+    gsel = sel_gpu[h, rows].cpu().numpy()
+    same = float((gsel == r["sel"]).all(axis=-1).mean())
+    err_max, err_sum, n = 0.0, 0.0, 0
+    ref = r
+    if same < 1.0:
+        ref = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32),
+                             rows, kc=kc, vc=vc, sel_in=gsel)
+    for a, i in enumerate(rows):
+        nn = min(T, (i + 1) * w.block) - i * w.block
+        g = out_gpu[i * w.block:i * w.block + nn, h].float().cpu().numpy()
+        d = abs(g - ref["out"][a, :nn])
+        err_max = max(err_max, float(d.max()))
+        err_sum += float(d.sum())
+        n += d.size
+    return {
+        "value": T / t_full, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+        "sample": f"head 0 of {H}: pooling over all {T} tokens ({t_pool:.2f} s) + {len(rows)} "
+                  f"query blocks of {w.block} ({t_rows:.2f} s); full job extrapolated as "
+                  f"H*(pool + Nb*row) = {t_full:.0f} s",
+    }, {"rows": len(rows), "rows_same_selection": same, "out_max_abs": err_max,
+        "out_mean_abs": err_sum / max(1, n)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="v1000_k16", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--dense-reps", type=int, default=1)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by head; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: T={w.T} H={w.H} B={w.block} k={w.topk}")
+    x = W.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    T, H, D = x["q"].shape
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"])
+    Nb = S.num_blocks(p)
+    ws = S.alloc_workspace(S.workspace_size(p), dev)
+    out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    sel = torch.empty(H, Nb, w.k_eff, dtype=torch.int32, device=dev)
+
+    def step():
+        S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
+                          sel_idx=sel, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] sparse forward {ms:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f})")
+
+    # per-kernel durations: the same kernels launched stage by stage
+    del ws
+    torch.cuda.empty_cache()
+    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, keep_o_sel=False)
+    st.run_all()
+    stage_ms = timed_stages(st, max(1, min(3, args.steps)))
+    log(f"[bench] stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
+    work = algorithmic_work(w, T, Nb)
+    # pool stage = pool kernel + pack kernel; report the pool stage against both kernels' bytes
+    kernels = {}
+    for name, ms_k in stage_ms.items():
+        if name == "pool":
+            wk = {"bytes": work["pool"]["bytes"] + work["pack"]["bytes"], "bound": "hbm"}
+        else:
+            wk = work[name]
+        if wk["bound"] == "hbm":
+            ach = wk["bytes"] / (ms_k * 1e-3)
+            kernels[name] = {"ms": ms_k, "bound": "hbm", "achieved": ach / 1e9, "unit": "GB/s",
+                             "frac": ach / PEAK_HBM}
+        else:
+            ach = wk["flops"] / (ms_k * 1e-3)
+            kernels[name] = {"ms": ms_k, "bound": "mfma", "achieved": ach / 1e12,
+                             "unit": "TFLOP/s", "frac": ach / PEAK_BF16}
+    dom = max(("cmp_fused", "cmp_lse", "sel"), key=lambda n: stage_ms[n])
+    roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+            "traffic": None}
+    del st
+    torch.cuda.empty_cache()
+
+    dense = None
+    if not args.no_dense:
+        small = W.make_inputs(W.WORKLOADS["tiny"], device=dev)
+        S.dense_attn_fwd(small["q"], small["k"], small["v"])  # load the kernel code
+        dws = S.alloc_workspace(S.dense_workspace_size(p), dev)
+        dout = torch.empty_like(out)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(args.dense_reps):
+            S.dense_attn_fwd(x["q"], x["k"], x["v"], out=dout, workspace=dws)
+        d1.record()
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_reps
+        dense = {"ms": dense_ms, "tflops": 4 * D * T * T * H / (dense_ms * 1e-3) / 1e12}
+        log(f"[bench] dense {dense_ms:.1f} ms ({dense['tflops']:.0f} TFLOP/s)")
+        del dws, dout
+
+    cpu, parity = None, None
+    if not args.no_cpu:
+        cpu, parity = cpu_baseline(w, x, sel, out)
+        log(f"[bench] cpu oracle {cpu['value']:.1f} tokens/s; parity {parity}")
+
+    rec = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded structured q/k/v, generated on the GPU)",
+        "config": {**w.describe(), "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "dense": dense,
+        "x_vs_dense": (dense["ms"] / ms) if dense else None,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

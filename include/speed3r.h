@@ -1,0 +1,161 @@
+/*
+ * speed3r.h - C ABI of the MI355X (gfx950) sparse global attention library (libspeed3r.so).
+ *
+ * The library computes the forward pass of Speed3R's dual-branch global sparse attention
+ * (Speed3R technical summary on gist.science, "Methodologie" section 1, dual-branch attention,
+ * and section 2, gated aggregation; Speed3R README, "Overview"):
+ *
+ *   compression branch   Kc_j, Vc_j = means of the keys / values of contiguous block j
+ *                        (B tokens; the last block may be shorter);
+ *                        P_tj = softmax_j(scale * q_t . Kc_j), O_cmp_t = sum_j P_tj Vc_j;
+ *                        Score[h][i][j] = sum over the queries t of query block i of P_tj.
+ *   selection branch     Sel[h][i] = the k blocks with the largest Score[h][i][.] (ties: the
+ *                        smaller block index wins; stored in ascending order);
+ *                        O_sel_t = softmax attention of q_t over the tokens of those blocks.
+ *   gated aggregation    out_t = g[h][0] * O_cmp_t + g[h][1] * O_sel_t.
+ *
+ * Conventions shared by every entry point
+ *   - Token tensors q, k, v are bf16 [T][H][D] with D = 64 contiguous; token and head strides
+ *     are given in elements and must be multiples of 8 (16-byte rows); base pointers must be
+ *     16-byte aligned. Query blocks and key blocks both have size B = params.block.
+ *   - Numerics: logits are bf16 x bf16 products accumulated in f32 (the pooled keys as a
+ *     bf16 hi + lo pair); softmax runs in f32 with base-2 exponentials; the P.V products take
+ *     fp16 operands with f32 accumulation, so values of v must stay below 65504 in magnitude.
+ *   - Every pointer is device memory owned by the caller; the library never allocates, frees
+ *     or synchronises. All work is enqueued on `stream` (NULL = the default stream) and the
+ *     call returns before it completes. Asynchronous faults surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated before anything is launched; on any error nothing is launched
+ *     and no output is touched.
+ *   - The library keeps no state between calls and may be called from several threads.
+ *     Calls that share a workspace must be ordered by the caller (same stream).
+ */
+#ifndef SPEED3R_H
+#define SPEED3R_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  S3R_OK = 0,
+  S3R_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment */
+  S3R_ERR_UNSUPPORTED = 2, /* well-formed but not built: D != 64, B not 16/32/64/128,
+                              more than 24576 blocks, H > 65535 */
+  S3R_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
+  S3R_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
+} s3r_status;
+
+typedef struct {
+  int64_t T;            /* number of tokens (all views concatenated), >= 1 */
+  int32_t H;            /* number of heads, >= 1 */
+  int32_t D;            /* head width; must be 64 */
+  int32_t block;        /* B: query and key block size, one of 16, 32, 64, 128 */
+  int32_t topk;         /* k >= 1: key blocks kept per query block; clamped to Nb */
+  float scale;          /* softmax scale; 0 selects 1/sqrt(D) */
+  int32_t reserved;     /* must be 0 */
+  int64_t q_stride_t, q_stride_h; /* element strides of q between tokens / heads */
+  int64_t k_stride_t, k_stride_h;
+  int64_t v_stride_t, v_stride_h;
+  int64_t gate_stride_t; /* 0: gates are [H][2]; otherwise per-token gates with
+                            gate(t, h, b) = gates[t * gate_stride_t + h * 2 + b] */
+} s3r_params;
+
+/* Human-readable name of a status code (static storage). */
+const char* speed3r_status_string(s3r_status s);
+
+/* Nb = ceil(T / B), the number of key blocks (= query blocks). -1 if p is invalid. */
+int64_t speed3r_num_blocks(const s3r_params* p);
+
+/* Row stride (in floats) of the score matrix [H][Nb][ld]: Nb rounded up to 32. -1 if invalid. */
+int64_t speed3r_score_row_stride(const s3r_params* p);
+
+/* Bytes of workspace the per-stage entry points need (packed tiles of the pooled keys and
+ * values and of the raw keys and values). 0 if p is invalid. */
+size_t speed3r_tiles_workspace_size(const s3r_params* p);
+
+/* Bytes of workspace speed3r_sparse_attn_fwd needs: the tiles plus LSE [H][T] f32, O_cmp
+ * [T][H][64] f32, the score matrix [H][Nb][ld] f32 and the selected indices. About 41 GB at
+ * T = 1,374,000, H = 16, B = 64. 0 if p is invalid. */
+size_t speed3r_workspace_size(const s3r_params* p);
+
+/* Bytes of workspace speed3r_dense_attn_fwd needs (packed raw keys and values). */
+size_t speed3r_dense_workspace_size(const s3r_params* p);
+
+/* The whole sparse forward pass (the method of the summary's "Methodologie" sections 1-2):
+ * pool -> compressed LSE -> compressed output + block scores -> top-k -> selection attention
+ * with the gate-combine epilogue.
+ *   gates    f32, [H][2] or per token (see gate_stride_t); column 0 multiplies the
+ *            compression branch, column 1 the selection branch.
+ *   out      bf16 [T][H][64], contiguous.
+ *   sel_idx  optional int32 [H][Nb][k_eff] (k_eff = min(k, Nb)); NULL keeps it in the
+ *            workspace.
+ *   workspace / workspace_bytes: at least speed3r_workspace_size(p) bytes, 256-byte aligned.
+ */
+s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const void* k,
+                                   const void* v, const float* gates, void* out,
+                                   int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* Per-stage entry points (the same kernels the fused entry point runs), for per-kernel
+ * timing and for feeding one stage with another implementation's intermediate results.
+ * `workspace` must hold at least speed3r_tiles_workspace_size(p) bytes and is the one that
+ * speed3r_pool filled. */
+
+/* Compression branch, pooling (summary "Methodologie" 1, average pooling of blocks): fills the
+ * workspace tiles from k and v. k_mean / v_mean (optional, f32 [H][Nb][64]) receive the block
+ * means themselves: sum in f32 then an IEEE division by the block's token count. */
+s3r_status speed3r_pool(const s3r_params* p, const void* k, const void* v, void* workspace,
+                        size_t workspace_bytes, float* k_mean, float* v_mean,
+                        hipStream_t stream);
+
+/* Compression branch, first pass: lse[h][t] = log sum_j exp(scale * q_t . Kc_j) (natural log,
+ * f32 [H][T]). The pooled keys enter as the sum of two bf16 terms (hi + lo) of
+ * Kc * scale * log2(e), accumulated in f32. */
+s3r_status speed3r_cmp_lse(const s3r_params* p, const void* q, const void* workspace,
+                           size_t workspace_bytes, float* lse, hipStream_t stream);
+
+/* Compression branch, second pass (summary "Methodologie" 1: coarse attention and the score
+ * matrix that guides selection): P_tj = exp(scale * q_t . Kc_j - lse[h][t]);
+ * o_cmp[t][h][:] = sum_j P_tj Vc_j (f32 [T][H][64]); score[(h*Nb + i)*ld + j] = sum over the
+ * queries of block i of P_tj (f32, ld = speed3r_score_row_stride; columns >= Nb are
+ * written with 0). */
+s3r_status speed3r_cmp_fused(const s3r_params* p, const void* q, const void* workspace,
+                             size_t workspace_bytes, const float* lse, float* o_cmp,
+                             float* score, hipStream_t stream);
+
+/* Top-k selection (summary "Methodologie" 1, selection guided by the compression scores):
+ * sel_idx[(h*Nb + i)*k_eff + a] = the k_eff largest entries of score row (h, i) by (value
+ * descending, index ascending), written in ascending order. Bit-exact, deterministic.
+ * Scores are compared as f32 values (-0 equals +0). */
+s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_idx,
+                        hipStream_t stream);
+
+/* Selection branch plus gated aggregation (summary "Methodologie" 1 selection branch and 2
+ * gated aggregation): for every query of block i, softmax attention over the tokens of the
+ * blocks sel_idx[h][i][0..k_eff), then out = g0 * o_cmp + g1 * O_sel rounded to bf16
+ * [T][H][64]. Rows are read in order; an index outside [0, Nb) or equal to the previous index
+ * of its row is skipped, so an ascending row (as speed3r_topk writes) attends to the union of
+ * its blocks. o_sel (optional, f32 [T][H][64]) receives O_sel itself. */
+s3r_status speed3r_sel_combine(const s3r_params* p, const void* q, const void* workspace,
+                               size_t workspace_bytes, const int32_t* sel_idx,
+                               const float* o_cmp, const float* gates, void* out,
+                               float* o_sel, hipStream_t stream);
+
+/* Dense global attention, the quadratic baseline the method replaces (summary
+ * "Probleemstelling"): out = softmax(scale * q k^T) v over all T tokens per head, bf16
+ * [T][H][64]. Workspace: speed3r_dense_workspace_size(p) bytes. */
+s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void* k,
+                                  const void* v, void* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEED3R_H */

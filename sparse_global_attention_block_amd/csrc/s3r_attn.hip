@@ -1,0 +1,337 @@
+// Exact softmax attention over packed key/value tiles: the selection branch (over the tokens
+// of each query block's chosen key blocks, with the gated-aggregation epilogue) and the dense
+// global attention it replaces.
+//
+// Speed3R technical summary (gist.science): "Methodologie" section 1 (the selection branch
+// attends finely to the selected tokens only) and section 2 (a learned gate mixes the two
+// branch outputs); "Probleemstelling" (dense global attention over all tokens is the
+// quadratic cost being removed).
+//
+// Both kernels share one tile step: S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (lane l holds
+// query l%16, keys 4*(l/16)+r), base-2 online softmax with a per-query offset shared by the
+// four lanes that hold a query, and O^T += V^T . P^T in fp16 with P taken straight from the
+// S^T registers. The offset only moves when a logit exceeds it by more than 2^8 (checked with one
+// max per element), which happens on the first tile and rarely afterwards.
+#include "s3r_common.hpp"
+#include "s3r_launch.hpp"
+
+namespace s3r {
+
+constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the offset must move
+
+template <int NT>
+struct Flash {
+  float m[NT];          // per-query offset (base 2), identical in the 4 lanes of a query
+  floatx4 l[NT];        // sum over keys of the bf16-rounded weights (all 4 entries equal)
+  floatx4 o[4][NT];     // O^T accumulators: dims 16*mt + 4g + r, query 16*nt + l%16
+
+  __device__ void init() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      m[nt] = -INFINITY;
+      l[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) o[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // One tile of 32 keys. rec[0..3] = K records (bf16), rec[4..7] = V^T records (fp16), this
+  // lane's 16 bytes of each. Keys outside [lo, hi) of the tile are masked. The softmax denominator is a
+  // ones-row MFMA over the same bf16 weights that multiply V, so numerator and denominator
+  // see identical rounding.
+  __device__ void step(const bf16x8 (&rec)[8], const bf16x8 (&qb)[NT][2], int lo, int hi,
+                       float mult, int g) {
+    floatx4 acc[2][NT];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        floatx4 x = mfma16(rec[2 * s2], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[s2][nt] = mfma16(rec[2 * s2 + 1], qb[nt][1], x);
+      }
+    if (lo > 0 || hi < kTileKeys) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * s2 + 4 * g + r;
+          if (key < lo || key >= hi) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[s2][nt][r] = -INFINITY;
+          }
+        }
+    }
+    bool need = false;
+    float mx[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float v = acc[0][nt][0];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v = fmaxf(v, acc[s2][nt][r]);
+      mx[nt] = v * mult;
+      need |= mx[nt] > m[nt] + kRescaleSlack;
+    }
+    if (__builtin_expect(__any(need), 0)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float M = mx[nt];
+        M = fmaxf(M, __shfl_xor(M, 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        if (M > m[nt]) {
+          const float f = (m[nt] == -INFINITY) ? 0.f : fast_exp2(m[nt] - M);
+          l[nt] *= f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) o[mt][nt] *= f;
+          m[nt] = M;
+        }
+      }
+    }
+    const halfx8 ones = pack8h(1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // a query whose every key so far is masked keeps m = -inf: use 0 so that p = 0
+      const float mm = (m[nt] == -INFINITY) ? 0.f : m[nt];
+      float p[2][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[s2][r] = fast_exp2(fmaf(acc[s2][nt][r], mult, -mm));
+      const halfx8 pb = pack8h(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2],
+                               p[1][3]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        o[mt][nt] = mfma16h(__builtin_bit_cast(halfx8, rec[4 + mt]), pb, o[mt][nt]);
+      l[nt] = mfma16h(ones, pb, l[nt]);
+    }
+  }
+
+  // 1 / softmax denominator per query, 0 for an empty softmax
+  __device__ void finish(float (&inv)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) inv[nt] = (l[nt][0] > 0.f) ? 1.0f / l[nt][0] : 0.f;
+  }
+};
+
+template <int NT>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int h, int64_t q0, int g, int li,
+                                       bf16x8 (&qb)[NT][2]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t t = q0 + 16 * nt + li;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      qb[nt][c] = (t < a.T) ? *reinterpret_cast<const bf16x8*>(a.q + t * a.q_st +
+                                                               (int64_t)h * a.q_sh + 32 * c + 8 * g)
+                            : bf16x8{};
+  }
+}
+
+__device__ __forceinline__ void load_tile(const unsigned char* base, int lane, bf16x8 (&rec)[8]) {
+  const bf16x8* p = reinterpret_cast<const bf16x8*>(base);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) rec[x] = p[x * 64 + lane];
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection branch. One wave per (head, query block) (two waves for B = 128, 64 queries
+// each). The wave walks the tiles of its selected blocks in list order, loading each tile's
+// 8 operand records straight from the packed raw tiles in global memory (one coalesced 1 KB
+// read per record) while it computes on the previous tile.
+// ---------------------------------------------------------------------------------------
+struct SelIter {
+  int idx;          // position in the selection row
+  int64_t prev;     // last block taken
+  int64_t tile, tile_end;
+  int64_t blk_lo, blk_hi;  // token range of the current block
+};
+
+__device__ __forceinline__ bool sel_next_block(const AttnArgs& a, const int32_t* row, SelIter& it) {
+  while (it.idx < a.k_eff) {
+    const int64_t j = row[it.idx++];
+    if (j < 0 || j >= a.Nb || j == it.prev) continue;
+    it.prev = j;
+    it.blk_lo = j * a.B;
+    it.blk_hi = (it.blk_lo + a.B < a.T) ? it.blk_lo + a.B : a.T;
+    it.tile = it.blk_lo / kTileKeys;
+    it.tile_end = (it.blk_hi - 1) / kTileKeys + 1;
+    return true;
+  }
+  return false;
+}
+
+__device__ __forceinline__ bool sel_advance(const AttnArgs& a, const int32_t* row, SelIter& it) {
+  if (it.tile + 1 < it.tile_end) {
+    ++it.tile;
+    return true;
+  }
+  return sel_next_block(a, row, it);
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int parts = (a.B > 64) ? a.B / 64 : 1;
+  const int64_t n_items = (int64_t)a.H * a.Nb * parts;
+  const int64_t n_wg = (n_items + 3) / 4;
+  const int64_t wg = xcd_logical_id(blockIdx.x, n_wg);
+  const int64_t item = wg * 4 + wave;
+  if (wg >= n_wg || item >= n_items) return;
+  const int part = (int)(item % parts);
+  const int64_t hi_ = item / parts;
+  const int h = (int)(hi_ / a.Nb);
+  const int64_t i = hi_ % a.Nb;
+  const int64_t q0 = i * a.B + 64 * part;
+
+  bf16x8 qb[NT][2];
+  load_q<NT>(a, h, q0, g, li, qb);
+  const int32_t* row = a.sel + ((int64_t)h * a.Nb + i) * a.k_eff;
+  const unsigned char* tiles = a.tiles + (int64_t)h * a.n_tiles * kRawTileBytes;
+
+  Flash<NT> f;
+  f.init();
+  SelIter it{0, -1, 0, 0, 0, 0};
+  bool valid = sel_next_block(a, row, it);
+  bf16x8 cur[8];
+  if (valid) load_tile(tiles + it.tile * kRawTileBytes, lane, cur);
+  while (valid) {
+    const int64_t t0 = it.tile * kTileKeys;
+    const int lo = (int)((it.blk_lo > t0) ? it.blk_lo - t0 : 0);
+    const int hi = (int)((it.blk_hi < t0 + kTileKeys) ? it.blk_hi - t0 : kTileKeys);
+    SelIter nx = it;
+    const bool nvalid = sel_advance(a, row, nx);
+    bf16x8 nxt[8];
+    if (nvalid) load_tile(tiles + nx.tile * kRawTileBytes, lane, nxt);
+    f.step(cur, qb, lo, hi, a.logit_mult, g);
+    if (nvalid) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) cur[x] = nxt[x];
+    }
+    it = nx;
+    valid = nvalid;
+  }
+
+  float inv[NT];
+  f.finish(inv);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t t = q0 + 16 * nt + li;
+    if (t >= a.T || 16 * nt + li + 64 * part >= a.B) continue;
+    const float* gp = a.gates + t * a.gate_st + (int64_t)h * 2;
+    const float g_cmp = gp[0], g_sel = gp[1];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t base = (t * a.H + h) * kD + 16 * mt + 4 * g;
+      const float4 oc = *reinterpret_cast<const float4*>(a.o_cmp + base);
+      const float s0 = f.o[mt][nt][0] * inv[nt], s1 = f.o[mt][nt][1] * inv[nt];
+      const float s2 = f.o[mt][nt][2] * inv[nt], s3 = f.o[mt][nt][3] * inv[nt];
+      if (a.o_sel) *reinterpret_cast<float4*>(a.o_sel + base) = make_float4(s0, s1, s2, s3);
+      uint2 w;
+      w.x = bf16_bits(g_cmp * oc.x + g_sel * s0) | ((uint32_t)bf16_bits(g_cmp * oc.y + g_sel * s1) << 16);
+      w.y = bf16_bits(g_cmp * oc.z + g_sel * s2) | ((uint32_t)bf16_bits(g_cmp * oc.w + g_sel * s3) << 16);
+      *reinterpret_cast<uint2*>(a.out + base) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Dense attention. A work-group of 4 waves owns 256 queries of one head and streams every
+// raw tile of that head through a double-buffered LDS ring (8 KB per tile).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
+  constexpr int kTileU4 = kRawTileBytes / 16;  // 512
+  __shared__ uint4 lds[2][kTileU4];
+  const int64_t n_qtiles = (a.T + 255) / 256;
+  const int64_t total = (int64_t)a.H * n_qtiles;
+  const int64_t logical = xcd_logical_id(blockIdx.x, total);
+  if (logical >= total) return;
+  const int h = (int)(logical / n_qtiles);
+  const int64_t qt = logical % n_qtiles;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t q0 = qt * 256 + wave * 64;
+
+  bf16x8 qb[4][2];
+  load_q<4>(a, h, q0, g, li, qb);
+  const uint4* tiles = reinterpret_cast<const uint4*>(a.tiles) + (int64_t)h * a.n_tiles * kTileU4;
+
+  Flash<4> f;
+  f.init();
+  uint4 stg[2];
+  stg[0] = tiles[tid];
+  stg[1] = tiles[256 + tid];
+  lds[0][tid] = stg[0];
+  lds[0][256 + tid] = stg[1];
+  __syncthreads();
+  for (int64_t tau = 0; tau < a.n_tiles; ++tau) {
+    const int buf = (int)(tau & 1);
+    const bool has_next = tau + 1 < a.n_tiles;
+    if (has_next) {
+      stg[0] = tiles[(tau + 1) * kTileU4 + tid];
+      stg[1] = tiles[(tau + 1) * kTileU4 + 256 + tid];
+    }
+    bf16x8 rec[8];
+    const bf16x8* L = reinterpret_cast<const bf16x8*>(lds[buf]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) rec[x] = L[x * 64 + lane];
+    const int64_t t0 = tau * kTileKeys;
+    const int hi = (int)((a.T - t0 < kTileKeys) ? a.T - t0 : kTileKeys);
+    f.step(rec, qb, 0, hi, a.logit_mult, g);
+    if (has_next) {
+      lds[buf ^ 1][tid] = stg[0];
+      lds[buf ^ 1][256 + tid] = stg[1];
+    }
+    __syncthreads();
+  }
+  float inv[4];
+  f.finish(inv);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t t = q0 + 16 * nt + li;
+    if (t >= a.T) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t base = (t * a.H + h) * kD + 16 * mt + 4 * g;
+      uint2 w;
+      w.x = bf16_bits(f.o[mt][nt][0] * inv[nt]) | ((uint32_t)bf16_bits(f.o[mt][nt][1] * inv[nt]) << 16);
+      w.y = bf16_bits(f.o[mt][nt][2] * inv[nt]) | ((uint32_t)bf16_bits(f.o[mt][nt][3] * inv[nt]) << 16);
+      *reinterpret_cast<uint2*>(a.out + base) = w;
+    }
+  }
+}
+
+hipError_t launch_sel(const AttnArgs& a, hipStream_t s) {
+  const int parts = (a.B > 64) ? a.B / 64 : 1;
+  const int64_t n_items = (int64_t)a.H * a.Nb * parts;
+  const int64_t n_wg = (n_items + 3) / 4;
+  const dim3 g3((unsigned)(((n_wg + 7) / 8) * 8)), b3(256);
+  switch (a.B) {
+    case 16: hipLaunchKernelGGL((sel_kernel<1>), g3, b3, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((sel_kernel<2>), g3, b3, 0, s, a); break;
+    default: hipLaunchKernelGGL((sel_kernel<4>), g3, b3, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dense(const AttnArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H * ((a.T + 255) / 256);
+  hipLaunchKernelGGL(dense_kernel, dim3((unsigned)(((total + 7) / 8) * 8)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace s3r

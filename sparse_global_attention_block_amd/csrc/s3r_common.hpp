@@ -1,0 +1,156 @@
+// Shared device-side definitions of the gfx950 kernels: MFMA operand types, the packed tile
+// layouts, DPP helpers and launch geometry. Private to the library (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s3r {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int kD = 64;           // head width
+constexpr int kTileKeys = 32;    // keys per packed tile
+constexpr int kRecBytes = 1024;  // one MFMA A-operand record: 64 lanes x 16 bytes
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------------
+// Packed tile layouts. Every tile covers 32 consecutive keys of one head and is stored as a
+// sequence of 1 KB records, each the exact register image of one A operand of
+// v_mfma_f32_16x16x32_bf16 (lane l holds row l%16, k-slots 8*(l/16)..+7), so a wave loads
+// an operand with one linear 16-byte read per lane.
+//
+//  K record (s, c), s = key half (0/1), c = dim chunk (0/1):
+//      lane l -> key 16*s + l%16, dims 32*c + 8*(l/16) + 0..7.           record index 2*s + c
+//  V^T record mt = 0..3 (16 output dims each):
+//      lane l -> dim 16*mt + l%16, slot e -> key vkey(l/16, e)           record index mt
+//      vkey(g, e) = e < 4 ? 4g + e : 16 + 4g + (e - 4).
+//  The S^T accumulator of keys 16*s..+15 x 16 queries puts key 16*s + 4g + r in lane group
+//  g = l/16, register r; the P operand of P.V therefore takes slot e < 4 from half 0 and
+//  slot e >= 4 from half 1, which is exactly vkey.
+//
+//  Pooled tiles (compression branch): [K hi: 4 records][K lo: 4 records][V^T: 4 records].
+//  Raw tiles (selection and dense):   [K: 4 records][V^T: 4 records].
+//  K records hold bf16 (the logits Q.K are exact products of bf16 inputs); V^T records hold
+//  fp16, because the P.V product takes both operands in fp16: the attention weights P lie in
+//  [0, 2^8] and fp16 rounds them 8x finer than bf16 at the same MFMA rate, and bf16 values of
+//  magnitude below 65504 convert to fp16 exactly (subnormal-range values to within 2^-25).
+// ---------------------------------------------------------------------------------------
+constexpr int kPooledTileBytes = 12 * kRecBytes;
+constexpr int kRawTileBytes = 8 * kRecBytes;
+
+__device__ __forceinline__ int vkey(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+
+// (key m within the tile, dim d) -> (record, lane, slot) of the V^T records
+__device__ __forceinline__ void vt_position(int m, int d, int& rec, int& lane, int& slot) {
+  const int half = m >> 4, w = m & 15;
+  const int g = w >> 2, e = (w & 3) + 4 * half;
+  rec = d >> 4;
+  lane = (d & 15) + 16 * g;
+  slot = e;
+}
+
+// (key m, dim group d8 of 8 dims) -> byte offset of the 16-byte chunk in the K records
+__device__ __forceinline__ int k_chunk_offset(int m, int d8) {
+  const int s = m >> 4, c = d8 >> 2;
+  const int lane = (m & 15) + 16 * (d8 & 3);
+  return ((2 * s + c) * 64 + lane) * 16;
+}
+
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16h(const halfx8& a, const halfx8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u16 bf16_bits(float x) {
+  __bf16 b = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(u16, b);
+}
+__device__ __forceinline__ float bf16_to_float(u16 b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ u16 f16_bits(float x) {
+  _Float16 b = (_Float16)x;  // round to nearest even
+  return __builtin_bit_cast(u16, b);
+}
+
+__device__ __forceinline__ halfx8 pack8h(float a0, float a1, float a2, float a3, float a4,
+                                         float a5, float a6, float a7) {
+  halfx8 r;
+  r[0] = (_Float16)a0; r[1] = (_Float16)a1; r[2] = (_Float16)a2; r[3] = (_Float16)a3;
+  r[4] = (_Float16)a4; r[5] = (_Float16)a5; r[6] = (_Float16)a6; r[7] = (_Float16)a7;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                        float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------
+// DPP lane exchanges (gfx9 encodings). All of them stay inside a row of 16 lanes.
+// ---------------------------------------------------------------------------------------
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppRor8 = 0x128,       // row_ror:8  (lane i <- i^8 inside a 16-lane row)
+  kDppHalfMirror = 0x141, // row_half_mirror (lane i <- 7-i inside each 8-lane half)
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of each DPP row of 8 values per lane, v[s][r] (key 16s + 4g + r of
+// lane group g). Returns the total for key 16*bit3 + 4g + 2*bit2 + bit0 of the lane index
+// inside the row; lanes i and i^2 hold the same key.
+__device__ __forceinline__ float row_reduce_scatter8(const float (&v)[2][4], int lane) {
+  const bool b3 = lane & 8, b2 = lane & 4, b0 = lane & 1;
+  float a[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float keep = b3 ? v[1][r] : v[0][r];
+    const float send = b3 ? v[0][r] : v[1][r];
+    a[r] = keep + dpp<kDppRor8>(send);
+  }
+  float b[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const float keep = b2 ? a[2 + x] : a[x];
+    const float send = b2 ? a[x] : a[2 + x];
+    b[x] = keep + dpp<kDppHalfMirror>(send);
+  }
+  const float keep = b0 ? b[1] : b[0];
+  const float send = b0 ? b[0] : b[1];
+  const float c = keep + dpp<kDppXor1>(send);
+  return c + dpp<kDppXor2>(c);
+}
+
+__device__ __forceinline__ int reduced_key(int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  return 16 * ((i >> 3) & 1) + 4 * g + 2 * ((i >> 2) & 1) + (i & 1);
+}
+
+// Work-group id remapped so that consecutive logical ids share an XCD: the dispatcher hands
+// work-groups to the 8 XCDs round-robin, so logical id x*per + s runs on XCD x.
+__device__ __forceinline__ int64_t xcd_logical_id(int64_t b, int64_t total) {
+  const int64_t per = (total + 7) / 8;
+  return (b % 8) * per + b / 8;
+}
+
+}  // namespace s3r

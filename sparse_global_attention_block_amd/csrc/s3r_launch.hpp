@@ -1,0 +1,74 @@
+// Kernel argument blocks and host launchers shared between the kernel files and the C ABI
+// layer. Private to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s3r {
+
+struct PoolArgs {
+  const uint16_t* k; const uint16_t* v;
+  int64_t k_st, k_sh, v_st, v_sh;
+  int64_t T, Nb, n_tiles;
+  int32_t H, B;
+  float key_mult;          // scale * log2(e), folded into the packed pooled keys
+  float* k_mean; float* v_mean;  // optional f32 [H][Nb][64]
+  unsigned char* tiles;    // [H][n_tiles][12 KB]
+};
+
+struct PackArgs {
+  const uint16_t* k; const uint16_t* v;
+  int64_t k_st, k_sh, v_st, v_sh;
+  int64_t T, n_tiles;
+  int32_t H;
+  unsigned char* tiles;    // [H][n_tiles][8 KB]
+};
+
+struct CmpArgs {
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  int64_t T, Nb, n_tiles;  // n_tiles = ceil(Nb / 32)
+  int32_t H, B;
+  const unsigned char* tiles;  // pooled tiles
+  float* lse;              // [H][T] natural log (written by the LSE pass, read by the fused pass)
+  const float* lse_in;
+  float* o_cmp;            // [T][H][64]
+  float* score;            // [H][Nb][ld]
+  int64_t ld;
+};
+
+struct TopkArgs {
+  const float* score;
+  int64_t ld;
+  int64_t Nb;
+  int64_t n_rows;          // H * Nb
+  int32_t k_eff;
+  int32_t* sel;            // [n_rows][k_eff]
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  int64_t T, Nb, n_tiles;  // raw tiles: n_tiles = ceil(T / 32)
+  int32_t H, B;
+  float logit_mult;        // scale * log2(e)
+  const unsigned char* tiles;  // raw packed k/v tiles
+  // selection only
+  const int32_t* sel; int32_t k_eff;
+  const float* o_cmp;
+  const float* gates; int64_t gate_st;
+  float* o_sel;            // optional
+  uint16_t* out;           // bf16 [T][H][64]
+};
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s);
+hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_sel(const AttnArgs& a, hipStream_t s);
+hipError_t launch_dense(const AttnArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+}  // namespace s3r

@@ -1,0 +1,140 @@
+// Block pooling (compression branch input) and raw key/value packing.
+//
+// Pooling follows the compression branch of the Speed3R technical summary (gist.science,
+// "Methodologie" section 1): each contiguous block of B tokens of the keys and values is
+// replaced by its mean. Both kernels stream q/k/v-shaped bf16 tensors once and are bound by
+// HBM bandwidth.
+#include "s3r_common.hpp"
+#include "s3r_launch.hpp"
+
+namespace s3r {
+
+// One work-group per (head, tile of 32 consecutive blocks). Thread (slot m = tid/8, dim group
+// d8 = tid%8) sums block 32*tile + m over its tokens, 8 dims of k and of v at a time, in f32,
+// then divides by the block's token count (IEEE division). Writes the f32 means (optional)
+// and one pooled tile: the mean keys scaled by key_mult = scale*log2(e) as bf16 hi + bf16 lo
+// (hi = bf16(x), lo = bf16(x - hi)), and the mean values as fp16 V^T records.
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kPooledTileBytes];
+  const int tid = threadIdx.x;
+  const int m = tid >> 3, d8 = tid & 7;
+  const int64_t tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int64_t j = tile * kTileKeys + m;
+  float ks[8], vs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ks[e] = 0.f; vs[e] = 0.f; }
+  int64_t n = 0;
+  if (j < a.Nb) {
+    const int64_t t0 = j * a.B;
+    const int64_t t1 = (t0 + a.B < a.T) ? t0 + a.B : a.T;
+    n = t1 - t0;
+    const u16* kp = a.k + t0 * a.k_st + (int64_t)h * a.k_sh + d8 * 8;
+    const u16* vp = a.v + t0 * a.v_st + (int64_t)h * a.v_sh + d8 * 8;
+    for (int64_t t = 0; t < n; ++t) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(kp + t * a.k_st);
+      const uint4 vv = *reinterpret_cast<const uint4*>(vp + t * a.v_st);
+      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ks[2 * e] += __builtin_bit_cast(float, kw[e] << 16);
+        ks[2 * e + 1] += __builtin_bit_cast(float, kw[e] & 0xFFFF0000u);
+        vs[2 * e] += __builtin_bit_cast(float, vw[e] << 16);
+        vs[2 * e + 1] += __builtin_bit_cast(float, vw[e] & 0xFFFF0000u);
+      }
+    }
+    const float fn = (float)n;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { ks[e] = ks[e] / fn; vs[e] = vs[e] / fn; }
+    if (a.k_mean) {
+      float4* km = reinterpret_cast<float4*>(a.k_mean + ((int64_t)h * a.Nb + j) * kD + d8 * 8);
+      km[0] = make_float4(ks[0], ks[1], ks[2], ks[3]);
+      km[1] = make_float4(ks[4], ks[5], ks[6], ks[7]);
+    }
+    if (a.v_mean) {
+      float4* vm = reinterpret_cast<float4*>(a.v_mean + ((int64_t)h * a.Nb + j) * kD + d8 * 8);
+      vm[0] = make_float4(vs[0], vs[1], vs[2], vs[3]);
+      vm[1] = make_float4(vs[4], vs[5], vs[6], vs[7]);
+    }
+  }
+  // K hi / lo chunks (16 bytes each, already in record order)
+  u16 hi[8], lo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = ks[e] * a.key_mult;
+    hi[e] = bf16_bits(x);
+    lo[e] = bf16_bits(x - bf16_to_float(hi[e]));
+  }
+  const int koff = k_chunk_offset(m, d8);
+  uint4 hv, lv;
+  hv.x = hi[0] | ((uint32_t)hi[1] << 16); hv.y = hi[2] | ((uint32_t)hi[3] << 16);
+  hv.z = hi[4] | ((uint32_t)hi[5] << 16); hv.w = hi[6] | ((uint32_t)hi[7] << 16);
+  lv.x = lo[0] | ((uint32_t)lo[1] << 16); lv.y = lo[2] | ((uint32_t)lo[3] << 16);
+  lv.z = lo[4] | ((uint32_t)lo[5] << 16); lv.w = lo[6] | ((uint32_t)lo[7] << 16);
+  *reinterpret_cast<uint4*>(stage + koff) = hv;
+  *reinterpret_cast<uint4*>(stage + 4 * kRecBytes + koff) = lv;
+  // V^T: 8 scattered bf16 per thread
+  u16* vt = reinterpret_cast<u16*>(stage + 8 * kRecBytes);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    int rec, lane, slot;
+    vt_position(m, d8 * 8 + e, rec, lane, slot);
+    vt[(rec * 64 + lane) * 8 + slot] = f16_bits(vs[e]);
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(a.tiles + ((int64_t)h * a.n_tiles + tile) * kPooledTileBytes);
+  const uint4* src = reinterpret_cast<const uint4*>(stage);
+#pragma unroll
+  for (int r = 0; r < kPooledTileBytes / (16 * 256); ++r) dst[r * 256 + tid] = src[r * 256 + tid];
+}
+
+// One work-group per (head, group of kPackTiles tiles of 32 tokens). Thread (key m, dims d8)
+// copies 16 bytes of k into its K record slot and scatters 8 values of v, converted to fp16,
+// into the V^T records through LDS. Tokens beyond T are zero.
+constexpr int kPackTiles = 4;
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char stage[4 * kRecBytes];
+  const int tid = threadIdx.x;
+  const int m = tid >> 3, d8 = tid & 7;
+  const int h = blockIdx.y;
+  for (int it = 0; it < kPackTiles; ++it) {
+    const int64_t tile = (int64_t)blockIdx.x * kPackTiles + it;
+    if (tile >= a.n_tiles) break;
+    const int64_t t = tile * kTileKeys + m;
+    uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (t < a.T) {
+      kk = *reinterpret_cast<const uint4*>(a.k + t * a.k_st + (int64_t)h * a.k_sh + d8 * 8);
+      vv = *reinterpret_cast<const uint4*>(a.v + t * a.v_st + (int64_t)h * a.v_sh + d8 * 8);
+    }
+    unsigned char* out = a.tiles + ((int64_t)h * a.n_tiles + tile) * kRawTileBytes;
+    *reinterpret_cast<uint4*>(out + k_chunk_offset(m, d8)) = kk;
+    u16* vt = reinterpret_cast<u16*>(stage);
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int rec, lane, slot;
+      vt_position(m, d8 * 8 + e, rec, lane, slot);
+      const uint32_t b = (e & 1) ? (vw[e >> 1] & 0xFFFF0000u) : (vw[e >> 1] << 16);
+      vt[(rec * 64 + lane) * 8 + slot] = f16_bits(__builtin_bit_cast(float, b));
+    }
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(out + 4 * kRecBytes);
+    dst[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+    __syncthreads();
+  }
+}
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)a.n_tiles, (unsigned)a.H);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.n_tiles + kPackTiles - 1) / kPackTiles), (unsigned)a.H);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace s3r

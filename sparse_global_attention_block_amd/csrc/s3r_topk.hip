@@ -1,0 +1,186 @@
+// Top-k block selection per (head, query block).
+//
+// Speed3R technical summary (gist.science), "Methodologie" section 1: the selection branch
+// keeps, per query block, the k key blocks with the highest compression score. This kernel
+// makes that choice exactly and deterministically: order by (score descending, block index
+// ascending), output the k indices in ascending order.
+//
+// One work-group (4 waves) per score row; the row (up to 96 entries per thread) is held in
+// registers as order-preserving 32-bit keys, so the row is read from HBM once.
+//  1. Each thread's maximum key; theta = the k-th largest of those 256 maxima (bitwise search
+//     in one wave). The k largest thread maxima are k distinct entries >= theta, so every entry
+//     of the true top-k is >= theta.
+//  2. Entries >= theta (usually a few dozen) are compacted into LDS. Each candidate's rank is
+//     its number of better candidates; rank < k selects it, and its output slot is the number
+//     of selected candidates with a smaller index.
+//  3. If more than kCap candidates survive (heavy ties), an exact fallback finds the k-th key
+//     and the cut inside the tied keys by bitwise search over all entries, then writes the
+//     selected indices in ascending order with block-wide prefix counts.
+#include "s3r_common.hpp"
+#include "s3r_launch.hpp"
+
+namespace s3r {
+
+constexpr int kCap = 256;
+
+// Unsigned key whose order equals the float order; -0 is folded onto +0 first.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int sh = 1; sh < 64; sh *= 2) x += __shfl_xor(x, sh);
+  return x;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  __shared__ uint32_t tmax_s[256];
+  __shared__ uint32_t cand_key[kCap];
+  __shared__ int32_t cand_idx[kCap];
+  __shared__ int32_t cand_rank[kCap];
+  __shared__ int part[4];
+  __shared__ uint32_t s_theta;
+  __shared__ int s_count;
+
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int Nb = (int)a.Nb;
+  const int k = a.k_eff;
+  int32_t* out = a.sel + row * k;
+  if (k >= Nb) {
+    for (int j = tid; j < Nb; j += 256) out[j] = j;
+    return;
+  }
+  const float* src = a.score + row * a.ld;
+
+  uint32_t key[E];
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 256 + tid;
+    key[e] = (j < Nb) ? order_key(src[j]) : 0u;
+    if (j < Nb) tmax = key[e] > tmax ? key[e] : tmax;
+  }
+  tmax_s[tid] = tmax;
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+
+  if (wave == 0) {
+    uint32_t t4[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) t4[x] = tmax_s[lane * 4 + x];
+    uint32_t theta = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = theta | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) cnt += __popcll(__ballot(t4[x] >= cand));
+      if (cnt >= k) theta = cand;
+    }
+    if (lane == 0) s_theta = theta;
+  }
+  __syncthreads();
+  const uint32_t theta = s_theta;
+
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 256 + tid;
+    if (j < Nb && key[e] >= theta) {
+      const int pos = atomicAdd(&s_count, 1);
+      if (pos < kCap) {
+        cand_key[pos] = key[e];
+        cand_idx[pos] = j;
+      }
+    }
+  }
+  __syncthreads();
+  const int C = s_count;
+
+  if (C <= kCap) {
+    if (tid < C) {
+      const uint32_t mk = cand_key[tid];
+      const int mi = cand_idx[tid];
+      int rank = 0;
+      for (int c = 0; c < C; ++c) {
+        const uint32_t ok = cand_key[c];
+        rank += (ok > mk) || (ok == mk && cand_idx[c] < mi);
+      }
+      cand_rank[tid] = rank;
+    }
+    __syncthreads();
+    if (tid < C && cand_rank[tid] < k) {
+      const int mi = cand_idx[tid];
+      int pos = 0;
+      for (int c = 0; c < C; ++c) pos += (cand_rank[c] < k) && (cand_idx[c] < mi);
+      out[pos] = mi;
+    }
+    return;
+  }
+
+  // ---- exact fallback: k-th key by bitwise search over all entries ------------------------
+  auto block_count = [&](int local) -> int {
+    const int w = wave_sum(local);
+    __syncthreads();
+    if (lane == 0) part[wave] = w;
+    __syncthreads();
+    return part[0] + part[1] + part[2] + part[3];
+  };
+  uint32_t kth = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = kth | (1u << b);
+    int local = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) local += (e * 256 + tid < Nb) && key[e] >= cand;
+    if (block_count(local) >= k) kth = cand;
+  }
+  int greater = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) greater += (e * 256 + tid < Nb) && key[e] > kth;
+  const int need = k - block_count(greater);  // tied entries to keep, >= 1
+  // largest J with #{ties with index < J} < need: J is the index of the last tie kept
+  int J = 0;
+  for (int b = 15; b >= 0; --b) {
+    const int cand = J | (1 << b);
+    int local = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = e * 256 + tid;
+      local += (j < Nb) && key[e] == kth && j < cand;
+    }
+    if (block_count(local) < need) J = cand;
+  }
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 256 + tid;
+    const bool take = (j < Nb) && (key[e] > kth || (key[e] == kth && j <= J));
+    const uint64_t m = __ballot(take);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    __syncthreads();
+    if (lane == 0) part[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += part[w];
+    if (take) out[off + before] = j;
+    base += part[0] + part[1] + part[2] + part[3];
+  }
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  const dim3 g3((unsigned)a.n_rows), b3(256);
+  const int64_t per = (a.Nb + 255) / 256;
+  if (per <= 1) hipLaunchKernelGGL((topk_kernel<1>), g3, b3, 0, s, a);
+  else if (per <= 2) hipLaunchKernelGGL((topk_kernel<2>), g3, b3, 0, s, a);
+  else if (per <= 4) hipLaunchKernelGGL((topk_kernel<4>), g3, b3, 0, s, a);
+  else if (per <= 8) hipLaunchKernelGGL((topk_kernel<8>), g3, b3, 0, s, a);
+  else if (per <= 16) hipLaunchKernelGGL((topk_kernel<16>), g3, b3, 0, s, a);
+  else if (per <= 32) hipLaunchKernelGGL((topk_kernel<32>), g3, b3, 0, s, a);
+  else if (per <= 64) hipLaunchKernelGGL((topk_kernel<64>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((topk_kernel<96>), g3, b3, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace s3r

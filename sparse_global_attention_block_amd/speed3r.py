@@ -1,0 +1,247 @@
+"""ctypes binding of libspeed3r.so (see include/speed3r.h for every contract).
+
+Argument marshalling only: tensors are passed as device pointers with their strides, the
+current torch (HIP) stream is passed as the stream, and the status code is turned into an
+exception. All computation happens in the library's HIP kernels; if the library is missing
+this module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspeed3r.so")
+
+S3R_OK, S3R_ERR_INVALID_ARG, S3R_ERR_UNSUPPORTED, S3R_ERR_WORKSPACE, S3R_ERR_HIP = range(5)
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+        ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
+        ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
+        ("gate_stride_t", ctypes.c_int64),
+    ]
+
+
+class Speed3RError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)}")
+        self.status = status
+
+
+EXPORTS = {
+    "speed3r_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "speed3r_num_blocks": (ctypes.c_int64, [ctypes.POINTER(Params)]),
+    "speed3r_score_row_stride": (ctypes.c_int64, [ctypes.POINTER(Params)]),
+    "speed3r_tiles_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "speed3r_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "speed3r_dense_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "speed3r_sparse_attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 6 +
+                                [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "speed3r_pool": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "speed3r_cmp_lse": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "speed3r_cmp_fused": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "speed3r_topk": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]),
+    "speed3r_sel_combine": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_size_t] +
+                            [ctypes.c_void_p] * 6),
+    "speed3r_dense_attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 5 +
+                               [ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library. Raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_global_attention_block_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().speed3r_status_string(int(s)).decode()
+
+
+def _check(fn: str, st: int):
+    if st != S3R_OK:
+        raise Speed3RError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
+                scale: float = 0.0, gates: Optional[torch.Tensor] = None) -> Params:
+    """Params for [T, H, 64] bf16 token tensors (any token/head strides, last dim contiguous)."""
+    T, H, D = q.shape
+    for x in (q, k, v):
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != (T, H, D) or x.stride(2) != 1:
+            raise ValueError("q, k, v must be bf16 [T, H, D] with a contiguous last dimension")
+    gst = 0
+    if gates is not None and gates.dim() == 3:
+        gst = gates.stride(0)
+    return Params(T, H, D, block, topk, float(scale), 0, q.stride(0), q.stride(1), k.stride(0),
+                  k.stride(1), v.stride(0), v.stride(1), gst)
+
+
+def num_blocks(p: Params) -> int:
+    return int(lib().speed3r_num_blocks(ctypes.byref(p)))
+
+
+def score_row_stride(p: Params) -> int:
+    return int(lib().speed3r_score_row_stride(ctypes.byref(p)))
+
+
+def workspace_size(p: Params) -> int:
+    return int(lib().speed3r_workspace_size(ctypes.byref(p)))
+
+
+def tiles_workspace_size(p: Params) -> int:
+    return int(lib().speed3r_tiles_workspace_size(ctypes.byref(p)))
+
+
+def dense_workspace_size(p: Params) -> int:
+    return int(lib().speed3r_dense_workspace_size(ctypes.byref(p)))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator hands out 512-byte aligned blocks, more than the 256 required
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
+                    out: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Full forward pass. Returns (out [T, H, 64] bf16, sel_idx or None)."""
+    p = make_params(q, k, v, block, topk, scale, gates)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size(p), q.device)
+    st = lib().speed3r_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gates),
+                                       _ptr(out), _ptr(sel_idx), _ptr(workspace),
+                                       workspace.numel(), _stream())
+    _check("speed3r_sparse_attn_fwd", st)
+    return out, sel_idx
+
+
+def pool(p: Params, k, v, workspace, k_mean=None, v_mean=None):
+    _check("speed3r_pool", lib().speed3r_pool(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(workspace),
+                                              workspace.numel(), _ptr(k_mean), _ptr(v_mean),
+                                              _stream()))
+
+
+def cmp_lse(p: Params, q, workspace, lse):
+    _check("speed3r_cmp_lse", lib().speed3r_cmp_lse(ctypes.byref(p), _ptr(q), _ptr(workspace),
+                                                    workspace.numel(), _ptr(lse), _stream()))
+
+
+def cmp_fused(p: Params, q, workspace, lse, o_cmp, score):
+    _check("speed3r_cmp_fused", lib().speed3r_cmp_fused(
+        ctypes.byref(p), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(lse), _ptr(o_cmp),
+        _ptr(score), _stream()))
+
+
+def topk(p: Params, score, sel_idx):
+    _check("speed3r_topk", lib().speed3r_topk(ctypes.byref(p), _ptr(score), _ptr(sel_idx),
+                                              _stream()))
+
+
+def sel_combine(p: Params, q, workspace, sel_idx, o_cmp, gates, out, o_sel=None):
+    _check("speed3r_sel_combine", lib().speed3r_sel_combine(
+        ctypes.byref(p), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(sel_idx),
+        _ptr(o_cmp), _ptr(gates), _ptr(out), _ptr(o_sel), _stream()))
+
+
+def dense_attn_fwd(q, k, v, scale: float = 0.0, out=None, workspace=None):
+    p = make_params(q, k, v, 64, 1, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(dense_workspace_size(p), q.device)
+    _check("speed3r_dense_attn_fwd", lib().speed3r_dense_attn_fwd(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out
+
+
+class Stages:
+    """Runs the forward pass one stage at a time and keeps every intermediate result:
+    k_mean, v_mean [H, Nb, 64] f32, lse [H, T] f32, o_cmp [T, H, 64] f32,
+    score [H, Nb, ld] f32, sel [H, Nb, k_eff] int32, o_sel [T, H, 64] f32, out bf16."""
+
+    def __init__(self, q, k, v, gates, block: int, topk_: int, scale: float = 0.0,
+                 keep_o_sel: bool = True):
+        self.q, self.k, self.v, self.gates = q, k, v, gates
+        self.p = make_params(q, k, v, block, topk_, scale, gates)
+        T, H, D = q.shape
+        dev = q.device
+        self.Nb = num_blocks(self.p)
+        self.ld = score_row_stride(self.p)
+        self.k_eff = min(topk_, self.Nb)
+        self.ws = alloc_workspace(tiles_workspace_size(self.p), dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.k_mean = torch.empty(H, self.Nb, D, **f32)
+        self.v_mean = torch.empty(H, self.Nb, D, **f32)
+        self.lse = torch.empty(H, T, **f32)
+        self.o_cmp = torch.empty(T, H, D, **f32)
+        self.score = torch.empty(H, self.Nb, self.ld, **f32)
+        self.sel = torch.empty(H, self.Nb, self.k_eff, dtype=torch.int32, device=dev)
+        self.o_sel = torch.empty(T, H, D, **f32) if keep_o_sel else None
+        self.out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+
+    def run_pool(self):
+        pool(self.p, self.k, self.v, self.ws, self.k_mean, self.v_mean)
+
+    def run_lse(self):
+        cmp_lse(self.p, self.q, self.ws, self.lse)
+
+    def run_fused(self, lse=None):
+        cmp_fused(self.p, self.q, self.ws, self.lse if lse is None else lse, self.o_cmp,
+                  self.score)
+
+    def run_topk(self, score=None):
+        topk(self.p, self.score if score is None else score, self.sel)
+
+    def run_sel(self, sel=None, o_cmp=None):
+        sel_combine(self.p, self.q, self.ws, self.sel if sel is None else sel,
+                    self.o_cmp if o_cmp is None else o_cmp, self.gates, self.out, self.o_sel)
+
+    def run_all(self):
+        self.run_pool()
+        self.run_lse()
+        self.run_fused()
+        self.run_topk()
+        self.run_sel()
+        return self

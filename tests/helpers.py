@@ -1,0 +1,80 @@
+"""Shared helpers of the test suite: inputs on the GPU, the oracle on a host copy of the very
+same bf16 values, and the comparison rules of the parity contract."""
+from __future__ import annotations
+
+import math
+from typing import Dict
+
+import numpy as np
+import torch
+
+from oracle import oracle as O
+from sparse_global_attention_block_amd import workloads as W
+
+# Contract tolerances on the bf16 output (max-abs / mean-abs) and the score gap above which
+# selected indices must match bit for bit.
+OUT_MAX_ABS = 2e-2
+OUT_MEAN_ABS = 2e-3
+GAP = 1e-3
+
+
+def cuda_inputs(w: W.Workload, T=None, views=None) -> Dict[str, torch.Tensor]:
+    return W.make_inputs(w, device="cuda", T=T, views=views)
+
+
+def host(x: torch.Tensor) -> torch.Tensor:
+    return x.detach().to("cpu")
+
+
+def row_gaps(score_row_f32: np.ndarray, k: int) -> float:
+    """S_(k) - S_(k+1) of one oracle score row (inf if every block is kept)."""
+    if k >= score_row_f32.size:
+        return math.inf
+    s = -np.sort(-score_row_f32.astype(np.float64))
+    return float(s[k - 1] - s[k])
+
+
+def check_selection(gpu_sel: np.ndarray, ora_score: np.ndarray, ora_sel: np.ndarray, k: int):
+    """Index parity: rows whose oracle gap exceeds GAP must match exactly; on the other rows
+    every GPU-chosen block must score within GAP of the oracle's k-th score. Returns the
+    fraction of rows that were held to the exact rule and the list of differing rows."""
+    rows = gpu_sel.reshape(-1, gpu_sel.shape[-1])
+    osel = ora_sel.reshape(-1, ora_sel.shape[-1])
+    osc = ora_score.reshape(-1, ora_score.shape[-1])
+    exact, differing = 0, []
+    for r in range(rows.shape[0]):
+        gap = row_gaps(osc[r], k)
+        same = np.array_equal(rows[r], osel[r])
+        if gap > GAP:
+            exact += 1
+            assert same, f"row {r}: gap {gap:.3e} > {GAP} but GPU {rows[r]} != oracle {osel[r]}"
+        elif not same:
+            kth = -np.sort(-osc[r].astype(np.float64))[k - 1]
+            assert (osc[r][rows[r]] >= kth - GAP).all(), f"row {r}: GPU picked a far block"
+            assert np.array_equal(np.sort(rows[r]), rows[r]) and len(set(rows[r])) == len(rows[r])
+            differing.append(r)
+    return exact / max(1, rows.shape[0]), differing
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
+def check_out(gpu_out: torch.Tensor, ref: np.ndarray, what="out",
+              max_abs=OUT_MAX_ABS, mean_abs=OUT_MEAN_ABS):
+    """Compare a GPU result with the float64 oracle. For a bf16 result both bounds apply to
+    the error beyond the final rounding to bf16, excess = max(0, |gpu - ref| - half_ulp(ref)):
+    the rounding alone reaches 2e-2 once |x| >= 8 and averages ~|x|/1024, so outputs of
+    magnitude > 2 would fail a plain mean-abs bound of 2e-3 even if computed exactly.
+    f32 results are held to the plain difference. Returns the plain max and mean."""
+    g = gpu_out.detach().float().cpu().numpy().astype(np.float64)
+    d = np.abs(g - ref)
+    assert np.isfinite(d).all(), f"{what}: non-finite values"
+    excess = np.maximum(d - bf16_half_ulp(ref), 0.0) if gpu_out.dtype == torch.bfloat16 else d
+    assert excess.max() <= max_abs, \
+        f"{what}: max-abs {d.max():.3e} (beyond output rounding {excess.max():.3e}) > {max_abs}"
+    assert excess.mean() <= mean_abs, \
+        f"{what}: mean-abs {d.mean():.3e} (beyond output rounding {excess.mean():.3e}) > {mean_abs}"
+    return float(d.max()), float(d.mean())

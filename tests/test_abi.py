@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments before touching the device (every call here returns from
+validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_global_attention_block_amd import speed3r as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "speed3r.h")
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(speed3r_\w+)\s*\(", txt)))
+
+
+def test_header_symbols_are_exported():
+    L = S.lib()
+    names = declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in speed3r.h but not exported"
+    assert set(names) == set(S.EXPORTS), "binding and header disagree"
+
+
+def test_status_strings():
+    for code, name in enumerate(["S3R_OK", "S3R_ERR_INVALID_ARG", "S3R_ERR_UNSUPPORTED",
+                                 "S3R_ERR_WORKSPACE", "S3R_ERR_HIP"]):
+        assert S.status_string(code) == name
+    assert S.status_string(99) == "S3R_ERR_UNKNOWN"
+
+
+def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None):
+    st = st or (H * D, D)
+    return S.Params(T, H, D, B, k, scale, 0, st[0], st[1], st[0], st[1], st[0], st[1], 0)
+
+
+def test_size_queries():
+    p = params()
+    assert S.num_blocks(p) == 64
+    assert S.score_row_stride(p) == 64
+    p2 = params(T=1000)
+    assert S.num_blocks(p2) == 63 and S.score_row_stride(p2) == 64
+    sizes = [S.workspace_size(params(T=t)) for t in (16, 1000, 5000, 20000)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:])), "workspace must grow with T"
+    assert S.tiles_workspace_size(p) < S.workspace_size(p)
+    assert S.dense_workspace_size(p) > 0
+    # 1000 views x 1374 tokens, 16 heads, B = 64, k = 16: about 41 GB
+    big = params(T=1_374_000, H=16, B=64, k=16)
+    assert 38e9 < S.workspace_size(big) < 44e9
+    assert S.num_blocks(big) == 21469
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=32), S.S3R_ERR_UNSUPPORTED),
+    (dict(B=48), S.S3R_ERR_UNSUPPORTED),
+    (dict(B=0), S.S3R_ERR_INVALID_ARG),
+    (dict(k=0), S.S3R_ERR_INVALID_ARG),
+    (dict(T=0), S.S3R_ERR_INVALID_ARG),
+    (dict(H=0), S.S3R_ERR_INVALID_ARG),
+    (dict(scale=-1.0), S.S3R_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), S.S3R_ERR_INVALID_ARG),
+    (dict(st=(4 * 64 + 4, 64)), S.S3R_ERR_INVALID_ARG),   # token stride not a multiple of 8
+    (dict(st=(-256, 64)), S.S3R_ERR_INVALID_ARG),
+    (dict(T=24577 * 16, B=16), S.S3R_ERR_UNSUPPORTED),     # more than 24576 blocks
+])
+def test_bad_params_rejected_everywhere(kw, code):
+    p = params(**kw)
+    L = S.lib()
+    ws = ctypes.c_void_p(1 << 20)
+    big = ctypes.c_size_t(1 << 40)
+    calls = [
+        L.speed3r_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, big,
+                                  None),
+        L.speed3r_pool(ctypes.byref(p), FAKE, FAKE, ws, big, None, None, None),
+        L.speed3r_cmp_lse(ctypes.byref(p), FAKE, ws, big, FAKE, None),
+        L.speed3r_cmp_fused(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, None),
+        L.speed3r_topk(ctypes.byref(p), FAKE, FAKE, None),
+        L.speed3r_sel_combine(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, FAKE, None, None),
+        L.speed3r_dense_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws, big, None),
+    ]
+    assert calls == [code] * len(calls)
+    assert S.workspace_size(p) == 0 and S.num_blocks(p) == -1
+
+
+def test_null_and_misaligned_pointers():
+    p = params()
+    L = S.lib()
+    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.speed3r_sparse_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, big, None) \
+        == S.S3R_ERR_INVALID_ARG
+    assert L.speed3r_sparse_attn_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None, ws,
+                                     big, None) == S.S3R_ERR_INVALID_ARG
+    assert L.speed3r_sparse_attn_fwd(ctypes.byref(p), odd, FAKE, FAKE, FAKE, FAKE, None, ws, big,
+                                     None) == S.S3R_ERR_INVALID_ARG
+    assert L.speed3r_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, None, ws,
+                                     big, None) == S.S3R_ERR_INVALID_ARG
+    assert L.speed3r_topk(ctypes.byref(p), None, FAKE, None) == S.S3R_ERR_INVALID_ARG
+    assert L.speed3r_cmp_lse(ctypes.byref(p), FAKE, ws, big, None, None) == S.S3R_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_or_missing():
+    p = params()
+    L = S.lib()
+    need = S.workspace_size(p)
+    ws = ctypes.c_void_p(1 << 20)
+    for w, n in ((ws, need - 1), (None, need), (ctypes.c_void_p((1 << 20) + 128), need)):
+        assert L.speed3r_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, w,
+                                         n, None) == S.S3R_ERR_WORKSPACE
+    tiles = S.tiles_workspace_size(p)
+    assert L.speed3r_pool(ctypes.byref(p), FAKE, FAKE, ws, tiles - 1, None, None, None) \
+        == S.S3R_ERR_WORKSPACE
+    assert L.speed3r_dense_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws,
+                                    S.dense_workspace_size(p) - 1, None) == S.S3R_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(S, "_lib", None)
+    monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        S.lib()
