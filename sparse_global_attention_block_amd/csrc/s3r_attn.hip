@@ -259,18 +259,17 @@ __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
 
   Flash<4> f;
   f.init();
-  uint4 stg[2];
-  stg[0] = tiles[tid];
-  stg[1] = tiles[256 + tid];
-  lds[0][tid] = stg[0];
-  lds[0][256 + tid] = stg[1];
+  uint4 s0 = tiles[tid], s1 = tiles[256 + tid];
+  lds[0][tid] = s0;
+  lds[0][256 + tid] = s1;
   __syncthreads();
   for (int64_t tau = 0; tau < a.n_tiles; ++tau) {
     const int buf = (int)(tau & 1);
-    const bool has_next = tau + 1 < a.n_tiles;
-    if (has_next) {
-      stg[0] = tiles[(tau + 1) * kTileU4 + tid];
-      stg[1] = tiles[(tau + 1) * kTileU4 + 256 + tid];
+    {
+      // prefetch the next tile (the last iteration re-reads its own tile; nobody consumes it)
+      const int64_t nxt = (tau + 1 < a.n_tiles) ? tau + 1 : tau;
+      s0 = tiles[nxt * kTileU4 + tid];
+      s1 = tiles[nxt * kTileU4 + 256 + tid];
     }
     bf16x8 rec[8];
     const bf16x8* L = reinterpret_cast<const bf16x8*>(lds[buf]);
@@ -279,10 +278,8 @@ __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
     const int64_t t0 = tau * kTileKeys;
     const int hi = (int)((a.T - t0 < kTileKeys) ? a.T - t0 : kTileKeys);
     f.step(rec, qb, 0, hi, a.logit_mult, g);
-    if (has_next) {
-      lds[buf ^ 1][tid] = stg[0];
-      lds[buf ^ 1][256 + tid] = stg[1];
-    }
+    lds[buf ^ 1][tid] = s0;
+    lds[buf ^ 1][256 + tid] = s1;
     __syncthreads();
   }
   float inv[4];

@@ -8,32 +8,48 @@
 //   pass 1 (cmp_lse):   L_t = log sum_j exp(c_tj)
 //   pass 2 (cmp_fused): P_tj = exp(c_tj - L_t), O_cmp_t = sum_j P_tj Vc_j,
 //                       Score[i][j] = sum_{t in block i} P_tj
-// with c_tj = scale * q_t . Kc_j. Both passes are MFMA-bound (bf16 16x16x32, f32 accumulate).
+// with c_tj = scale * q_t . Kc_j. Both passes are MFMA-bound (16x16x32, f32 accumulate).
 //
 // Work decomposition: a work-group of 4 waves owns 256 consecutive queries of one head; each
 // wave holds 64 queries (4 column tiles of 16) as resident B operands and streams the pooled
-// tiles (32 coarse tokens each) through a double-buffered LDS ring. The accumulator tile is
-// S^T (keys x queries): lane l holds query l%16 and keys 4*(l/16)+r, so P feeds the P.V MFMA
-// directly as its B operand (in fp16, against fp16 pooled values). The pooled keys arrive
-// pre-multiplied by scale*log2(e) as bf16 hi + lo, so logits come out in base-2 units; the query's offset (-running max in pass 1,
-// -L_t*log2(e) in pass 2) is the MFMA's C input, leaving one exp2 per logit on the VALU.
+// tiles (32 coarse tokens each) through a 3-slot LDS ring. The accumulator tile is S^T (keys x
+// queries): lane l holds query l%16 and keys 4*(l/16)+r, so P feeds the P.V MFMA directly as
+// its B operand (in fp16, against fp16 pooled values). The pooled keys arrive pre-multiplied
+// by scale*log2(e) as bf16 hi + lo, so logits come out in base-2 units; the query's offset
+// (-running offset in pass 1, -L_t*log2(e) in pass 2) is the MFMA's C input, leaving one exp2
+// per logit on the VALU.
+//
+// Software pipeline (pass 2): while the VALU works on the probabilities of tile t, the logits
+// of tile t+1 are already being computed on the matrix cores (two accumulator sets alternate),
+// and tile t+2 is on its way from memory. The ring slot of tile t is only rewritten after the
+// barrier that ends iteration t+1, when no wave reads it any more. Pass 1 has less VALU work
+// per tile and runs unpipelined with more resident waves instead.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
 namespace s3r {
 
-constexpr int kCmpWaves = 4;
-constexpr int kCmpQueries = 64 * kCmpWaves;
+constexpr int kLseWaves = 4;
+constexpr int kFusedWaves = 4;
 
 // kQB: query blocks per wave (64 / B for B <= 64, else 1; B = 128 blocks span two waves and
 // their scores are completed with a second atomic add onto a zeroed matrix).
-template <bool kFused, int kQB>
-__global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
+// kPipe: overlap the logits of tile t+1 with the probabilities of tile t inside one wave
+// (two accumulator sets, 3-slot ring); without it the kernel needs fewer registers and relies
+// on more resident waves per SIMD for the same overlap.
+template <bool kFused, int kQB, int kWaves, bool kPipe>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void cmp_kernel(CmpArgs a) {
+  constexpr int kRing = kPipe ? 3 : 2;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kQueries = 64 * kWaves;
   constexpr int kTileU4 = (kFused ? 12 : 8) * kRecBytes / 16;  // bytes of a tile this pass reads
-  constexpr int kLoads = kTileU4 / 256;
-  __shared__ uint4 lds[2][kTileU4];
+  constexpr int kLoads = kTileU4 / kThreads;
+  static_assert(kLoads * kThreads == kTileU4 && kLoads <= 3, "whole staging registers");
+  constexpr int kTileStrideU4 = kPooledTileBytes / 16;
+  constexpr int kNtPerQB = 4 / kQB;
+  __shared__ uint4 lds[kRing][kTileU4];
 
-  const int64_t n_qtiles = (a.T + kCmpQueries - 1) / kCmpQueries;
+  const int64_t n_qtiles = (a.T + kQueries - 1) / kQueries;
   const int64_t total = (int64_t)a.H * n_qtiles;
   const int64_t logical = xcd_logical_id(blockIdx.x, total);
   if (logical >= total) return;
@@ -41,7 +57,8 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
   const int64_t qt = logical % n_qtiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t q0 = qt * kCmpQueries + wave * 64;
+  const int64_t q0 = qt * kQueries + wave * 64;
+  const int64_t n = a.n_tiles;
 
   // Resident query operands: column tile nt, dim chunk c.
   bf16x8 qb[4][2];
@@ -59,12 +76,8 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
     }
   }
 
-  const uint4* tiles = reinterpret_cast<const uint4*>(a.tiles) +
-                       (int64_t)h * a.n_tiles * (kPooledTileBytes / 16);
-  constexpr int kTileStrideU4 = kPooledTileBytes / 16;
-
   // Per-lane softmax state. Pass 1: running offset m (base 2) and partial sum l of this lane's
-  // keys; pass 2: the fixed offset L_t*log2(e).
+  // keys; pass 2: the fixed offset L_t*log2(e) (+inf for a query past the end: P = 0).
   float off[4], lsum[4];
   floatx4 cneg[4];
 #pragma unroll
@@ -86,26 +99,23 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
       for (int nt = 0; nt < 4; ++nt) o[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint4 stg[kLoads];
-#pragma unroll
-  for (int r = 0; r < kLoads; ++r) stg[r] = tiles[r * 256 + tid];
-#pragma unroll
-  for (int r = 0; r < kLoads; ++r) lds[0][r * 256 + tid] = stg[r];
-  __syncthreads();
+  const uint4* tiles = reinterpret_cast<const uint4*>(a.tiles) + (int64_t)h * n * kTileStrideU4;
+  // Staging registers of one tile (named, not an array, so that they stay in VGPRs).
+  uint4 s0 = make_uint4(0, 0, 0, 0), s1 = s0, s2 = s0;
+  auto fetch = [&](int64_t t) {
+    const uint4* src = tiles + t * kTileStrideU4;
+    s0 = src[tid];
+    if constexpr (kLoads > 1) s1 = src[kThreads + tid];
+    if constexpr (kLoads > 2) s2 = src[2 * kThreads + tid];
+  };
+  auto stash = [&](int slot) {
+    lds[slot][tid] = s0;
+    if constexpr (kLoads > 1) lds[slot][kThreads + tid] = s1;
+    if constexpr (kLoads > 2) lds[slot][2 * kThreads + tid] = s2;
+  };
 
-  constexpr int kNtPerQB = 4 / kQB;
-
-  for (int64_t tau = 0; tau < a.n_tiles; ++tau) {
-    const int buf = (int)(tau & 1);
-    const bool has_next = tau + 1 < a.n_tiles;
-    if (has_next) {
-      const uint4* src = tiles + (tau + 1) * kTileStrideU4;
-#pragma unroll
-      for (int r = 0; r < kLoads; ++r) stg[r] = src[r * 256 + tid];
-    }
-    const uint4* L = lds[buf];
-
-    floatx4 acc[2][4];
+  // S^T of one tile: keys (16 per half s2) x queries (16 per column tile nt), offset applied.
+  auto qk = [&](const uint4* L, floatx4 (&acc)[2][4]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(&L[(2 * s2 + 0) * 64 + lane]);
@@ -114,13 +124,17 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
       const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 1) * 64 + lane]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        floatx4 x = mfma16(h0, qb[nt][0], cneg[nt]);
+        // pass 2 subtracts its fixed offset on the VALU (no C registers held across tiles)
+        floatx4 x = mfma16(h0, qb[nt][0], kFused ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[nt]);
         x = mfma16(h1, qb[nt][1], x);
         x = mfma16(l0, qb[nt][0], x);
         acc[s2][nt] = mfma16(l1, qb[nt][1], x);
       }
     }
-    if (tau == a.n_tiles - 1) {
+  };
+
+  auto process = [&](int64_t tau, const uint4* L, floatx4 (&acc)[2][4], bool last) {
+    if (last) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -132,18 +146,17 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
           }
         }
     }
-
     if constexpr (!kFused) {
-      // ---- pass 1: partial sums with a lazily moved offset -------------------------------
+      // ---- pass 1: partial sums with a lazily moved offset -----------------------------
       bool bad = false;
       float prev[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        float s = 0.f;
+        float s = fast_exp2(acc[0][nt][0]);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s += fast_exp2(acc[s2][nt][r]);
+          for (int r = (s2 == 0 ? 1 : 0); r < 4; ++r) s += fast_exp2(acc[s2][nt][r]);
         prev[nt] = lsum[nt];
         lsum[nt] += s;
         // the sum must stay inside [2^-64, 2^64]: otherwise move the offset to this tile's max
@@ -174,24 +187,23 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
         }
       }
     } else {
-      // ---- pass 2: probabilities, P.V and block scores -----------------------------------
+      // ---- pass 2: probabilities, P.V and block scores ---------------------------------
       float p[2][4][4];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[s2][nt][r] = fast_exp2(acc[s2][nt][r]);
-      halfx8 pb[4];
+          for (int r = 0; r < 4; ++r) p[s2][nt][r] = fast_exp2(acc[s2][nt][r] - off[nt]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        pb[nt] = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3], p[1][nt][0],
-                        p[1][nt][1], p[1][nt][2], p[1][nt][3]);
+      for (int nt = 0; nt < 4; ++nt) {
+        const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
+                                 p[1][nt][0], p[1][nt][1], p[1][nt][2], p[1][nt][3]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const halfx8 vt = *reinterpret_cast<const halfx8*>(&L[512 + mt * 64 + lane]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma16h(vt, pb[nt], o[mt][nt]);
+        for (int mt = 0; mt < 4; ++mt) {
+          const halfx8 vt = *reinterpret_cast<const halfx8*>(&L[512 + mt * 64 + lane]);
+          o[mt][nt] = mfma16h(vt, pb, o[mt][nt]);
+        }
       }
       // column sums over the queries of each query block
 #pragma unroll
@@ -201,10 +213,9 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float s = 0.f;
+            float s = p[s2][qb * kNtPerQB][r];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              if (nt >= qb * kNtPerQB && nt < (qb + 1) * kNtPerQB) s += p[s2][nt][r];
+            for (int nt = qb * kNtPerQB + 1; nt < (qb + 1) * kNtPerQB; ++nt) s += p[s2][nt][r];
             v[s2][r] = s;
           }
         const float tot = row_reduce_scatter8(v, lane);
@@ -220,12 +231,56 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
         }
       }
     }
+  };
 
-    if (has_next) {
-#pragma unroll
-      for (int r = 0; r < kLoads; ++r) lds[buf ^ 1][r * 256 + tid] = stg[r];
-    }
+  // One pipeline step (t < n - 1): fetch tile t+2, logits of tile t+1, probabilities of
+  // tile t. Branch-free, so the matrix-core work of t+1 and the VALU work of t share one
+  // basic block and interleave. The last tile is peeled off (it alone needs key masking).
+  auto body = [&](int64_t tau, floatx4 (&cur)[2][4], floatx4 (&nxt)[2][4]) {
+    fetch((tau + 2 < n) ? tau + 2 : n - 1);
+    // keep the prefetch at the top of the step: its latency hides behind the whole step
+    __builtin_amdgcn_sched_barrier(0);
+    qk(lds[(int)((tau + 1) % kRing)], nxt);
+    process(tau, lds[(int)(tau % kRing)], cur, false);
+    stash((int)((tau + 2) % kRing));
     __syncthreads();
+  };
+
+  if constexpr (kPipe) {
+    fetch(0);
+    stash(0);
+    fetch(n > 1 ? 1 : 0);
+    stash(1);
+    __syncthreads();
+    floatx4 accA[2][4], accB[2][4];
+    qk(lds[0], accA);
+    int64_t tau = 0;
+    for (; tau + 2 < n; tau += 2) {
+      body(tau, accA, accB);
+      body(tau + 1, accB, accA);
+    }
+    if (tau + 1 < n) {  // two tiles left: tau, tau + 1
+      body(tau, accA, accB);
+      process(tau + 1, lds[(int)((tau + 1) % kRing)], accB, true);
+    } else {            // one tile left
+      process(tau, lds[(int)(tau % kRing)], accA, true);
+    }
+  } else {
+    // one tile per step: fetch t+1, logits and probabilities of t, 2-slot ring
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    floatx4 acc[2][4];
+    for (int64_t tau = 0; tau + 1 < n; ++tau) {
+      fetch(tau + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      qk(lds[(int)(tau & 1)], acc);
+      process(tau, lds[(int)(tau & 1)], acc, false);
+      stash((int)((tau + 1) & 1));
+      __syncthreads();
+    }
+    qk(lds[(int)((n - 1) & 1)], acc);
+    process(n - 1, lds[(int)((n - 1) & 1)], acc, true);
   }
 
   if constexpr (!kFused) {
@@ -261,19 +316,23 @@ __global__ __launch_bounds__(256) void cmp_kernel(CmpArgs a) {
   }
 }
 
+static dim3 cmp_grid(const CmpArgs& a, int waves) {
+  const int64_t q = 64 * waves;
+  const int64_t total = (int64_t)a.H * ((a.T + q - 1) / q);
+  return dim3((unsigned)(((total + 7) / 8) * 8));
+}
+
 static hipError_t launch_cmp(const CmpArgs& a, hipStream_t s, bool fused) {
-  const int64_t n_qtiles = (a.T + kCmpQueries - 1) / kCmpQueries;
-  const int64_t total = (int64_t)a.H * n_qtiles;
-  const int64_t grid = ((total + 7) / 8) * 8;
-  const dim3 g3((unsigned)grid), b3(256);
   if (fused) {
+    const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
     switch (a.B) {
-      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4>), g3, b3, 0, s, a); break;
-      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2>), g3, b3, 0, s, a); break;
-      default: hipLaunchKernelGGL((cmp_kernel<true, 1>), g3, b3, 0, s, a); break;
+      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true>), g3, b3, 0, s, a); break;
+      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true>), g3, b3, 0, s, a); break;
+      default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true>), g3, b3, 0, s, a); break;
     }
   } else {
-    hipLaunchKernelGGL((cmp_kernel<false, 1>), g3, b3, 0, s, a);
+    hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false>), cmp_grid(a, kLseWaves),
+                       dim3(64 * kLseWaves), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -56,13 +56,21 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   }
   const float* src = a.score + row * a.ld;
 
+  // All E loads are issued before any is used: the index is clamped instead of branched on,
+  // so no load waits behind a bounds check.
+  float raw[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 256 + tid;
+    raw[e] = src[j < Nb ? j : Nb - 1];
+  }
   uint32_t key[E];
   uint32_t tmax = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    key[e] = (j < Nb) ? order_key(src[j]) : 0u;
-    if (j < Nb) tmax = key[e] > tmax ? key[e] : tmax;
+    key[e] = (j < Nb) ? order_key(raw[e]) : 0u;
+    tmax = key[e] > tmax ? key[e] : tmax;
   }
   tmax_s[tid] = tmax;
   if (tid == 0) s_count = 0;
