@@ -10,6 +10,7 @@ shape. Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v1000_k16]
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -52,6 +53,25 @@ def algorithmic_work(w: W.Workload, T: int, Nb: int):
         # q.k and p.v over the k*B selected tokens: 4*D flops per (token, head, key)
         "sel": {"flops": 4 * D * th * sel_keys, "bound": "mfma"},
     }
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the compressed-attention pass-2 kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy calibration). None
+    when no summary exists for this workload or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("s3r_cmp.hip", "s3r_common.hpp"):
+        h.update(open(os.path.join(ROOT, "sparse_global_attention_block_amd", "csrc", f), "rb").read())
+    if rec.get("cmp_fused_source_sha256") != h.hexdigest():
+        return None
+    for name, v in rec["kernels"].items():
+        if name.startswith("s3r::cmp_kernel<true"):
+            return v["read_bytes"] + v["write_bytes"]
+    return None
 
 
 def timed_stages(st: "S.Stages", reps: int):
@@ -128,7 +148,19 @@ def main():
     ap.add_argument("--dense-reps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB (the reference kernel "
+                         "for scaling HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -195,7 +227,7 @@ def main():
     dom = max(("cmp_fused", "cmp_lse", "sel"), key=lambda n: stage_ms[n])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
-            "traffic": None}
+            "traffic": measured_traffic(w.name) if dom == "cmp_fused" else None}
     del st
     torch.cuda.empty_cache()
 
