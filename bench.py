@@ -77,8 +77,12 @@ def measured_traffic(workload: str):
 def timed_stages(st: "S.Stages", reps: int):
     """Runs the hot path stage by stage with HIP events between stages (on the stream the
     library launches on) and returns the mean duration of each stage in ms."""
-    names = ["pool", "cmp_lse", "cmp_fused", "topk", "sel"]
-    fns = [st.run_pool, st.run_lse, st.run_fused, st.run_topk, st.run_sel]
+    if st.folds_topk:  # the path speed3r_sparse_attn_fwd takes: top-k inside pass 2
+        names = ["pool", "cmp_lse", "cmp_fused", "sel"]
+        fns = [st.run_pool, st.run_lse, st.run_fused_topk, st.run_sel]
+    else:
+        names = ["pool", "cmp_lse", "cmp_fused", "topk", "sel"]
+        fns = [st.run_pool, st.run_lse, st.run_fused, st.run_topk, st.run_sel]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
     torch.cuda.synchronize()
     for r in range(reps):
@@ -204,8 +208,11 @@ def main():
     # per-kernel durations: the same kernels launched stage by stage
     del ws
     torch.cuda.empty_cache()
-    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, keep_o_sel=False)
-    st.run_all()
+    folds = w.block <= 64 and w.k_eff <= 64
+    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, keep_o_sel=False,
+                  keep_score=not folds)
+    st.run_pool()
+    st.run_lse()
     stage_ms = timed_stages(st, max(1, min(3, args.steps)))
     log(f"[bench] stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
     work = algorithmic_work(w, T, Nb)

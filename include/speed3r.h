@@ -80,8 +80,9 @@ int64_t speed3r_score_row_stride(const s3r_params* p);
 size_t speed3r_tiles_workspace_size(const s3r_params* p);
 
 /* Bytes of workspace speed3r_sparse_attn_fwd needs: the tiles plus LSE [H][T] f32, O_cmp
- * [T][H][64] f32, the score matrix [H][Nb][ld] f32 and the selected indices. About 41 GB at
- * T = 1,374,000, H = 16, B = 64. 0 if p is invalid. */
+ * [T][H][64] f32, the selected indices and, only when the selection cannot be folded into
+ * the compression pass (B = 128 or k_eff > 64), the score matrix [H][Nb][ld] f32. About 11.5
+ * GB at T = 1,374,000, H = 16, B = 64, k = 16. 0 if p is invalid. */
 size_t speed3r_workspace_size(const s3r_params* p);
 
 /* Bytes of workspace speed3r_dense_attn_fwd needs (packed raw keys and values). */
@@ -89,7 +90,8 @@ size_t speed3r_dense_workspace_size(const s3r_params* p);
 
 /* The whole sparse forward pass (the method of the summary's "Methodologie" sections 1-2):
  * pool -> compressed LSE -> compressed output + block scores -> top-k -> selection attention
- * with the gate-combine epilogue.
+ * with the gate-combine epilogue. When B <= 64 and k_eff <= 64 the scores never leave the chip
+ * (speed3r_cmp_fused_topk); otherwise they go through the score matrix and speed3r_topk.
  *   gates    f32, [H][2] or per token (see gate_stride_t); column 0 multiplies the
  *            compression branch, column 1 the selection branch.
  *   out      bf16 [T][H][64], contiguous.
@@ -128,6 +130,17 @@ s3r_status speed3r_cmp_lse(const s3r_params* p, const void* q, const void* works
 s3r_status speed3r_cmp_fused(const s3r_params* p, const void* q, const void* workspace,
                              size_t workspace_bytes, const float* lse, float* o_cmp,
                              float* score, hipStream_t stream);
+
+/* Compression branch, second pass with the selection folded in (the page's kernel keeps top-k
+ * and softmax on chip without materialising the score matrix, summary "Methodologie" 4):
+ * computes o_cmp exactly as speed3r_cmp_fused and, instead of the score matrix, keeps the
+ * running top-k of each query block while the key blocks stream by, writing sel_idx [H][Nb]
+ * [k_eff] in ascending order. The choice equals speed3r_topk applied to the score matrix
+ * speed3r_cmp_fused writes, bit for bit. Requires B <= 64 and k_eff <= 64
+ * (S3R_ERR_UNSUPPORTED otherwise). */
+s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void* workspace,
+                                  size_t workspace_bytes, const float* lse, float* o_cmp,
+                                  int32_t* sel_idx, hipStream_t stream);
 
 /* Top-k selection (summary "Methodologie" 1, selection guided by the compression scores):
  * sel_idx[(h*Nb + i)*k_eff + a] = the k_eff largest entries of score row (h, i) by (value

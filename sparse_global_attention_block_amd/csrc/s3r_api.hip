@@ -19,6 +19,7 @@ struct Dims {
   int64_t T, Nb, n_ctiles, n_ktiles, ld, k_eff;
   int32_t H, B;
   float scale;
+  bool fold_topk;  // selection folded into the compression pass (no score matrix)
 };
 
 // Workspace regions, in this order, each 256-byte aligned.
@@ -52,6 +53,7 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->ld = d->n_ctiles * kTileKeys;
   d->k_eff = p->topk < d->Nb ? p->topk : d->Nb;
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)kD);
+  d->fold_topk = d->B <= 64 && d->k_eff <= kFusedTopkMaxK;
   return S3R_OK;
 }
 
@@ -68,7 +70,7 @@ Layout layout(const Dims& d) {
   L.o_cmp = off;
   off += align256((size_t)d.T * d.H * kD * sizeof(float));
   L.score = off;
-  off += align256((size_t)d.H * d.Nb * d.ld * sizeof(float));
+  if (!d.fold_topk) off += align256((size_t)d.H * d.Nb * d.ld * sizeof(float));
   L.sel = off;
   off += align256((size_t)d.H * d.Nb * d.k_eff * sizeof(int32_t));
   L.end = off;
@@ -226,6 +228,26 @@ s3r_status speed3r_cmp_fused(const s3r_params* p, const void* q, const void* wor
   return run_cmp_fused(d, a, stream);
 }
 
+s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void* workspace,
+                                  size_t workspace_bytes, const float* lse, float* o_cmp,
+                                  int32_t* sel_idx, hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  if (!tok_ok(q) || !lse || !aligned(lse, 4) || !o_cmp || !aligned(o_cmp, 16) || !sel_idx ||
+      !aligned(sel_idx, 4))
+    return S3R_ERR_INVALID_ARG;
+  if (!d.fold_topk) return S3R_ERR_UNSUPPORTED;
+  const Layout L = layout(d);
+  if ((st = check_ws(workspace, workspace_bytes, L.tiles_end)) != S3R_OK) return st;
+  CmpArgs a = cmp_args(p, d, q, workspace, L);
+  a.lse_in = lse;
+  a.o_cmp = o_cmp;
+  a.sel = sel_idx;
+  a.k_eff = (int32_t)d.k_eff;
+  return hip_status(launch_cmp_fused_topk(a, stream));
+}
+
 s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_idx,
                         hipStream_t stream) {
   Dims d;
@@ -284,12 +306,18 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
   if ((st = hip_status(launch_cmp_lse(c, stream))) != S3R_OK) return st;
   c.lse_in = lse;
   c.o_cmp = o_cmp;
-  c.score = score;
-  if ((st = run_cmp_fused(d, c, stream)) != S3R_OK) return st;
-  TopkArgs t;
-  t.score = score; t.ld = d.ld; t.Nb = d.Nb; t.n_rows = (int64_t)d.H * d.Nb;
-  t.k_eff = (int32_t)d.k_eff; t.sel = sel;
-  if ((st = hip_status(launch_topk(t, stream))) != S3R_OK) return st;
+  if (d.fold_topk) {
+    c.sel = sel;
+    c.k_eff = (int32_t)d.k_eff;
+    if ((st = hip_status(launch_cmp_fused_topk(c, stream))) != S3R_OK) return st;
+  } else {
+    c.score = score;
+    if ((st = run_cmp_fused(d, c, stream)) != S3R_OK) return st;
+    TopkArgs t;
+    t.score = score; t.ld = d.ld; t.Nb = d.Nb; t.n_rows = (int64_t)d.H * d.Nb;
+    t.k_eff = (int32_t)d.k_eff; t.sel = sel;
+    if ((st = hip_status(launch_topk(t, stream))) != S3R_OK) return st;
+  }
   AttnArgs a = attn_args(p, d, q, ws + L.raw);
   a.sel = sel; a.o_cmp = o_cmp; a.gates = gates; a.o_sel = nullptr; a.out = (uint16_t*)out;
   return hip_status(launch_sel(a, stream));

@@ -37,7 +37,12 @@ constexpr int kFusedWaves = 4;
 // kPipe: overlap the logits of tile t+1 with the probabilities of tile t inside one wave
 // (two accumulator sets, 3-slot ring); without it the kernel needs fewer registers and relies
 // on more resident waves per SIMD for the same overlap.
-template <bool kFused, int kQB, int kWaves, bool kPipe>
+// kTopk (pass 2, B <= 64, k <= 64): instead of writing the score matrix, each wave keeps the
+// running top-k of its query block(s) in registers, one entry per lane, and writes the chosen
+// indices at the end. The entries are ordered by (score desc, block index asc), a total order,
+// so the final set does not depend on the order in which blocks arrive, and the decision is
+// made on exactly the f32 column sums the score matrix would have held.
+template <bool kFused, int kQB, int kWaves, bool kPipe, bool kTopk = false>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void cmp_kernel(CmpArgs a) {
   constexpr int kRing = kPipe ? 3 : 2;
   constexpr int kThreads = 64 * kWaves;
@@ -91,6 +96,22 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     lsum[nt] = 0.f;
     cneg[nt] = floatx4{-off[nt], -off[nt], -off[nt], -off[nt]};
   }
+  // running top-k: lane e holds entry e (score, block index) of each query block's list;
+  // th_v / th_j mirror entry K-1 (the current k-th best) in scalar registers
+  float tk_v[kQB], th_v[kQB];
+  int tk_j[kQB], th_j[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    tk_v[qb] = -1.0f;  // below every score (scores are sums of probabilities, >= 0)
+    tk_j[qb] = 0x7FFFFFFF;
+    th_v[qb] = -1.0f;
+    th_j[qb] = 0x7FFFFFFF;
+  }
+  const int K = a.k_eff;
+  auto better = [](float v1, int j1, float v2, int j2) {
+    return v1 > v2 || (v1 == v2 && j1 < j2);
+  };
+
   floatx4 o[4][4];
   if constexpr (kFused) {
 #pragma unroll
@@ -220,7 +241,36 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
           }
         const float tot = row_reduce_scatter8(v, lane);
         const int64_t qblk = (q0 + 16 * qb * kNtPerQB) / a.B;
-        if (((lane & 2) == 0) && qblk < a.Nb) {
+        if constexpr (kTopk) {
+          if (qblk < a.Nb) {
+            // lanes with bit 1 clear hold the 32 distinct keys of this tile; a block can only
+            // enter the list if its score is >= the current k-th score (one compare per tile)
+            const int j = (int)(tau * kTileKeys) + reduced_key(lane);
+            const bool mine = ((lane & 2) == 0) && j < a.Nb;
+            uint64_t cand = __ballot(mine && tot >= th_v[qb]);
+            while (cand) {  // rare after the first tiles
+              const int c = __builtin_ctzll(cand);
+              cand &= cand - 1;
+              const float cv = __builtin_bit_cast(
+                  float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tot), c));
+              const int cj = __builtin_amdgcn_readlane(j, c);
+              if (!better(cv, cj, th_v[qb], th_j[qb])) continue;
+              const bool ahead = lane < K && better(tk_v[qb], tk_j[qb], cv, cj);
+              const int pos = __popcll(__ballot(ahead));
+              // shift entries pos.. one lane up (DPP wave_shr:1), then place the new one
+              const float up_v = __builtin_bit_cast(
+                  float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, tk_v[qb]),
+                                                     kDppWaveShr1, 0xF, 0xF, false));
+              const int up_j = __builtin_amdgcn_update_dpp(0, tk_j[qb], kDppWaveShr1, 0xF, 0xF,
+                                                           false);
+              tk_v[qb] = lane == pos ? cv : (lane > pos ? up_v : tk_v[qb]);
+              tk_j[qb] = lane == pos ? cj : (lane > pos ? up_j : tk_j[qb]);
+              th_v[qb] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                       __builtin_bit_cast(int, tk_v[qb]), K - 1));
+              th_j[qb] = __builtin_amdgcn_readlane(tk_j[qb], K - 1);
+            }
+          }
+        } else if (((lane & 2) == 0) && qblk < a.Nb) {
           float* dst = a.score + ((int64_t)h * a.Nb + qblk) * a.ld + tau * kTileKeys +
                        reduced_key(lane);
           if (a.B > 64) {
@@ -302,6 +352,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       if (g == 0 && t < a.T) a.lse[(int64_t)h * a.T + t] = (m + __log2f(l)) * kLn2;
     }
   } else {
+    if constexpr (kTopk) {
+      // the chosen blocks of each query block, in ascending index order
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int64_t qblk = (q0 + 16 * qb * kNtPerQB) / a.B;
+        if (qblk < a.Nb) {
+          int rank = 0;
+          for (int m = 0; m < K; ++m) rank += __builtin_amdgcn_readlane(tk_j[qb], m) < tk_j[qb];
+          if (lane < K) a.sel[((int64_t)h * a.Nb + qblk) * K + rank] = tk_j[qb];
+        }
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int64_t t = q0 + 16 * nt + li;
@@ -339,5 +401,15 @@ static hipError_t launch_cmp(const CmpArgs& a, hipStream_t s, bool fused) {
 
 hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, false); }
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, true); }
+
+hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s) {
+  const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
+  switch (a.B) {
+    case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, true>), g3, b3, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, true>), g3, b3, 0, s, a); break;
+    default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, true>), g3, b3, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace s3r

@@ -101,13 +101,14 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
 }
 
 // ---------------------------------------------------------------------------------------
-// DPP lane exchanges (gfx9 encodings). All of them stay inside a row of 16 lanes.
+// DPP lane exchanges (gfx9 encodings). All but the wave shift stay inside a row of 16 lanes.
 // ---------------------------------------------------------------------------------------
 enum : int {
   kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
   kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
   kDppRor8 = 0x128,       // row_ror:8  (lane i <- i^8 inside a 16-lane row)
   kDppHalfMirror = 0x141, // row_half_mirror (lane i <- 7-i inside each 8-lane half)
+  kDppWaveShr1 = 0x138,   // wave_shr:1 (lane i <- lane i-1 across the whole wave)
 };
 
 template <int kCtrl>

@@ -36,6 +36,8 @@ struct CmpArgs {
   float* o_cmp;            // [T][H][64]
   float* score;            // [H][Nb][ld]
   int64_t ld;
+  int32_t* sel;            // running top-k output [H][Nb][k_eff] (fused selection only)
+  int32_t k_eff;
 };
 
 struct TopkArgs {
@@ -66,6 +68,8 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s);
+hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s);
+constexpr int kFusedTopkMaxK = 64;  // the running top-k keeps one entry per lane
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sel(const AttnArgs& a, hipStream_t s);
 hipError_t launch_dense(const AttnArgs& a, hipStream_t s);

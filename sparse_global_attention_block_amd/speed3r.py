@@ -55,6 +55,9 @@ EXPORTS = {
     "speed3r_cmp_fused": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "speed3r_cmp_fused_topk": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "speed3r_topk": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]),
     "speed3r_sel_combine": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
@@ -173,6 +176,12 @@ def cmp_fused(p: Params, q, workspace, lse, o_cmp, score):
         _ptr(score), _stream()))
 
 
+def cmp_fused_topk(p: Params, q, workspace, lse, o_cmp, sel_idx):
+    _check("speed3r_cmp_fused_topk", lib().speed3r_cmp_fused_topk(
+        ctypes.byref(p), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(lse), _ptr(o_cmp),
+        _ptr(sel_idx), _stream()))
+
+
 def topk(p: Params, score, sel_idx):
     _check("speed3r_topk", lib().speed3r_topk(ctypes.byref(p), _ptr(score), _ptr(sel_idx),
                                               _stream()))
@@ -202,7 +211,7 @@ class Stages:
     score [H, Nb, ld] f32, sel [H, Nb, k_eff] int32, o_sel [T, H, 64] f32, out bf16."""
 
     def __init__(self, q, k, v, gates, block: int, topk_: int, scale: float = 0.0,
-                 keep_o_sel: bool = True):
+                 keep_o_sel: bool = True, keep_score: bool = True):
         self.q, self.k, self.v, self.gates = q, k, v, gates
         self.p = make_params(q, k, v, block, topk_, scale, gates)
         T, H, D = q.shape
@@ -216,7 +225,7 @@ class Stages:
         self.v_mean = torch.empty(H, self.Nb, D, **f32)
         self.lse = torch.empty(H, T, **f32)
         self.o_cmp = torch.empty(T, H, D, **f32)
-        self.score = torch.empty(H, self.Nb, self.ld, **f32)
+        self.score = torch.empty(H, self.Nb, self.ld, **f32) if keep_score else None
         self.sel = torch.empty(H, self.Nb, self.k_eff, dtype=torch.int32, device=dev)
         self.o_sel = torch.empty(T, H, D, **f32) if keep_o_sel else None
         self.out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
@@ -233,6 +242,15 @@ class Stages:
 
     def run_topk(self, score=None):
         topk(self.p, self.score if score is None else score, self.sel)
+
+    def run_fused_topk(self, lse=None, sel=None):
+        """Pass 2 with the running top-k: o_cmp and the selection, no score matrix."""
+        cmp_fused_topk(self.p, self.q, self.ws, self.lse if lse is None else lse, self.o_cmp,
+                       self.sel if sel is None else sel)
+
+    @property
+    def folds_topk(self) -> bool:
+        return self.p.block <= 64 and self.k_eff <= 64
 
     def run_sel(self, sel=None, o_cmp=None):
         sel_combine(self.p, self.q, self.ws, self.sel if sel is None else sel,

@@ -53,7 +53,9 @@ def test_size_queries():
     assert S.dense_workspace_size(p) > 0
     # 1000 views x 1374 tokens, 16 heads, B = 64, k = 16: about 41 GB
     big = params(T=1_374_000, H=16, B=64, k=16)
-    assert 38e9 < S.workspace_size(big) < 44e9
+    assert 10e9 < S.workspace_size(big) < 13e9
+    big128 = params(T=1_374_000, H=16, B=128, k=16)
+    assert S.workspace_size(big128) > 14e9  # B = 128 keeps the score matrix
     assert S.num_blocks(big) == 21469
 
 
@@ -81,6 +83,7 @@ def test_bad_params_rejected_everywhere(kw, code):
         L.speed3r_pool(ctypes.byref(p), FAKE, FAKE, ws, big, None, None, None),
         L.speed3r_cmp_lse(ctypes.byref(p), FAKE, ws, big, FAKE, None),
         L.speed3r_cmp_fused(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, None),
+        L.speed3r_cmp_fused_topk(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, None),
         L.speed3r_topk(ctypes.byref(p), FAKE, FAKE, None),
         L.speed3r_sel_combine(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, FAKE, None, None),
         L.speed3r_dense_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws, big, None),
@@ -126,3 +129,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         S.lib()
+
+
+def test_fused_topk_limits():
+    """The selection folds into the compression pass only for B <= 64 and k <= 64."""
+    L = S.lib()
+    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
+    for kw in (dict(B=128, T=4096), dict(k=65, T=100 * 64, B=64)):
+        p = params(**kw)
+        assert L.speed3r_cmp_fused_topk(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE,
+                                        None) == S.S3R_ERR_UNSUPPORTED

@@ -99,6 +99,22 @@ def test_topk_bit_exact_on_gpu_scores(name):
                                           err_msg=f"row h={h} i={i}")
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_topk_equals_separate_topk(name):
+    """The running top-k inside the compression pass must choose exactly what the separate
+    top-k chooses on the score matrix, and leave O_cmp bit-identical."""
+    w, x, hx, st, ora = run_case(name)
+    if not st.folds_topk:
+        pytest.skip("B = 128 or k > 64 goes through the score matrix")
+    ref_sel = st.sel.clone()
+    ref_ocmp = st.o_cmp.clone()
+    sel = torch.full_like(st.sel, -7)
+    st.run_fused_topk(sel=sel)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, ref_sel)
+    assert torch.equal(st.o_cmp, ref_ocmp)
+
+
 def test_topk_ties_and_fallback():
     """Heavy ties (all scores equal, few distinct levels) force the exact fallback path."""
     H, Nb, k = 2, 700, 16
