@@ -19,11 +19,12 @@
 // (-running offset in pass 1, -L_t*log2(e) in pass 2) is the MFMA's C input, leaving one exp2
 // per logit on the VALU.
 //
-// Software pipeline (pass 2): while the VALU works on the probabilities of tile t, the logits
-// of tile t+1 are already being computed on the matrix cores (two accumulator sets alternate),
-// and tile t+2 is on its way from memory. The ring slot of tile t is only rewritten after the
-// barrier that ends iteration t+1, when no wave reads it any more. Pass 1 has less VALU work
-// per tile and runs unpipelined with more resident waves instead.
+// Optional software pipeline (kPipe): while the VALU works on the probabilities of tile t,
+// the logits of tile t+1 are already computed on the matrix cores (two accumulator sets), and
+// tile t+2 is on its way from memory. Measured on MI355X it loses to the unpipelined loop for
+// both passes: the second accumulator set pushes pass 2 to ~254 VGPRs and forces its offset
+// out of the MFMA C operand onto the VALU, while two resident waves per SIMD already overlap
+// one wave's VALU work with the other's MFMAs. Both passes therefore launch unpipelined.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
@@ -52,6 +53,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   static_assert(kLoads * kThreads == kTileU4 && kLoads <= 3, "whole staging registers");
   constexpr int kTileStrideU4 = kPooledTileBytes / 16;
   constexpr int kNtPerQB = 4 / kQB;
+  constexpr bool kOffsetOnValu = kFused && kPipe;
   __shared__ uint4 lds[kRing][kTileU4];
 
   const int64_t n_qtiles = (a.T + kQueries - 1) / kQueries;
@@ -145,8 +147,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 1) * 64 + lane]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        // pass 2 subtracts its fixed offset on the VALU (no C registers held across tiles)
-        floatx4 x = mfma16(h0, qb[nt][0], kFused ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[nt]);
+        // the pipelined pass 2 subtracts its fixed offset on the VALU (its second accumulator
+        // set leaves no room to hold the offset as a C operand across tiles)
+        floatx4 x = mfma16(h0, qb[nt][0], kOffsetOnValu ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[nt]);
         x = mfma16(h1, qb[nt][1], x);
         x = mfma16(l0, qb[nt][0], x);
         acc[s2][nt] = mfma16(l1, qb[nt][1], x);
@@ -215,7 +218,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[s2][nt][r] = fast_exp2(acc[s2][nt][r] - off[nt]);
+          for (int r = 0; r < 4; ++r)
+            p[s2][nt][r] = fast_exp2(kOffsetOnValu ? acc[s2][nt][r] - off[nt] : acc[s2][nt][r]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
@@ -388,9 +392,9 @@ static hipError_t launch_cmp(const CmpArgs& a, hipStream_t s, bool fused) {
   if (fused) {
     const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
     switch (a.B) {
-      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true>), g3, b3, 0, s, a); break;
-      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true>), g3, b3, 0, s, a); break;
-      default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true>), g3, b3, 0, s, a); break;
+      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false>), g3, b3, 0, s, a); break;
+      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false>), g3, b3, 0, s, a); break;
+      default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false>), g3, b3, 0, s, a); break;
     }
   } else {
     hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false>), cmp_grid(a, kLseWaves),
@@ -405,9 +409,9 @@ hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) { return launch_cmp
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s) {
   const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
   switch (a.B) {
-    case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, true>), g3, b3, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, true>), g3, b3, 0, s, a); break;
-    default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, true>), g3, b3, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, true>), g3, b3, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, true>), g3, b3, 0, s, a); break;
+    default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, true>), g3, b3, 0, s, a); break;
   }
   return hipGetLastError();
 }
