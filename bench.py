@@ -115,7 +115,7 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
     t_pool = time.perf_counter() - t0
     t0 = time.perf_counter()
     r = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32), rows,
-                       kc=kc, vc=vc)
+                       kc=kc, vc=vc, forced=w.forced)
     t_rows = time.perf_counter() - t0
     per_row = t_rows / len(rows)
     t_full = H * (t_pool + Nb * per_row)
@@ -126,7 +126,7 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
     ref = r
     if same < 1.0:
         ref = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32),
-                             rows, kc=kc, vc=vc, sel_in=gsel)
+                             rows, kc=kc, vc=vc, sel_in=gsel, forced=w.forced)
     for a, i in enumerate(rows):
         nn = min(T, (i + 1) * w.block) - i * w.block
         g = out_gpu[i * w.block:i * w.block + nn, h].float().cpu().numpy()
@@ -175,11 +175,11 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] workload {w.name}: T={w.T} H={w.H} B={w.block} k={w.topk}")
+    log(f"[bench] workload {w.name}: T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}")
     x = W.make_inputs(w, device=dev)
     torch.cuda.synchronize()
     T, H, D = x["q"].shape
-    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"])
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced)
     Nb = S.num_blocks(p)
     ws = S.alloc_workspace(S.workspace_size(p), dev)
     out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
@@ -187,7 +187,7 @@ def main():
 
     def step():
         S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
-                          sel_idx=sel, workspace=ws)
+                          sel_idx=sel, workspace=ws, forced_blocks=w.forced)
 
     for _ in range(args.warmup):
         step()
@@ -208,9 +208,9 @@ def main():
     # per-kernel durations: the same kernels launched stage by stage
     del ws
     torch.cuda.empty_cache()
-    folds = w.block <= 64 and w.k_eff <= 64
+    folds = w.block <= 64 and w.k_eff - min(w.forced, Nb) <= 64
     st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, keep_o_sel=False,
-                  keep_score=not folds)
+                  keep_score=not folds, forced_blocks=w.forced)
     st.run_pool()
     st.run_lse()
     stage_ms = timed_stages(st, max(1, min(3, args.steps)))

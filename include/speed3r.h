@@ -44,7 +44,8 @@ extern "C" {
 
 typedef enum {
   S3R_OK = 0,
-  S3R_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment */
+  S3R_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, negative forced_blocks, bad
+                              stride or alignment */
   S3R_ERR_UNSUPPORTED = 2, /* well-formed but not built: D != 64, B not 16/32/64/128,
                               more than 24576 blocks, H > 65535 */
   S3R_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
@@ -58,7 +59,10 @@ typedef struct {
   int32_t block;        /* B: query and key block size, one of 16, 32, 64, 128 */
   int32_t topk;         /* k >= 1: key blocks kept per query block; clamped to Nb */
   float scale;          /* softmax scale; 0 selects 1/sqrt(D) */
-  int32_t reserved;     /* must be 0 */
+  int32_t forced_blocks; /* F >= 0: key blocks 0..F-1 are selected for every query block in
+                            addition to the top-k of the remaining blocks (the VGGT variant
+                            keeps the reference frame's tokens dense, summary "Methodologie"
+                            3). 0 = plain top-k */
   int64_t q_stride_t, q_stride_h; /* element strides of q between tokens / heads */
   int64_t k_stride_t, k_stride_h;
   int64_t v_stride_t, v_stride_h;
@@ -72,6 +76,10 @@ const char* speed3r_status_string(s3r_status s);
 /* Nb = ceil(T / B), the number of key blocks (= query blocks). -1 if p is invalid. */
 int64_t speed3r_num_blocks(const s3r_params* p);
 
+/* Entries per selection row: n_sel = F' + min(k, Nb - F') with F' = min(forced_blocks, Nb).
+ * Rows hold the forced blocks 0..F'-1 followed by the chosen ones, ascending. -1 if invalid. */
+int64_t speed3r_num_selected(const s3r_params* p);
+
 /* Row stride (in floats) of the score matrix [H][Nb][ld]: Nb rounded up to 32. -1 if invalid. */
 int64_t speed3r_score_row_stride(const s3r_params* p);
 
@@ -81,7 +89,8 @@ size_t speed3r_tiles_workspace_size(const s3r_params* p);
 
 /* Bytes of workspace speed3r_sparse_attn_fwd needs: the tiles plus LSE [H][T] f32, O_cmp
  * [T][H][64] f32, the selected indices and, only when the selection cannot be folded into
- * the compression pass (B = 128 or k_eff > 64), the score matrix [H][Nb][ld] f32. About 11.5
+ * the compression pass (B = 128 or more than 64 chosen blocks), the score matrix [H][Nb][ld]
+ * f32. About 11.5
  * GB at T = 1,374,000, H = 16, B = 64, k = 16. 0 if p is invalid. */
 size_t speed3r_workspace_size(const s3r_params* p);
 
@@ -95,7 +104,7 @@ size_t speed3r_dense_workspace_size(const s3r_params* p);
  *   gates    f32, [H][2] or per token (see gate_stride_t); column 0 multiplies the
  *            compression branch, column 1 the selection branch.
  *   out      bf16 [T][H][64], contiguous.
- *   sel_idx  optional int32 [H][Nb][k_eff] (k_eff = min(k, Nb)); NULL keeps it in the
+ *   sel_idx  optional int32 [H][Nb][n_sel] (speed3r_num_selected); NULL keeps it in the
  *            workspace.
  *   workspace / workspace_bytes: at least speed3r_workspace_size(p) bytes, 256-byte aligned.
  */
@@ -135,17 +144,17 @@ s3r_status speed3r_cmp_fused(const s3r_params* p, const void* q, const void* wor
  * and softmax on chip without materialising the score matrix, summary "Methodologie" 4):
  * computes o_cmp exactly as speed3r_cmp_fused and, instead of the score matrix, keeps the
  * running top-k of each query block while the key blocks stream by, writing sel_idx [H][Nb]
- * [k_eff] in ascending order. The choice equals speed3r_topk applied to the score matrix
- * speed3r_cmp_fused writes, bit for bit. Requires B <= 64 and k_eff <= 64
+ * [n_sel] in ascending order. The choice equals speed3r_topk applied to the score matrix
+ * speed3r_cmp_fused writes, bit for bit. Requires B <= 64 and n_sel - F' <= 64
  * (S3R_ERR_UNSUPPORTED otherwise). */
 s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void* workspace,
                                   size_t workspace_bytes, const float* lse, float* o_cmp,
                                   int32_t* sel_idx, hipStream_t stream);
 
 /* Top-k selection (summary "Methodologie" 1, selection guided by the compression scores):
- * sel_idx[(h*Nb + i)*k_eff + a] = the k_eff largest entries of score row (h, i) by (value
- * descending, index ascending), written in ascending order. Bit-exact, deterministic.
- * Scores are compared as f32 values (-0 equals +0). */
+ * sel_idx[(h*Nb + i)*n_sel + a]: the forced blocks 0..F'-1, then the n_sel - F' largest
+ * entries of score row (h, i) among blocks F'..Nb-1 by (value descending, index ascending),
+ * in ascending order. Bit-exact, deterministic. Scores are compared as f32 (-0 equals +0). */
 s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_idx,
                         hipStream_t stream);
 

@@ -63,8 +63,10 @@ def lib():
                                             _i64, _i64, _f32p, _i64, _i64, _i32, _i64, _i64,
                                             _f64p]
         L.s3r_oracle_dense_rows.restype = None
+        L.s3r_oracle_num_selected.argtypes = [_i64, _i32, _i32, _i32]
+        L.s3r_oracle_num_selected.restype = _i32
         L.s3r_oracle_forward_rows.argtypes = [
-            _i64, _i32, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p, _i64, _i64, _f32p,
+            _i64, _i32, _i32, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p, _i64, _i64, _f32p,
             _i64, _i64, _f64p, _f64p, _f32p, _i64, _i64, _i32p, _i64p,
             ctypes.c_void_p, _f64p, _f64p, _f32p, _i32p, _f64p, _f64p]
         L.s3r_oracle_forward_rows.restype = None
@@ -154,20 +156,25 @@ def dense_rows(q, k, v, h: int, t0: int, nt: int, scale: Optional[float] = None)
     return out
 
 
+def num_selected(T: int, B: int, topk_: int, forced: int = 0) -> int:
+    return int(lib().s3r_oracle_num_selected(T, B, topk_, forced))
+
+
 def forward_rows(q, k, v, gates, B: int, topk_: int, rows_h: Sequence[int],
                  rows_i: Sequence[int], kc: Optional[np.ndarray] = None,
                  vc: Optional[np.ndarray] = None, sel_in: Optional[np.ndarray] = None,
-                 scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+                 scale: Optional[float] = None, forced: int = 0) -> Dict[str, np.ndarray]:
     """Whole forward pass for the listed (head, query block) rows.
 
     Returns per-row arrays: lse [R, B], ocmp [R, B, D], score [R, Nb] (float32), sel
-    [R, k_eff], osel [R, B, D], out [R, B, D]; rows of a short last block are valid for their
-    first n_i entries only. ``kc``/``vc`` may be passed in to reuse a pooling.
+    [R, n_sel], osel [R, B, D], out [R, B, D]; rows of a short last block are valid for their
+    first n_i entries only. ``kc``/``vc`` may be passed in to reuse a pooling. ``forced``
+    blocks (the first F) are always selected and top-k runs over the rest.
     """
     a, b, c = _f32(q), _f32(k), _f32(v)
     T, H, D = a.shape
     Nb = n_blocks(T, B)
-    k_eff = min(topk_, Nb)
+    k_eff = num_selected(T, B, topk_, forced)
     if kc is None:
         kc = pool(b, B)
     if vc is None:
@@ -187,22 +194,24 @@ def forward_rows(q, k, v, gates, B: int, topk_: int, rows_h: Sequence[int],
         sel_in = np.ascontiguousarray(np.asarray(sel_in, dtype=np.int32).reshape(R, k_eff))
         sel_ptr = sel_in.ctypes.data
     lib().s3r_oracle_forward_rows(
-        T, H, D, B, topk_, default_scale(D) if scale is None else scale, a, H * D, D, b, H * D,
+        T, H, D, B, topk_, forced, default_scale(D) if scale is None else scale, a, H * D, D,
+        b, H * D,
         D, c, H * D, D, np.ascontiguousarray(kc), np.ascontiguousarray(vc), g.reshape(-1),
         gate_st, R, rh, ri, sel_ptr, res["lse"], res["ocmp"], res["score"], res["sel"],
         res["osel"], res["out"])
     return res
 
 
-def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = None):
+def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = None,
+                forced: int = 0):
     """Forward pass over every row, reassembled into token-major tensors:
-    out/ocmp/osel [T, H, D], lse [H, T], score [H, Nb, Nb] float32, sel [H, Nb, k_eff]."""
+    out/ocmp/osel [T, H, D], lse [H, T], score [H, Nb, Nb] float32, sel [H, Nb, n_sel]."""
     a = _f32(q)
     T, H, D = a.shape
     Nb = n_blocks(T, B)
     rows_h = np.repeat(np.arange(H), Nb)
     rows_i = np.tile(np.arange(Nb), H)
-    r = forward_rows(q, k, v, gates, B, topk_, rows_h, rows_i, scale=scale)
+    r = forward_rows(q, k, v, gates, B, topk_, rows_h, rows_i, scale=scale, forced=forced)
     k_eff = r["sel"].shape[1]
     full = {}
     for name in ("ocmp", "osel", "out"):

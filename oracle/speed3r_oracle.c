@@ -27,6 +27,9 @@
  *     attention probabilities;
  *   - top-k is taken per head, ties go to the smaller block index, indices are returned in
  *     ascending order, k is clamped to the number of blocks;
+ *   - optional forced blocks (the VGGT variant keeps the reference frame's tokens dense,
+ *     summary "Methodologie" 3): the first F key blocks are always selected and top-k is taken
+ *     over the remaining blocks, so a row holds min(F, Nb) + min(k, Nb - min(F, Nb)) blocks;
  *   - the top-k decision is made on the scores rounded to float32 (the precision the GPU
  *     kernel decides in);
  *   - no masking (bidirectional attention), no forced blocks.
@@ -220,14 +223,22 @@ void s3r_oracle_dense_rows(int64_t T, int32_t H, int32_t D, double scale, const 
   }
 }
 
+/* Number of selected blocks per row: the forced prefix plus top-k of the rest. */
+int32_t s3r_oracle_num_selected(int64_t T, int32_t B, int32_t topk, int32_t forced) {
+  const int64_t Nb = n_blocks(T, B);
+  const int64_t f = (forced < Nb) ? forced : Nb;
+  const int64_t rest = Nb - f;
+  return (int32_t)(f + ((topk < rest) ? topk : rest));
+}
+
 /* The whole forward pass for a list of (head, query block) rows, given the pooled tensors.
  * Per row r (B_ = B, n_i <= B rows of each per-query output are written):
  *   lse[r][B][1], ocmp[r][B][D], score[r][Nb] (float32, the values top-k decides on),
- *   sel[r][k_eff], osel[r][B][D], out[r][B][D].
- * If sel_in is not NULL it supplies the selected blocks ([r][k_eff]) instead of top-k.
+ *   sel[r][n_sel], osel[r][B][D], out[r][B][D], n_sel = s3r_oracle_num_selected().
+ * If sel_in is not NULL it supplies the selected blocks ([r][n_sel]) instead of top-k.
  * Gate of (t, h, branch b) is gates[t*gate_st + h*2 + b] (gate_st = 0: per-head gates). */
 void s3r_oracle_forward_rows(int64_t T, int32_t H, int32_t D, int32_t B, int32_t topk,
-                             double scale, const float* q, int64_t qst, int64_t qsh,
+                             int32_t forced, double scale, const float* q, int64_t qst, int64_t qsh,
                              const float* k, int64_t kst, int64_t ksh, const float* v,
                              int64_t vst, int64_t vsh, const double* kc, const double* vc,
                              const float* gates, int64_t gate_st, int64_t n_rows,
@@ -235,7 +246,8 @@ void s3r_oracle_forward_rows(int64_t T, int32_t H, int32_t D, int32_t B, int32_t
                              double* lse, double* ocmp, float* score, int32_t* sel,
                              double* osel, double* out) {
   const int64_t Nb = n_blocks(T, B);
-  const int32_t k_eff = (int32_t)((topk < Nb) ? topk : Nb);
+  const int32_t k_eff = s3r_oracle_num_selected(T, B, topk, forced);
+  const int32_t f = (int32_t)((forced < Nb) ? forced : Nb);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
     const int32_t h = row_h[r];
@@ -251,7 +263,12 @@ void s3r_oracle_forward_rows(int64_t T, int32_t H, int32_t D, int32_t B, int32_t
     if (sel_in) {
       memcpy(my_sel, sel_in + r * k_eff, sizeof(int32_t) * (size_t)k_eff);
     } else {
-      s3r_oracle_topk(my_score, Nb, topk, my_sel);
+      /* forced prefix, then top-k over blocks f..Nb-1 (indices shifted back by f) */
+      for (int32_t a = 0; a < f; ++a) my_sel[a] = a;
+      if (f < Nb) {
+        const int32_t got = s3r_oracle_topk(my_score + f, Nb - f, topk, my_sel + f);
+        for (int32_t a = 0; a < got; ++a) my_sel[f + a] += f;
+      }
     }
     double* my_osel = osel + r * B * D;
     s3r_oracle_sel_row(T, H, D, B, scale, q, qst, qsh, k, kst, ksh, v, vst, vsh, h, i, my_sel,

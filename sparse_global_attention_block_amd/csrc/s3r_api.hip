@@ -16,7 +16,9 @@ constexpr int64_t kMaxBlocks = 96 * 256;  // top-k holds a row of up to 96 keys 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Dims {
-  int64_t T, Nb, n_ctiles, n_ktiles, ld, k_eff;
+  int64_t T, Nb, n_ctiles, n_ktiles, ld;
+  int64_t k_eff;   // entries per selection row: forced prefix + chosen blocks (n_sel)
+  int64_t forced;  // F' = min(forced_blocks, Nb)
   int32_t H, B;
   float scale;
   bool fold_topk;  // selection folded into the compression pass (no score matrix)
@@ -32,7 +34,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 s3r_status check_params(const s3r_params* p, Dims* d) {
   if (!p) return S3R_ERR_INVALID_ARG;
-  if (p->T < 1 || p->H < 1 || p->topk < 1 || p->reserved != 0) return S3R_ERR_INVALID_ARG;
+  if (p->T < 1 || p->H < 1 || p->topk < 1 || p->forced_blocks < 0) return S3R_ERR_INVALID_ARG;
   if (p->block < 1 || p->D < 1) return S3R_ERR_INVALID_ARG;
   if (!(p->scale >= 0.f) || isinf(p->scale)) return S3R_ERR_INVALID_ARG;
   if (!valid_stride(p->q_stride_t) || !valid_stride(p->q_stride_h) ||
@@ -51,9 +53,11 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->n_ctiles = (d->Nb + kTileKeys - 1) / kTileKeys;
   d->n_ktiles = (d->T + kTileKeys - 1) / kTileKeys;
   d->ld = d->n_ctiles * kTileKeys;
-  d->k_eff = p->topk < d->Nb ? p->topk : d->Nb;
+  d->forced = p->forced_blocks < d->Nb ? p->forced_blocks : d->Nb;
+  const int64_t rest = d->Nb - d->forced;
+  d->k_eff = d->forced + (p->topk < rest ? p->topk : rest);
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)kD);
-  d->fold_topk = d->B <= 64 && d->k_eff <= kFusedTopkMaxK;
+  d->fold_topk = d->B <= 64 && d->k_eff - d->forced <= kFusedTopkMaxK;
   return S3R_OK;
 }
 
@@ -160,6 +164,11 @@ int64_t speed3r_num_blocks(const s3r_params* p) {
   return check_params(p, &d) == S3R_OK ? d.Nb : -1;
 }
 
+int64_t speed3r_num_selected(const s3r_params* p) {
+  Dims d;
+  return check_params(p, &d) == S3R_OK ? d.k_eff : -1;
+}
+
 int64_t speed3r_score_row_stride(const s3r_params* p) {
   Dims d;
   return check_params(p, &d) == S3R_OK ? d.ld : -1;
@@ -244,7 +253,8 @@ s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void
   a.lse_in = lse;
   a.o_cmp = o_cmp;
   a.sel = sel_idx;
-  a.k_eff = (int32_t)d.k_eff;
+  a.n_sel = (int32_t)d.k_eff;
+  a.forced = (int32_t)d.forced;
   return hip_status(launch_cmp_fused_topk(a, stream));
 }
 
@@ -257,7 +267,7 @@ s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_id
     return S3R_ERR_INVALID_ARG;
   TopkArgs a;
   a.score = score; a.ld = d.ld; a.Nb = d.Nb; a.n_rows = (int64_t)d.H * d.Nb;
-  a.k_eff = (int32_t)d.k_eff; a.sel = sel_idx;
+  a.n_sel = (int32_t)d.k_eff; a.forced = (int32_t)d.forced; a.sel = sel_idx;
   return hip_status(launch_topk(a, stream));
 }
 
@@ -308,14 +318,15 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
   c.o_cmp = o_cmp;
   if (d.fold_topk) {
     c.sel = sel;
-    c.k_eff = (int32_t)d.k_eff;
+    c.n_sel = (int32_t)d.k_eff;
+    c.forced = (int32_t)d.forced;
     if ((st = hip_status(launch_cmp_fused_topk(c, stream))) != S3R_OK) return st;
   } else {
     c.score = score;
     if ((st = run_cmp_fused(d, c, stream)) != S3R_OK) return st;
     TopkArgs t;
     t.score = score; t.ld = d.ld; t.Nb = d.Nb; t.n_rows = (int64_t)d.H * d.Nb;
-    t.k_eff = (int32_t)d.k_eff; t.sel = sel;
+    t.n_sel = (int32_t)d.k_eff; t.forced = (int32_t)d.forced; t.sel = sel;
     if ((st = hip_status(launch_topk(t, stream))) != S3R_OK) return st;
   }
   AttnArgs a = attn_args(p, d, q, ws + L.raw);

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     th_v[qb] = -1.0f;
     th_j[qb] = 0x7FFFFFFF;
   }
-  const int K = a.k_eff;
+  const int K = a.n_sel - a.forced;  // blocks chosen per query block (after the forced prefix)
   auto better = [](float v1, int j1, float v2, int j2) {
     return v1 > v2 || (v1 == v2 && j1 < j2);
   };
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
             // lanes with bit 1 clear hold the 32 distinct keys of this tile; a block can only
             // enter the list if its score is >= the current k-th score (one compare per tile)
             const int j = (int)(tau * kTileKeys) + reduced_key(lane);
-            const bool mine = ((lane & 2) == 0) && j < a.Nb;
+            const bool mine = ((lane & 2) == 0) && K > 0 && j >= a.forced && j < a.Nb;
             uint64_t cand = __ballot(mine && tot >= th_v[qb]);
             while (cand) {  // rare after the first tiles
               const int c = __builtin_ctzll(cand);
@@ -362,9 +362,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int qb = 0; qb < kQB; ++qb) {
         const int64_t qblk = (q0 + 16 * qb * kNtPerQB) / a.B;
         if (qblk < a.Nb) {
+          int32_t* row = a.sel + ((int64_t)h * a.Nb + qblk) * a.n_sel;
+          for (int m = lane; m < a.forced; m += 64) row[m] = m;
           int rank = 0;
           for (int m = 0; m < K; ++m) rank += __builtin_amdgcn_readlane(tk_j[qb], m) < tk_j[qb];
-          if (lane < K) a.sel[((int64_t)h * a.Nb + qblk) * K + rank] = tk_j[qb];
+          if (lane < K) row[a.forced + rank] = tk_j[qb];
         }
       }
     }

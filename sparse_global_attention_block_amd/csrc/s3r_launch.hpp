@@ -36,8 +36,9 @@ struct CmpArgs {
   float* o_cmp;            // [T][H][64]
   float* score;            // [H][Nb][ld]
   int64_t ld;
-  int32_t* sel;            // running top-k output [H][Nb][k_eff] (fused selection only)
-  int32_t k_eff;
+  int32_t* sel;            // running top-k output [H][Nb][n_sel] (fused selection only)
+  int32_t n_sel;           // row length: forced prefix + chosen blocks
+  int32_t forced;          // F': blocks 0..F'-1 always selected, top-k over the rest
 };
 
 struct TopkArgs {
@@ -45,8 +46,9 @@ struct TopkArgs {
   int64_t ld;
   int64_t Nb;
   int64_t n_rows;          // H * Nb
-  int32_t k_eff;
-  int32_t* sel;            // [n_rows][k_eff]
+  int32_t n_sel;           // row length of sel
+  int32_t forced;          // F': blocks 0..F'-1 always selected, top-(n_sel - F') of the rest
+  int32_t* sel;            // [n_rows][n_sel]
 };
 
 struct AttnArgs {
@@ -57,7 +59,7 @@ struct AttnArgs {
   float logit_mult;        // scale * log2(e)
   const unsigned char* tiles;  // raw packed k/v tiles
   // selection only
-  const int32_t* sel; int32_t k_eff;
+  const int32_t* sel; int32_t k_eff;  // k_eff = entries per selection row (n_sel)
   const float* o_cmp;
   const float* gates; int64_t gate_st;
   float* o_sel;            // optional

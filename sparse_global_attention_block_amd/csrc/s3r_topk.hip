@@ -1,4 +1,4 @@
-// Top-k block selection per (head, query block).
+// Top-k block selection per (head, query block), after an optional forced prefix of blocks.
 //
 // Speed3R technical summary (gist.science), "Methodologie" section 1: the selection branch
 // keeps, per query block, the k key blocks with the highest compression score. This kernel
@@ -48,12 +48,15 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Nb = (int)a.Nb;
-  const int k = a.k_eff;
-  int32_t* out = a.sel + row * k;
-  if (k >= Nb) {
-    for (int j = tid; j < Nb; j += 256) out[j] = j;
+  const int F = a.forced;       // blocks 0..F-1 are selected outright
+  const int k = a.n_sel - F;    // chosen among blocks F..Nb-1
+  int32_t* row_out = a.sel + row * a.n_sel;
+  for (int j = tid; j < F; j += 256) row_out[j] = j;
+  if (k >= Nb - F) {
+    for (int j = F + tid; j < Nb; j += 256) row_out[j] = j;
     return;
   }
+  int32_t* out = row_out + F;
   const float* src = a.score + row * a.ld;
 
   // All E loads are issued before any is used: the index is clamped instead of branched on,
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    key[e] = (j < Nb) ? order_key(raw[e]) : 0u;
+    key[e] = (j >= F && j < Nb) ? order_key(raw[e]) : 0u;
     tmax = key[e] > tmax ? key[e] : tmax;
   }
   tmax_s[tid] = tmax;
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    if (j < Nb && key[e] >= theta) {
+    if (j >= F && j < Nb && key[e] >= theta) {
       const int pos = atomicAdd(&s_count, 1);
       if (pos < kCap) {
         cand_key[pos] = key[e];
@@ -141,12 +144,18 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     const uint32_t cand = kth | (1u << b);
     int local = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) local += (e * 256 + tid < Nb) && key[e] >= cand;
+    for (int e = 0; e < E; ++e) {
+      const int j = e * 256 + tid;
+      local += (j >= F && j < Nb) && key[e] >= cand;
+    }
     if (block_count(local) >= k) kth = cand;
   }
   int greater = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) greater += (e * 256 + tid < Nb) && key[e] > kth;
+  for (int e = 0; e < E; ++e) {
+    const int j = e * 256 + tid;
+    greater += (j >= F && j < Nb) && key[e] > kth;
+  }
   const int need = k - block_count(greater);  // tied entries to keep, >= 1
   // largest J with #{ties with index < J} < need: J is the index of the last tie kept
   int J = 0;
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = e * 256 + tid;
-      local += (j < Nb) && key[e] == kth && j < cand;
+      local += (j >= F && j < Nb) && key[e] == kth && j < cand;
     }
     if (block_count(local) < need) J = cand;
   }
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    const bool take = (j < Nb) && (key[e] > kth || (key[e] == kth && j <= J));
+    const bool take = (j >= F && j < Nb) && (key[e] > kth || (key[e] == kth && j <= J));
     const uint64_t m = __ballot(take);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     __syncthreads();

@@ -24,7 +24,7 @@ class Params(ctypes.Structure):
     _fields_ = [
         ("T", ctypes.c_int64), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
         ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("forced_blocks", ctypes.c_int32),
         ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
         ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
         ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
@@ -41,6 +41,7 @@ class Speed3RError(RuntimeError):
 EXPORTS = {
     "speed3r_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "speed3r_num_blocks": (ctypes.c_int64, [ctypes.POINTER(Params)]),
+    "speed3r_num_selected": (ctypes.c_int64, [ctypes.POINTER(Params)]),
     "speed3r_score_row_stride": (ctypes.c_int64, [ctypes.POINTER(Params)]),
     "speed3r_tiles_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "speed3r_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
@@ -104,8 +105,11 @@ def _stream():
 
 
 def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
-                scale: float = 0.0, gates: Optional[torch.Tensor] = None) -> Params:
-    """Params for [T, H, 64] bf16 token tensors (any token/head strides, last dim contiguous)."""
+                scale: float = 0.0, gates: Optional[torch.Tensor] = None,
+                forced_blocks: int = 0) -> Params:
+    """Params for [T, H, 64] bf16 token tensors (any token/head strides, last dim contiguous).
+    ``forced_blocks`` key blocks 0..F-1 are selected for every query block on top of the
+    top-k of the rest."""
     T, H, D = q.shape
     for x in (q, k, v):
         if x.dtype != torch.bfloat16 or tuple(x.shape) != (T, H, D) or x.stride(2) != 1:
@@ -113,12 +117,17 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, t
     gst = 0
     if gates is not None and gates.dim() == 3:
         gst = gates.stride(0)
-    return Params(T, H, D, block, topk, float(scale), 0, q.stride(0), q.stride(1), k.stride(0),
-                  k.stride(1), v.stride(0), v.stride(1), gst)
+    return Params(T, H, D, block, topk, float(scale), forced_blocks, q.stride(0), q.stride(1),
+                  k.stride(0), k.stride(1), v.stride(0), v.stride(1), gst)
 
 
 def num_blocks(p: Params) -> int:
     return int(lib().speed3r_num_blocks(ctypes.byref(p)))
+
+
+def num_selected(p: Params) -> int:
+    """Entries per selection row: forced prefix + chosen blocks."""
+    return int(lib().speed3r_num_selected(ctypes.byref(p)))
 
 
 def score_row_stride(p: Params) -> int:
@@ -144,10 +153,10 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None
+                    workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Full forward pass. Returns (out [T, H, 64] bf16, sel_idx or None)."""
-    p = make_params(q, k, v, block, topk, scale, gates)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if workspace is None:
@@ -208,17 +217,19 @@ def dense_attn_fwd(q, k, v, scale: float = 0.0, out=None, workspace=None):
 class Stages:
     """Runs the forward pass one stage at a time and keeps every intermediate result:
     k_mean, v_mean [H, Nb, 64] f32, lse [H, T] f32, o_cmp [T, H, 64] f32,
-    score [H, Nb, ld] f32, sel [H, Nb, k_eff] int32, o_sel [T, H, 64] f32, out bf16."""
+    score [H, Nb, ld] f32, sel [H, Nb, k_eff] int32 (k_eff = forced prefix + chosen blocks),
+    o_sel [T, H, 64] f32, out bf16."""
 
     def __init__(self, q, k, v, gates, block: int, topk_: int, scale: float = 0.0,
-                 keep_o_sel: bool = True, keep_score: bool = True):
+                 keep_o_sel: bool = True, keep_score: bool = True, forced_blocks: int = 0):
         self.q, self.k, self.v, self.gates = q, k, v, gates
-        self.p = make_params(q, k, v, block, topk_, scale, gates)
+        self.p = make_params(q, k, v, block, topk_, scale, gates, forced_blocks)
         T, H, D = q.shape
         dev = q.device
         self.Nb = num_blocks(self.p)
         self.ld = score_row_stride(self.p)
-        self.k_eff = min(topk_, self.Nb)
+        self.k_eff = num_selected(self.p)
+        self.forced = min(forced_blocks, self.Nb)
         self.ws = alloc_workspace(tiles_workspace_size(self.p), dev)
         f32 = dict(dtype=torch.float32, device=dev)
         self.k_mean = torch.empty(H, self.Nb, D, **f32)
@@ -250,7 +261,7 @@ class Stages:
 
     @property
     def folds_topk(self) -> bool:
-        return self.p.block <= 64 and self.k_eff <= 64
+        return self.p.block <= 64 and self.k_eff - self.forced <= 64
 
     def run_sel(self, sel=None, o_cmp=None):
         sel_combine(self.p, self.q, self.ws, self.sel if sel is None else sel,

@@ -49,6 +49,7 @@ class Workload:
     alpha: float = 0.5
     special_mult: float = 1.0
     D: int = D_HEAD
+    forced: int = 0       # leading key blocks every query block attends (reference view)
 
     @property
     def T(self) -> int:
@@ -60,13 +61,16 @@ class Workload:
 
     @property
     def k_eff(self) -> int:
-        return min(self.topk, self.n_blocks)
+        """Entries per selection row: the forced blocks plus the chosen ones."""
+        f = min(self.forced, self.n_blocks)
+        return f + min(self.topk, self.n_blocks - f)
 
     def describe(self) -> Dict:
         return {
             "workload": self.name, "views": self.views, "tokens_per_view": self.tokens_per_view,
             "T": self.T, "H": self.H, "D": self.D, "block": self.block, "topk": self.topk,
             "generator": self.gen, "seed": self.seed,
+            **({"forced_blocks": self.forced} if self.forced else {}),
             **({"iid_scale": self.iid_scale} if self.gen == "iid" else
                {"alpha": self.alpha, "special_tokens": self.special,
                 "special_kv_mult": self.special_mult}),
@@ -86,6 +90,10 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("v100", 100, 1374, 5, 16, 64, 16, "structured", seed=100, special_mult=3.0),
     Workload("v1000_k16", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000, special_mult=3.0),
     Workload("v1000_k32", 1000, 1374, 5, 16, 64, 32, "structured", seed=1000, special_mult=3.0),
+    # same as v1000_k16, with the 22 key blocks that cover the first (reference) view attended
+    # by every query block in addition to its top-16
+    Workload("v1000_k16_ref", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
+             special_mult=3.0, forced=22),
 ]}
 
 

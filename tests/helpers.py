@@ -34,24 +34,30 @@ def row_gaps(score_row_f32: np.ndarray, k: int) -> float:
     return float(s[k - 1] - s[k])
 
 
-def check_selection(gpu_sel: np.ndarray, ora_score: np.ndarray, ora_sel: np.ndarray, k: int):
-    """Index parity: rows whose oracle gap exceeds GAP must match exactly; on the other rows
-    every GPU-chosen block must score within GAP of the oracle's k-th score. Returns the
-    fraction of rows that were held to the exact rule and the list of differing rows."""
+def check_selection(gpu_sel: np.ndarray, ora_score: np.ndarray, ora_sel: np.ndarray, k: int,
+                    forced: int = 0):
+    """Index parity: every row starts with the forced blocks 0..forced-1; of the k chosen
+    after them, rows whose oracle gap (over blocks >= forced) exceeds GAP must match exactly;
+    on the other rows every GPU-chosen block must score within GAP of the oracle's k-th score.
+    Returns the fraction of rows held to the exact rule and the list of differing rows."""
     rows = gpu_sel.reshape(-1, gpu_sel.shape[-1])
     osel = ora_sel.reshape(-1, ora_sel.shape[-1])
     osc = ora_score.reshape(-1, ora_score.shape[-1])
+    assert rows.shape[1] == forced + k == osel.shape[1]
     exact, differing = 0, []
     for r in range(rows.shape[0]):
-        gap = row_gaps(osc[r], k)
-        same = np.array_equal(rows[r], osel[r])
+        np.testing.assert_array_equal(rows[r][:forced], np.arange(forced), err_msg=f"row {r}")
+        got, want, free = rows[r][forced:], osel[r][forced:], osc[r][forced:]
+        gap = row_gaps(free, k) if k > 0 else math.inf
+        same = np.array_equal(got, want)
         if gap > GAP:
             exact += 1
             assert same, f"row {r}: gap {gap:.3e} > {GAP} but GPU {rows[r]} != oracle {osel[r]}"
         elif not same:
-            kth = -np.sort(-osc[r].astype(np.float64))[k - 1]
-            assert (osc[r][rows[r]] >= kth - GAP).all(), f"row {r}: GPU picked a far block"
-            assert np.array_equal(np.sort(rows[r]), rows[r]) and len(set(rows[r])) == len(rows[r])
+            kth = -np.sort(-free.astype(np.float64))[k - 1]
+            assert (got >= forced).all(), f"row {r}: a forced block was chosen twice"
+            assert (osc[r][got] >= kth - GAP).all(), f"row {r}: GPU picked a far block"
+            assert np.array_equal(np.sort(got), got) and len(set(got)) == len(got)
             differing.append(r)
     return exact / max(1, rows.shape[0]), differing
 

@@ -36,9 +36,9 @@ def test_status_strings():
     assert S.status_string(99) == "S3R_ERR_UNKNOWN"
 
 
-def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None):
+def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0):
     st = st or (H * D, D)
-    return S.Params(T, H, D, B, k, scale, 0, st[0], st[1], st[0], st[1], st[0], st[1], 0)
+    return S.Params(T, H, D, B, k, scale, forced, st[0], st[1], st[0], st[1], st[0], st[1], 0)
 
 
 def test_size_queries():
@@ -51,7 +51,7 @@ def test_size_queries():
     assert all(a < b for a, b in zip(sizes, sizes[1:])), "workspace must grow with T"
     assert S.tiles_workspace_size(p) < S.workspace_size(p)
     assert S.dense_workspace_size(p) > 0
-    # 1000 views x 1374 tokens, 16 heads, B = 64, k = 16: about 41 GB
+    # 1000 views x 1374 tokens, 16 heads, B = 64, k = 16: about 11.5 GB
     big = params(T=1_374_000, H=16, B=64, k=16)
     assert 10e9 < S.workspace_size(big) < 13e9
     big128 = params(T=1_374_000, H=16, B=128, k=16)
@@ -71,6 +71,7 @@ def test_size_queries():
     (dict(st=(4 * 64 + 4, 64)), S.S3R_ERR_INVALID_ARG),   # token stride not a multiple of 8
     (dict(st=(-256, 64)), S.S3R_ERR_INVALID_ARG),
     (dict(T=24577 * 16, B=16), S.S3R_ERR_UNSUPPORTED),     # more than 24576 blocks
+    (dict(forced=-1), S.S3R_ERR_INVALID_ARG),
 ])
 def test_bad_params_rejected_everywhere(kw, code):
     p = params(**kw)
@@ -89,7 +90,16 @@ def test_bad_params_rejected_everywhere(kw, code):
         L.speed3r_dense_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws, big, None),
     ]
     assert calls == [code] * len(calls)
-    assert S.workspace_size(p) == 0 and S.num_blocks(p) == -1
+    assert S.workspace_size(p) == 0 and S.num_blocks(p) == -1 and S.num_selected(p) == -1
+
+
+@pytest.mark.parametrize("T,B,k,F,n_sel", [
+    (1024, 16, 8, 0, 8), (1024, 16, 8, 3, 11), (1024, 16, 100, 0, 64), (1024, 16, 60, 10, 64),
+    (1024, 16, 8, 64, 64), (1024, 16, 8, 1000, 64), (40, 16, 8, 1, 3), (1, 64, 16, 2, 1),
+])
+def test_num_selected_counts_forced_prefix(T, B, k, F, n_sel):
+    """Rows hold F' = min(F, Nb) forced blocks and min(k, Nb - F') chosen ones."""
+    assert S.num_selected(params(T=T, B=B, k=k, forced=F)) == n_sel
 
 
 def test_null_and_misaligned_pointers():
@@ -135,7 +145,12 @@ def test_fused_topk_limits():
     """The selection folds into the compression pass only for B <= 64 and k <= 64."""
     L = S.lib()
     ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
-    for kw in (dict(B=128, T=4096), dict(k=65, T=100 * 64, B=64)):
+    for kw in (dict(B=128, T=4096), dict(k=65, T=100 * 64, B=64),
+               dict(k=65, T=100 * 64, B=64, forced=20)):
         p = params(**kw)
         assert L.speed3r_cmp_fused_topk(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE,
                                         None) == S.S3R_ERR_UNSUPPORTED
+    # the limit is on the chosen blocks: 60 forced + 40 chosen of the remaining 40 folds in
+    p = params(k=65, T=100 * 64, B=64, forced=60)
+    assert S.num_selected(p) == 100
+    assert S.workspace_size(p) < S.workspace_size(params(k=65, T=100 * 64, B=64))

@@ -24,6 +24,14 @@ CASES = {
     "b128": (dataclasses.replace(_tiny_s, name="b128", H=2, block=128, topk=3), 1100),
     "b16_many_tiles": (dataclasses.replace(_tiny_s, name="b16", H=1, block=16, topk=6), 3000),
     "shorter_than_block": (dataclasses.replace(W.WORKLOADS["v8"], name="short", H=2), 40),
+    # forced leading blocks: the 16 blocks of the first view, 3 blocks, or every block
+    "tiny_s_ref": (dataclasses.replace(_tiny_s, name="tiny_s_ref", forced=16), None),
+    "tiny_forced3": (dataclasses.replace(W.WORKLOADS["tiny"], name="tiny_f3", forced=3), None),
+    "v3_ref": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_ref", forced=22), 3 * 1374),
+    "b128_forced": (dataclasses.replace(_tiny_s, name="b128_f", H=2, block=128, topk=3,
+                                        forced=2), 1100),
+    "forced_all": (dataclasses.replace(_tiny_s, name="forced_all", H=2, block=32, topk=5,
+                                       forced=100), 1000),
 }
 
 _cache = {}
@@ -33,12 +41,14 @@ def run_case(name):
     if name in _cache:
         return _cache[name]
     w, T = CASES[name]
-    print(f"[case {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk}", flush=True)
+    print(f"[case {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}", flush=True)
     x = cuda_inputs(w, T=T)
-    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk).run_all()
+    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
+                  forced_blocks=w.forced).run_all()
     torch.cuda.synchronize()
     hx = {n: host(t) for n, t in x.items()}
-    ora = O.forward_all(hx["q"], hx["k"], hx["v"], hx["gates"], w.block, w.topk)
+    ora = O.forward_all(hx["q"], hx["k"], hx["v"], hx["gates"], w.block, w.topk,
+                        forced=w.forced)
     ora["k_mean"] = O.pool(hx["k"], w.block)
     ora["v_mean"] = O.pool(hx["v"], w.block)
     _cache[name] = (w, x, hx, st, ora)
@@ -89,14 +99,17 @@ def test_cmp_output_and_scores(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_topk_bit_exact_on_gpu_scores(name):
     """Integer stage: on identical f32 score rows the GPU's choice must equal the oracle's
-    top-k on every row."""
+    (forced prefix, then top-k of the remaining blocks) on every row."""
     w, x, hx, st, ora = run_case(name)
     sc = host(st.score).numpy()[:, :, :st.Nb]
     got = host(st.sel).numpy()
+    F = st.forced
     for h in range(sc.shape[0]):
         for i in range(sc.shape[1]):
-            np.testing.assert_array_equal(got[h, i], O.topk(sc[h, i], w.topk),
-                                          err_msg=f"row h={h} i={i}")
+            want = np.arange(F, dtype=np.int32)
+            if F < st.Nb:
+                want = np.concatenate([want, F + O.topk(sc[h, i, F:], w.topk)])
+            np.testing.assert_array_equal(got[h, i], want, err_msg=f"row h={h} i={i}")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -140,9 +153,10 @@ def test_topk_ties_and_fallback():
 @pytest.mark.parametrize("name", list(CASES))
 def test_selection_indices(name):
     w, x, hx, st, ora = run_case(name)
-    frac, diff = check_selection(host(st.sel).numpy(), ora["score"], ora["sel"], min(w.topk, st.Nb))
+    frac, diff = check_selection(host(st.sel).numpy(), ora["score"], ora["sel"],
+                                 st.k_eff - st.forced, forced=st.forced)
     print(f"[{name}] rows held to exact index parity: {frac:.1%}, near-tie rows differing: {len(diff)}")
-    if name in ("tiny_s", "v3_ragged"):
+    if name in ("tiny_s", "v3_ragged", "tiny_s_ref", "v3_ref"):
         assert frac > 0.5
 
 
@@ -166,9 +180,10 @@ def test_end_to_end(name):
     set are compared with the oracle run on the GPU's own indices."""
     w, x, hx, st, ora = run_case(name)
     Nb = st.Nb
-    k_eff = min(w.topk, Nb)
+    k_eff = st.k_eff
     sel = torch.empty(w.H, Nb, k_eff, dtype=torch.int32, device="cuda")
-    out, _ = S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, sel_idx=sel)
+    out, _ = S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, sel_idx=sel,
+                               forced_blocks=w.forced)
     torch.cuda.synchronize()
     gsel = host(sel).numpy()
     ref = ora["out"]
@@ -176,7 +191,7 @@ def test_end_to_end(name):
         rows_h = np.repeat(np.arange(w.H), Nb)
         rows_i = np.tile(np.arange(Nb), w.H)
         r = O.forward_rows(hx["q"], hx["k"], hx["v"], hx["gates"], w.block, w.topk, rows_h,
-                           rows_i, sel_in=gsel.reshape(-1, k_eff))
+                           rows_i, sel_in=gsel.reshape(-1, k_eff), forced=w.forced)
         T = x["q"].shape[0]
         ref = np.ascontiguousarray(r["out"].reshape(w.H, Nb * w.block, 64)[:, :T]
                                    .transpose(1, 0, 2))

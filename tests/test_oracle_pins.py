@@ -275,3 +275,43 @@ def test_tiny_iid_has_no_clear_topk_rows_but_tiny_s_does():
         return (gap > 1e-3).mean()
     assert gap_fraction("tiny") == 0.0
     assert gap_fraction("tiny_s") > 0.5
+
+
+# ----------------------------------------------------------------------------- forced blocks
+@pytest.mark.parametrize("forced", [1, 3, 7])
+def test_forced_prefix_then_topk_of_the_rest(forced):
+    """Forced reference blocks (the VGGT hybrid keeps the reference frame dense): the first F
+    blocks are always kept and the other k are the brute-force top-k of the remaining scores;
+    the selection branch is masked SDPA over exactly those blocks."""
+    T, B, k = 320, 16, 4
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=T)
+    r = O.forward_all(x["q"], x["k"], x["v"], x["gates"], B, k, forced=forced)
+    Nb = -(-T // B)
+    assert r["sel"].shape[-1] == O.num_selected(T, B, k, forced) == forced + k
+    for h in range(w.H):
+        for i in range(Nb):
+            row = r["sel"][h, i]
+            np.testing.assert_array_equal(row[:forced], np.arange(forced))
+            np.testing.assert_array_equal(row[forced:], forced + brute_topk(r["score"][h, i, forced:], k))
+    blk = torch.arange(T) // B
+    h = 1
+    mask = torch.zeros(T, T, dtype=torch.bool)
+    for i in range(Nb):
+        cols = torch.isin(blk, torch.from_numpy(r["sel"][h, i].astype(np.int64)))
+        mask[(blk == i).nonzero()[:, None, 0], cols.nonzero()[None, :, 0]] = True
+    ref = sdpa(x["q"][:, h:h + 1], x["k"][:, h:h + 1], x["v"][:, h:h + 1], 1 / 8,
+               mask=mask.unsqueeze(0))
+    np.testing.assert_allclose(r["osel"][:, h], ref[:, 0], atol=1e-12)
+
+
+def test_forced_zero_is_the_plain_method_and_all_forced_is_dense():
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=200)
+    a = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 3)
+    b = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 3, forced=0)
+    np.testing.assert_array_equal(a["sel"], b["sel"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    c = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 3, forced=50)  # F >= Nb = 13
+    assert c["sel"].shape[-1] == 13
+    np.testing.assert_allclose(c["osel"], sdpa(x["q"], x["k"], x["v"], 1 / 8), atol=1e-12)
