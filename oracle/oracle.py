@@ -223,6 +223,56 @@ def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = Non
     return full
 
 
+def window_order(views: int, special: int, grid_h: int, grid_w: int, win_h: int,
+                 win_w: int) -> np.ndarray:
+    """Token order that makes contiguous blocks spatial windows (2-D pooling windows).
+
+    The compression branch pools by spatial downsampling of the patch grid (the summary,
+    "Methodologie" 1) and the model takes image sides in multiples of 56 pixels, i.e. patch
+    grids in multiples of 4 (README "Notice" 1). Reading used here: each view is `special`
+    tokens followed by a row-major grid_h x grid_w patch grid; the grid is cut into
+    win_h x win_w windows. Position p of the reordered sequence holds token order[p]:
+    for each view, its windows in row-major window order, each window's patches row-major;
+    after all views, every view's special tokens (view by view, in their own order).
+    """
+    if grid_h % win_h or grid_w % win_w:
+        raise ValueError("windows must tile the patch grid")
+    per_view = special + grid_h * grid_w
+    order = []
+    for v in range(views):
+        base = v * per_view + special
+        for a in range(grid_h // win_h):
+            for b in range(grid_w // win_w):
+                for r in range(win_h):
+                    row = base + (a * win_h + r) * grid_w + b * win_w
+                    order.extend(range(row, row + win_w))
+    for v in range(views):
+        order.extend(range(v * per_view, v * per_view + special))
+    return np.asarray(order, dtype=np.int64)
+
+
+def forward_windows(q, k, v, gates, B: int, topk_: int, layout: Sequence[int],
+                    scale: Optional[float] = None, forced: int = 0):
+    """The forward pass on window-ordered tokens: reorder q, k, v (and per-token gates) by
+    window_order(*layout), run forward_all, and put out/ocmp/osel back in the caller's token
+    order. lse stays in the caller's order too; score and sel refer to blocks of the
+    reordered sequence."""
+    order = window_order(*layout)
+    a, b, c = _f32(q), _f32(k), _f32(v)
+    if order.size != a.shape[0]:
+        raise ValueError("layout does not match the token count")
+    g = _f32(gates)
+    gp = g[order] if g.ndim == 3 else g
+    r = forward_all(a[order], b[order], c[order], gp, B, topk_, scale=scale, forced=forced)
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    for name in ("out", "ocmp", "osel"):
+        r[name] = np.ascontiguousarray(r[name][inv])
+    r["lse"] = np.ascontiguousarray(r["lse"][:, inv])
+    r["order"] = order
+    return r
+
+
 def timed(fn, *args, **kw):
     t0 = time.perf_counter()
     r = fn(*args, **kw)

@@ -315,3 +315,89 @@ def test_forced_zero_is_the_plain_method_and_all_forced_is_dense():
     c = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 3, forced=50)  # F >= Nb = 13
     assert c["sel"].shape[-1] == 13
     np.testing.assert_allclose(c["osel"], sdpa(x["q"], x["k"], x["v"], 1 / 8), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- 2-D windows
+def test_window_order_hand_enumerated():
+    """2 views, 1 special token, 4x4 grid, 2x2 windows (17 tokens per view), written out by
+    hand: view 0's grid starts at token 1, so window (0,0) holds rows 0-1, cols 0-1 =
+    tokens 1,2,5,6; view 1 starts at 17 (its grid at 18); the specials 0 and 17 go last."""
+    want = [1, 2, 5, 6, 3, 4, 7, 8, 9, 10, 13, 14, 11, 12, 15, 16,
+            18, 19, 22, 23, 20, 21, 24, 25, 26, 27, 30, 31, 28, 29, 32, 33,
+            0, 17]
+    np.testing.assert_array_equal(O.window_order(2, 1, 4, 4, 2, 2), want)
+
+
+@pytest.mark.parametrize("layout", [(3, 5, 8, 12, 4, 4), (2, 0, 16, 16, 8, 8), (1, 2, 6, 4, 3, 2),
+                                    (4, 5, 8, 8, 4, 8)])
+def test_window_order_is_a_bijection_of_spatial_windows(layout):
+    """Every position is used once, and each run of win_h*win_w grid positions is exactly one
+    win_h x win_w rectangle of one view's grid (catches swapped row/col strides, a window
+    stepping across views, specials left inside the grid part)."""
+    V, S, Gh, Gw, wh, ww = layout
+    order = O.window_order(*layout)
+    per = S + Gh * Gw
+    assert sorted(order.tolist()) == list(range(V * per))
+    grid = order[:V * Gh * Gw].reshape(-1, wh * ww)
+    for blk in grid:
+        view, r = blk // per, blk % per - S
+        assert (view == view[0]).all() and (r >= 0).all()
+        rows, cols = r // Gw, r % Gw
+        assert rows.min() % wh == 0 and rows.max() - rows.min() == wh - 1
+        assert cols.min() % ww == 0 and cols.max() - cols.min() == ww - 1
+        assert len(set(zip(rows.tolist(), cols.tolist()))) == wh * ww
+    specials = order[V * Gh * Gw:]
+    assert specials.tolist() == [v * per + s for v in range(V) for s in range(S)]
+
+
+def test_window_order_full_width_rows_is_identity_on_the_grid():
+    """Windows one row high and one grid wide keep row-major order: only specials move."""
+    order = O.window_order(3, 2, 4, 6, 1, 6)
+    per = 2 + 24
+    want = [v * per + 2 + i for v in range(3) for i in range(24)] + \
+           [v * per + s for v in range(3) for s in range(2)]
+    np.testing.assert_array_equal(order, want)
+
+
+def test_window_blocks_pool_spatial_windows():
+    """No special tokens, k and v constant on every 4x4 window of an 8x8 grid, B = 16: with
+    window order every block is one constant window, so the compression branch equals dense
+    softmax attention over all tokens (every block has the same size). With plain 1-D
+    blocks each block mixes rows of two windows and the equality fails."""
+    V, Gh, Gw, wh, ww, H, D = 2, 8, 8, 4, 4, 2, 64
+    T = V * Gh * Gw
+    nwin = V * (Gh // wh) * (Gw // ww)
+    kw, vw = bf16_tensor((nwin, H, D), 41, 0.8), bf16_tensor((nwin, H, D), 42)
+    t = np.arange(T)
+    view, r = t // (Gh * Gw), t % (Gh * Gw)
+    win = view * (Gh // wh) * (Gw // ww) + (r // Gw) // wh * (Gw // ww) + (r % Gw) // ww
+    win = torch.from_numpy(win)
+    k, v = kw[win].contiguous(), vw[win].contiguous()
+    q = bf16_tensor((T, H, D), 43)
+    gates = torch.ones(H, 2)
+    dense = sdpa(q, k, v, 1 / 8)
+    rw = O.forward_windows(q, k, v, gates, wh * ww, 2, (V, 0, Gh, Gw, wh, ww))
+    np.testing.assert_allclose(rw["ocmp"], dense, atol=1e-12)
+    r1 = O.forward_all(q, k, v, gates, wh * ww, 2)
+    assert np.abs(r1["ocmp"] - dense).max() > 1e-3
+
+
+def test_window_forward_is_the_plain_forward_on_reordered_tokens():
+    """Identity layout (no specials, full-width rows) gives forward_all unchanged; with
+    k = all blocks the selection branch is dense attention in any token order; per-token
+    gates travel with their tokens."""
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w)
+    T = x["q"].shape[0]
+    a = O.forward_windows(x["q"], x["k"], x["v"], x["gates"], 16, 4, (4, 0, 16, 16, 1, 16))
+    b = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 4)
+    for n in ("out", "ocmp", "osel", "lse", "sel"):
+        np.testing.assert_array_equal(a[n], b[n])
+    layout = (4, 0, 16, 16, 4, 4)
+    c = O.forward_windows(x["q"], x["k"], x["v"], x["gates"], 16, 64, layout)
+    np.testing.assert_allclose(c["osel"], sdpa(x["q"], x["k"], x["v"], 1 / 8), atol=1e-12)
+    g = torch.rand(T, w.H, 2, generator=torch.Generator().manual_seed(5))
+    d = O.forward_windows(x["q"], x["k"], x["v"], g, 16, 4, layout)
+    gd = g.double().numpy()
+    np.testing.assert_allclose(d["out"], gd[..., :1] * d["ocmp"] + gd[..., 1:] * d["osel"],
+                               atol=1e-12)
