@@ -47,7 +47,9 @@ typedef enum {
   S3R_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, negative forced_blocks, bad
                               stride or alignment */
   S3R_ERR_UNSUPPORTED = 2, /* well-formed but not built: D != 64, B not 16/32/64/128,
-                              more than 24576 blocks, H > 65535 */
+                              H > 65535, T >= 2^31, or more than 24576 blocks where the
+                              separate top-k kernel is needed (speed3r_topk, and B = 128 or
+                              more than 64 chosen blocks) */
   S3R_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
   S3R_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } s3r_status;
@@ -175,6 +177,54 @@ s3r_status speed3r_sel_combine(const s3r_params* p, const void* q, const void* w
 s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void* k,
                                   const void* v, void* out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * 2-D pooling windows. The compression branch pools by spatial downsampling of the patch grid
+ * (summary "Methodologie" 1) and the model takes image sides in multiples of 56 pixels, i.e.
+ * patch grids in multiples of 4 patches (README "Notice" 1). With contiguous blocks that is
+ * obtained by reordering the tokens: each view is `special` tokens followed by its row-major
+ * grid_h x grid_w patch grid; in window order every view's grid is listed window by window
+ * (windows row-major, patches row-major inside a window) and all views' special tokens follow
+ * at the end, in view order. A block of B = win_h * win_w positions is then one spatial
+ * window (B a multiple of win_h * win_w: a row of B / (win_h * win_w) windows).
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t views;     /* V >= 1 */
+  int32_t special;   /* S >= 0 tokens at the start of every view */
+  int32_t grid_h;    /* patch grid of every view, >= 1 */
+  int32_t grid_w;
+  int32_t win_h;     /* window shape: win_h divides grid_h, win_w divides grid_w */
+  int32_t win_w;
+} s3r_windows;
+
+/* Caller token held at position `pos` of the window order, for T = V * (S + grid_h*grid_w)
+ * tokens (host function). -1 if w is invalid or pos is outside [0, T). */
+int64_t speed3r_window_source(const s3r_windows* w, int64_t pos);
+
+/* Reorders a bf16 [T][H][64] tensor into window order (inverse = 0: dst[pos] =
+ * src[source(pos)]) or back (inverse = 1: dst[source(pos)] = src[pos]), T = V * (S + grid).
+ * Strides are in elements, multiples of 8; src and dst must not overlap. Byte-exact copy. */
+s3r_status speed3r_window_permute(const s3r_windows* w, int32_t H, const void* src,
+                                  int64_t src_stride_t, int64_t src_stride_h, void* dst,
+                                  int64_t dst_stride_t, int64_t dst_stride_h, int32_t inverse,
+                                  hipStream_t stream);
+
+/* Bytes of workspace speed3r_sparse_attn_fwd_windows needs: window-ordered copies of q, k, v
+ * (and of per-token gates), the window-ordered output, then speed3r_workspace_size of the
+ * reordered problem. 0 if p or w is invalid or p->T != V * (S + grid_h*grid_w). */
+size_t speed3r_windows_workspace_size(const s3r_params* p, const s3r_windows* w);
+
+/* The sparse forward pass with 2-D windows as blocks: reorders q, k, v (and per-token gates)
+ * into window order inside the workspace, runs speed3r_sparse_attn_fwd on them, and writes
+ * out (bf16 [T][H][64], contiguous) back in the caller's token order. sel_idx (optional,
+ * [H][Nb][n_sel]) and forced_blocks refer to blocks of the window order: forced blocks
+ * 0..F-1 are the first view's first windows. Arguments are checked as for
+ * speed3r_sparse_attn_fwd; on any error nothing is launched. */
+s3r_status speed3r_sparse_attn_fwd_windows(const s3r_params* p, const s3r_windows* w,
+                                           const void* q, const void* k, const void* v,
+                                           const float* gates, void* out, int32_t* sel_idx,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

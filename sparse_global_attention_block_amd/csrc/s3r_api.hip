@@ -49,7 +49,6 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->H = p->H;
   d->B = p->block;
   d->Nb = (p->T + p->block - 1) / p->block;
-  if (d->Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   d->n_ctiles = (d->Nb + kTileKeys - 1) / kTileKeys;
   d->n_ktiles = (d->T + kTileKeys - 1) / kTileKeys;
   d->ld = d->n_ctiles * kTileKeys;
@@ -58,6 +57,8 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->k_eff = d->forced + (p->topk < rest ? p->topk : rest);
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)kD);
   d->fold_topk = d->B <= 64 && d->k_eff - d->forced <= kFusedTopkMaxK;
+  // the separate top-k kernel holds a score row in registers; the folded one has no limit
+  if (!d->fold_topk && d->Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   return S3R_OK;
 }
 
@@ -142,6 +143,58 @@ s3r_status run_cmp_fused(const Dims& d, CmpArgs a, hipStream_t stream) {
     if (st != S3R_OK) return st;
   }
   return hip_status(launch_cmp_fused(a, stream));
+}
+
+// ---------------------------------------------------------------------------------------
+// 2-D windows: layout checks and the workspace of the windowed forward pass
+// ---------------------------------------------------------------------------------------
+bool window_layout(const s3r_windows* w, WindowLayout* L, int64_t* T) {
+  if (!w || w->views < 1 || w->special < 0 || w->grid_h < 1 || w->grid_w < 1 ||
+      w->win_h < 1 || w->win_w < 1 || w->grid_h % w->win_h || w->grid_w % w->win_w)
+    return false;
+  const int64_t per_view = (int64_t)w->special + (int64_t)w->grid_h * w->grid_w;
+  if (w->views > (((int64_t)1 << 31) - 1) / per_view) return false;
+  L->views = w->views; L->special = w->special; L->grid_h = w->grid_h; L->grid_w = w->grid_w;
+  L->win_h = w->win_h; L->win_w = w->win_w;
+  *T = w->views * per_view;
+  return true;
+}
+
+// window-ordered copies of q, k, v, gates and out, then the inner workspace
+struct WindowWs {
+  size_t q, k, v, gates, out, inner, end;
+};
+
+WindowWs window_ws(const Dims& d, bool token_gates, size_t inner_bytes) {
+  WindowWs L;
+  const size_t tok = align256((size_t)d.T * d.H * kD * 2);
+  size_t off = 0;
+  L.q = off; off += tok;
+  L.k = off; off += tok;
+  L.v = off; off += tok;
+  L.gates = off; off += token_gates ? align256((size_t)d.T * d.H * 2 * sizeof(float)) : 0;
+  L.out = off; off += tok;
+  L.inner = off; off += inner_bytes;
+  L.end = off;
+  return L;
+}
+
+s3r_params windowed_params(const s3r_params* p) {
+  s3r_params r = *p;
+  r.q_stride_t = r.k_stride_t = r.v_stride_t = (int64_t)p->H * kD;
+  r.q_stride_h = r.k_stride_h = r.v_stride_h = kD;
+  r.gate_stride_t = p->gate_stride_t ? 2 * (int64_t)p->H : 0;
+  return r;
+}
+
+WindowCopyArgs copy_args(const WindowLayout& w, int64_t T, int32_t H, int32_t inverse,
+                         const void* src, int64_t src_st, int64_t src_sh, void* dst,
+                         int64_t dst_st, int64_t dst_sh) {
+  WindowCopyArgs a;
+  a.w = w; a.T = T; a.H = H; a.inverse = inverse;
+  a.src = (const unsigned char*)src; a.src_st = src_st; a.src_sh = src_sh;
+  a.dst = (unsigned char*)dst; a.dst_st = dst_st; a.dst_sh = dst_sh;
+  return a;
 }
 
 }  // namespace
@@ -265,6 +318,7 @@ s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_id
   if (st != S3R_OK) return st;
   if (!score || !aligned(score, 4) || !sel_idx || !aligned(sel_idx, 4))
     return S3R_ERR_INVALID_ARG;
+  if (d.Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   TopkArgs a;
   a.score = score; a.ld = d.ld; a.Nb = d.Nb; a.n_rows = (int64_t)d.H * d.Nb;
   a.n_sel = (int32_t)d.k_eff; a.forced = (int32_t)d.forced; a.sel = sel_idx;
@@ -349,6 +403,84 @@ s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void
   AttnArgs a = attn_args(p, d, q, raw);
   a.out = (uint16_t*)out;
   return hip_status(launch_dense(a, stream));
+}
+
+int64_t speed3r_window_source(const s3r_windows* w, int64_t pos) {
+  WindowLayout L;
+  int64_t T;
+  if (!window_layout(w, &L, &T) || pos < 0 || pos >= T) return -1;
+  return window_source(L, pos);
+}
+
+s3r_status speed3r_window_permute(const s3r_windows* w, int32_t H, const void* src,
+                                  int64_t src_stride_t, int64_t src_stride_h, void* dst,
+                                  int64_t dst_stride_t, int64_t dst_stride_h, int32_t inverse,
+                                  hipStream_t stream) {
+  WindowLayout L;
+  int64_t T;
+  if (!window_layout(w, &L, &T) || H < 1 || H > 65535 || !tok_ok(src) || !tok_ok(dst) ||
+      !valid_stride(src_stride_t) || !valid_stride(src_stride_h) ||
+      !valid_stride(dst_stride_t) || !valid_stride(dst_stride_h) ||
+      (inverse != 0 && inverse != 1))
+    return S3R_ERR_INVALID_ARG;
+  return hip_status(launch_window_copy(
+      copy_args(L, T, H, inverse, src, src_stride_t * 2, src_stride_h * 2, dst,
+                dst_stride_t * 2, dst_stride_h * 2), 128, stream));
+}
+
+size_t speed3r_windows_workspace_size(const s3r_params* p, const s3r_windows* w) {
+  Dims d;
+  WindowLayout L;
+  int64_t T;
+  if (check_params(p, &d) != S3R_OK || !window_layout(w, &L, &T) || T != p->T) return 0;
+  return window_ws(d, p->gate_stride_t != 0, layout(d).end).end;
+}
+
+s3r_status speed3r_sparse_attn_fwd_windows(const s3r_params* p, const s3r_windows* w,
+                                           const void* q, const void* k, const void* v,
+                                           const float* gates, void* out, int32_t* sel_idx,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  WindowLayout L;
+  int64_t T;
+  if (!window_layout(w, &L, &T) || T != p->T) return S3R_ERR_INVALID_ARG;
+  if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !out ||
+      !aligned(out, 16) || (sel_idx && !aligned(sel_idx, 4)))
+    return S3R_ERR_INVALID_ARG;
+  // per-token gates move as 8-byte (token, head) pairs
+  if (p->gate_stride_t && (!aligned(gates, 8) || p->gate_stride_t % 2)) return S3R_ERR_INVALID_ARG;
+  const bool token_gates = p->gate_stride_t != 0;
+  const WindowWs W = window_ws(d, token_gates, layout(d).end);
+  if ((st = check_ws(workspace, workspace_bytes, W.end)) != S3R_OK) return st;
+  unsigned char* ws = (unsigned char*)workspace;
+  const s3r_params pw = windowed_params(p);
+  const int64_t row = (int64_t)d.H * kD * 2;
+  const void* srcs[3] = {q, k, v};
+  const int64_t st_t[3] = {p->q_stride_t, p->k_stride_t, p->v_stride_t};
+  const int64_t st_h[3] = {p->q_stride_h, p->k_stride_h, p->v_stride_h};
+  const size_t offs[3] = {W.q, W.k, W.v};
+  for (int x = 0; x < 3; ++x) {
+    st = hip_status(launch_window_copy(copy_args(L, T, d.H, 0, srcs[x], st_t[x] * 2,
+                                                 st_h[x] * 2, ws + offs[x], row, kD * 2),
+                                       128, stream));
+    if (st != S3R_OK) return st;
+  }
+  const float* g = gates;
+  if (token_gates) {
+    st = hip_status(launch_window_copy(copy_args(L, T, d.H, 0, gates, p->gate_stride_t * 4, 8,
+                                                 ws + W.gates, (int64_t)d.H * 8, 8),
+                                       8, stream));
+    if (st != S3R_OK) return st;
+    g = (const float*)(ws + W.gates);
+  }
+  st = speed3r_sparse_attn_fwd(&pw, ws + W.q, ws + W.k, ws + W.v, g, ws + W.out, sel_idx,
+                               ws + W.inner, workspace_bytes - W.inner, stream);
+  if (st != S3R_OK) return st;
+  return hip_status(launch_window_copy(copy_args(L, T, d.H, 1, ws + W.out, row, kD * 2, out,
+                                                 row, kD * 2), 128, stream));
 }
 
 }  // extern "C"

@@ -66,6 +66,43 @@ struct AttnArgs {
   uint16_t* out;           // bf16 [T][H][64]
 };
 
+// Token layout of the window order (see s3r_window.hip): views x (special + grid_h*grid_w).
+struct WindowLayout {
+  int64_t views;
+  int32_t special, grid_h, grid_w, win_h, win_w;
+};
+
+// Caller token of position pos of the window-ordered sequence (pos < views*(special+grid)).
+__host__ __device__ inline int64_t window_source(const WindowLayout& w, int64_t pos) {
+  const int64_t grid = (int64_t)w.grid_h * w.grid_w;
+  const int64_t per_view = w.special + grid;
+  const int64_t grid_total = w.views * grid;
+  if (pos < grid_total) {
+    const int64_t v = pos / grid;
+    const int64_t r = pos - v * grid;
+    const int64_t win = (int64_t)w.win_h * w.win_w;
+    const int64_t wi = r / win, e = r - wi * win;
+    const int64_t nwx = w.grid_w / w.win_w;
+    const int64_t wy = wi / nwx, wx = wi - wy * nwx;
+    const int64_t i = e / w.win_w, j = e - i * w.win_w;
+    return v * per_view + w.special + (wy * w.win_h + i) * w.grid_w + wx * w.win_w + j;
+  }
+  const int64_t u = pos - grid_total;
+  const int64_t v = u / w.special;
+  return v * per_view + (u - v * w.special);
+}
+
+struct WindowCopyArgs {
+  WindowLayout w;
+  int64_t T;
+  int32_t H;
+  int32_t inverse;         // 0: dst[pos] = src[source(pos)]; 1: dst[source(pos)] = src[pos]
+  const unsigned char* src;
+  int64_t src_st, src_sh;  // byte strides between tokens / heads
+  unsigned char* dst;
+  int64_t dst_st, dst_sh;
+};
+
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s);
@@ -76,5 +113,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sel(const AttnArgs& a, hipStream_t s);
 hipError_t launch_dense(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_window_copy(const WindowCopyArgs& a, int row_bytes, hipStream_t s);
 
 }  // namespace s3r

@@ -32,6 +32,14 @@ class Params(ctypes.Structure):
     ]
 
 
+class Windows(ctypes.Structure):
+    """Token layout for 2-D pooling windows: views x (special + grid_h * grid_w)."""
+    _fields_ = [
+        ("views", ctypes.c_int64), ("special", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+        ("grid_w", ctypes.c_int32), ("win_h", ctypes.c_int32), ("win_w", ctypes.c_int32),
+    ]
+
+
 class Speed3RError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {status_string(status)}")
@@ -66,6 +74,17 @@ EXPORTS = {
                             [ctypes.c_void_p] * 6),
     "speed3r_dense_attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 5 +
                                [ctypes.c_size_t, ctypes.c_void_p]),
+    "speed3r_window_source": (ctypes.c_int64, [ctypes.POINTER(Windows), ctypes.c_int64]),
+    "speed3r_window_permute": (ctypes.c_int, [ctypes.POINTER(Windows), ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int32, ctypes.c_void_p]),
+    "speed3r_windows_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params),
+                                                         ctypes.POINTER(Windows)]),
+    "speed3r_sparse_attn_fwd_windows": (ctypes.c_int, [ctypes.POINTER(Params),
+                                                       ctypes.POINTER(Windows)] +
+                                        [ctypes.c_void_p] * 6 +
+                                        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -212,6 +231,51 @@ def dense_attn_fwd(q, k, v, scale: float = 0.0, out=None, workspace=None):
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream()))
     return out
+
+
+def make_windows(layout) -> Windows:
+    """layout = (views, special, grid_h, grid_w, win_h, win_w)."""
+    return Windows(*[int(x) for x in layout])
+
+
+def window_source(layout, pos: int) -> int:
+    return int(lib().speed3r_window_source(ctypes.byref(make_windows(layout)), pos))
+
+
+def window_permute(layout, src: torch.Tensor, dst: Optional[torch.Tensor] = None,
+                   inverse: bool = False) -> torch.Tensor:
+    """Reorder a bf16 [T, H, 64] tensor into window order (or back, inverse=True)."""
+    w = make_windows(layout)
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=src.dtype, device=src.device)
+    _check("speed3r_window_permute", lib().speed3r_window_permute(
+        ctypes.byref(w), src.shape[1], _ptr(src), src.stride(0), src.stride(1), _ptr(dst),
+        dst.stride(0), dst.stride(1), int(inverse), _stream()))
+    return dst
+
+
+def windows_workspace_size(p: Params, layout) -> int:
+    return int(lib().speed3r_windows_workspace_size(ctypes.byref(p),
+                                                     ctypes.byref(make_windows(layout))))
+
+
+def sparse_attn_fwd_windows(q, k, v, gates, block: int, topk: int, layout, scale: float = 0.0,
+                            out: Optional[torch.Tensor] = None,
+                            sel_idx: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0
+                            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward pass with 2-D windows as blocks; out in the caller's token order, sel_idx over
+    blocks of the window order."""
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
+    w = make_windows(layout)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(windows_workspace_size(p, layout), q.device)
+    _check("speed3r_sparse_attn_fwd_windows", lib().speed3r_sparse_attn_fwd_windows(
+        ctypes.byref(p), ctypes.byref(w), _ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(out),
+        _ptr(sel_idx), _ptr(workspace), workspace.numel(), _stream()))
+    return out, sel_idx
 
 
 class Stages:

@@ -16,6 +16,10 @@ Generators:
     q and k share the projection (so tokens of the same view attract each other), v has its
     own. Optionally the k and v rows of each view's 5 special tokens are multiplied by
     ``special_mult`` to create heavy-hitter keys.
+  * Window workloads (``grid`` set) add to q and k a smooth term of each patch's grid
+    position: ``spatial`` * phi(row, col) @ W_pos[h], with phi the 8 features cos/sin of
+    pi*m*row/grid_h and pi*m*col/grid_w (m = 1, 2), W_pos ~ N(0, 1/8) per head; zero on the
+    special tokens.
   * Gates: sigmoid(N(0, 1)) per head and branch, shape [H, 2] (column 0 weights the
     compression branch, column 1 the selection branch).
 
@@ -27,7 +31,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import torch
 
@@ -50,6 +54,9 @@ class Workload:
     special_mult: float = 1.0
     D: int = D_HEAD
     forced: int = 0       # leading key blocks every query block attends (reference view)
+    grid: Optional[Tuple[int, int]] = None    # patch grid (rows, cols) after the specials
+    window: Optional[Tuple[int, int]] = None  # 2-D pooling window (rows, cols): window order
+    spatial: float = 0.0  # weight of the smooth 2-D position term (grid workloads only)
 
     @property
     def T(self) -> int:
@@ -58,6 +65,12 @@ class Workload:
     @property
     def n_blocks(self) -> int:
         return -(-self.T // self.block)
+
+    def layout(self, views: Optional[int] = None):
+        """(views, special, grid_h, grid_w, win_h, win_w) of a window workload, else None."""
+        if self.window is None:
+            return None
+        return (views or self.views, self.special, *self.grid, *self.window)
 
     @property
     def k_eff(self) -> int:
@@ -71,6 +84,8 @@ class Workload:
             "T": self.T, "H": self.H, "D": self.D, "block": self.block, "topk": self.topk,
             "generator": self.gen, "seed": self.seed,
             **({"forced_blocks": self.forced} if self.forced else {}),
+            **({"grid": list(self.grid)} if self.grid else {}),
+            **({"window": list(self.window), "spatial": self.spatial} if self.window else {}),
             **({"iid_scale": self.iid_scale} if self.gen == "iid" else
                {"alpha": self.alpha, "special_tokens": self.special,
                 "special_kv_mult": self.special_mult}),
@@ -94,6 +109,13 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     # by every query block in addition to its top-16
     Workload("v1000_k16_ref", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
              special_mult=3.0, forced=22),
+    # 2-D windows: 560x560 images (a multiple of 56) give a 40x40 patch grid; 8x8 windows are
+    # the 64-token blocks; a smooth position term makes nearby patches alike
+    Workload("v1000_win8", 1000, 5 + 40 * 40, 5, 16, 64, 16, "structured", seed=1001,
+             special_mult=3.0, grid=(40, 40), window=(8, 8), spatial=0.5),
+    # 504x504 images: 36x36 grid in 4x4 windows of 16 tokens
+    Workload("v8_win4", 8, 5 + 36 * 36, 5, 4, 16, 8, "structured", seed=9, special_mult=3.0,
+             grid=(36, 36), window=(4, 4), spatial=0.5),
 ]}
 
 
@@ -135,9 +157,24 @@ def make_inputs(w: Workload, device="cpu", T: Optional[int] = None,
         emb_v = torch.einsum("ve,hed->vhd", e, w_v)
         pos = torch.arange(TT, device=dev) % w.tokens_per_view
         special = (pos < w.special) if w.special > 0 else None
+        pos_qk = None
+        if w.grid is not None and w.spatial != 0.0:
+            # smooth position term on the patch grid: 8 Fourier features of (row, col)
+            # projected per head (q and k share it, so nearby patches attract)
+            gh, gw = w.grid
+            cell = (pos - w.special).clamp(min=0)
+            r = torch.div(cell, gw, rounding_mode="floor").float() / gh
+            c = (cell % gw).float() / gw
+            feats = torch.stack([f(math.pi * m * x) for x in (r, c) for m in (1, 2)
+                                 for f in (torch.cos, torch.sin)], dim=1)  # [TT, 8]
+            feats[pos < w.special] = 0.0
+            w_pos = _randn((H, 8, D), w.seed, 13, dev, math.sqrt(1.0 / 8.0))
+            pos_qk = feats, w_pos
         for i, name in enumerate(("q", "k", "v")):
             x = _randn((TT, H, D), w.seed, i, dev)
             x.add_((emb_v if name == "v" else emb_qk)[view_of_t], alpha=w.alpha)
+            if pos_qk is not None and name != "v":
+                x.add_(torch.einsum("tf,hfd->thd", *pos_qk), alpha=w.spatial)
             if name in ("k", "v") and special is not None and w.special_mult != 1.0:
                 x[special] *= w.special_mult
             out[name] = x.to(torch.bfloat16)

@@ -5,8 +5,10 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
+from oracle import oracle as O
 from sparse_global_attention_block_amd import speed3r as S
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -70,7 +72,7 @@ def test_size_queries():
     (dict(scale=float("nan")), S.S3R_ERR_INVALID_ARG),
     (dict(st=(4 * 64 + 4, 64)), S.S3R_ERR_INVALID_ARG),   # token stride not a multiple of 8
     (dict(st=(-256, 64)), S.S3R_ERR_INVALID_ARG),
-    (dict(T=24577 * 16, B=16), S.S3R_ERR_UNSUPPORTED),     # more than 24576 blocks
+    (dict(T=24577 * 16, B=16, k=65), S.S3R_ERR_UNSUPPORTED),  # > 24576 blocks, not folded
     (dict(forced=-1), S.S3R_ERR_INVALID_ARG),
 ])
 def test_bad_params_rejected_everywhere(kw, code):
@@ -134,6 +136,16 @@ def test_workspace_too_small_or_missing():
                                     S.dense_workspace_size(p) - 1, None) == S.S3R_ERR_WORKSPACE
 
 
+def test_block_limit_only_without_folded_selection():
+    """More than 24576 blocks: fine when the selection folds into the compression pass (no
+    score row to hold), rejected by the separate top-k kernel."""
+    p = params(T=25079 * 64, H=16, B=64, k=16)
+    assert S.num_blocks(p) == 25079 and S.workspace_size(p) > 0
+    assert S.lib().speed3r_topk(ctypes.byref(p), FAKE, FAKE, None) == S.S3R_ERR_UNSUPPORTED
+    assert S.workspace_size(params(T=25079 * 64, H=16, B=128, k=16)) > 0  # 12540 blocks
+    assert S.workspace_size(params(T=25079 * 128, H=16, B=128, k=16)) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(S, "_lib", None)
     monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "missing.so"))
@@ -154,3 +166,54 @@ def test_fused_topk_limits():
     p = params(k=65, T=100 * 64, B=64, forced=60)
     assert S.num_selected(p) == 100
     assert S.workspace_size(p) < S.workspace_size(params(k=65, T=100 * 64, B=64))
+
+
+@pytest.mark.parametrize("layout", [(2, 1, 4, 4, 2, 2), (3, 5, 8, 12, 4, 4), (2, 0, 16, 16, 8, 8),
+                                    (4, 5, 40, 40, 8, 8)])
+def test_window_source_matches_oracle_order(layout):
+    """Host index function of the library against the oracle's own window order."""
+    order = O.window_order(*layout)
+    got = [S.window_source(layout, p) for p in range(order.size)]
+    np.testing.assert_array_equal(got, order)
+    assert S.window_source(layout, -1) == -1 and S.window_source(layout, order.size) == -1
+
+
+@pytest.mark.parametrize("layout", [(0, 5, 8, 8, 4, 4), (2, -1, 8, 8, 4, 4), (2, 5, 8, 8, 3, 4),
+                                    (2, 5, 8, 10, 4, 4), (2, 5, 8, 8, 0, 4)])
+def test_bad_window_layouts_rejected(layout):
+    L = S.lib()
+    w = S.make_windows(layout)
+    assert S.window_source(layout, 0) == -1
+    p = params(T=2 * (5 + 64), H=4, B=16, k=4)
+    assert S.windows_workspace_size(p, layout) == 0
+    assert L.speed3r_window_permute(ctypes.byref(w), 4, FAKE, 256, 64, FAKE, 256, 64, 0,
+                                    None) == S.S3R_ERR_INVALID_ARG
+    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
+    assert L.speed3r_sparse_attn_fwd_windows(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, FAKE,
+                                             FAKE, FAKE, None, ws, big, None) \
+        == S.S3R_ERR_INVALID_ARG
+
+
+def test_window_forward_checks():
+    """Token count must match the layout; per-token gates need an even stride; the workspace
+    adds the reordered copies to the plain forward's."""
+    L = S.lib()
+    layout = (2, 5, 8, 8, 4, 4)
+    w = S.make_windows(layout)
+    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
+    p = params(T=2 * 69, H=4, B=16, k=4)
+    need = S.windows_workspace_size(p, layout)
+    assert need > S.workspace_size(p) + 4 * 138 * 4 * 64 * 2 - 1
+    bad_T = params(T=2 * 69 + 1, H=4, B=16, k=4)
+    assert S.windows_workspace_size(bad_T, layout) == 0
+    assert L.speed3r_sparse_attn_fwd_windows(ctypes.byref(bad_T), ctypes.byref(w), FAKE, FAKE,
+                                             FAKE, FAKE, FAKE, None, ws, big, None) \
+        == S.S3R_ERR_INVALID_ARG
+    odd = params(T=2 * 69, H=4, B=16, k=4)
+    odd.gate_stride_t = 9
+    assert L.speed3r_sparse_attn_fwd_windows(ctypes.byref(odd), ctypes.byref(w), FAKE, FAKE,
+                                             FAKE, FAKE, FAKE, None, ws, big, None) \
+        == S.S3R_ERR_INVALID_ARG
+    assert L.speed3r_sparse_attn_fwd_windows(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, FAKE,
+                                             FAKE, FAKE, None, ws, ctypes.c_size_t(need - 1),
+                                             None) == S.S3R_ERR_WORKSPACE
