@@ -108,7 +108,12 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
     h = 0
     rng = np.random.default_rng(seed)
     rows = sorted(set([0, Nb - 1] + [int(r) for r in rng.integers(0, Nb, n_rows - 2)]))
-    hq, hk, hv = (x[n][:, h:h + 1].contiguous().cpu() for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    # window workloads: the oracle reorders the head's tokens itself (its own window order)
+    order = O.window_order(*w.layout()) if w.window else np.arange(T)
+    t_order = time.perf_counter() - t0
+    hq, hk, hv = (x[n][:, h:h + 1].cpu()[torch.from_numpy(order)].contiguous()
+                  for n in ("q", "k", "v"))
     hg = x["gates"][h:h + 1].cpu()
     t0 = time.perf_counter()
     kc, vc = O.pool(hk, w.block), O.pool(hv, w.block)
@@ -118,7 +123,7 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
                        kc=kc, vc=vc, forced=w.forced)
     t_rows = time.perf_counter() - t0
     per_row = t_rows / len(rows)
-    t_full = H * (t_pool + Nb * per_row)
+    t_full = t_order + H * (t_pool + Nb * per_row)
     # parity of the sampled rows
     gsel = sel_gpu[h, rows].cpu().numpy()
     same = float((gsel == r["sel"]).all(axis=-1).mean())
@@ -129,7 +134,8 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
                              rows, kc=kc, vc=vc, sel_in=gsel, forced=w.forced)
     for a, i in enumerate(rows):
         nn = min(T, (i + 1) * w.block) - i * w.block
-        g = out_gpu[i * w.block:i * w.block + nn, h].float().cpu().numpy()
+        toks = torch.from_numpy(order[i * w.block:i * w.block + nn]).to(out_gpu.device)
+        g = out_gpu[toks, h].float().cpu().numpy()
         d = abs(g - ref["out"][a, :nn])
         err_max = max(err_max, float(d.max()))
         err_sum += float(d.sum())
@@ -181,13 +187,20 @@ def main():
     T, H, D = x["q"].shape
     p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced)
     Nb = S.num_blocks(p)
-    ws = S.alloc_workspace(S.workspace_size(p), dev)
+    layout = w.layout()
+    ws = S.alloc_workspace(S.windows_workspace_size(p, layout) if layout else
+                           S.workspace_size(p), dev)
     out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
     sel = torch.empty(H, Nb, w.k_eff, dtype=torch.int32, device=dev)
 
     def step():
-        S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
-                          sel_idx=sel, workspace=ws, forced_blocks=w.forced)
+        if layout:  # 2-D windows: reorder in, forward, reorder out
+            S.sparse_attn_fwd_windows(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
+                                      layout, out=out, sel_idx=sel, workspace=ws,
+                                      forced_blocks=w.forced)
+        else:
+            S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
+                              sel_idx=sel, workspace=ws, forced_blocks=w.forced)
 
     for _ in range(args.warmup):
         step()
@@ -209,11 +222,29 @@ def main():
     del ws
     torch.cuda.empty_cache()
     folds = w.block <= 64 and w.k_eff - min(w.forced, Nb) <= 64
-    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, keep_o_sel=False,
+    xs, perm_ms = x, None
+    if layout:
+        # window order once; the reordering (3 tensors in, 1 out) is timed on its own
+        xs = {n: S.window_permute(layout, x[n]) for n in ("q", "k", "v")}
+        xs["gates"] = x["gates"]
+        tmp = torch.empty_like(out)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        p0.record()
+        for n in ("q", "k", "v"):
+            S.window_permute(layout, x[n], dst=tmp)
+        S.window_permute(layout, xs["q"], dst=tmp, inverse=True)
+        p1.record()
+        torch.cuda.synchronize()
+        perm_ms = p0.elapsed_time(p1)
+        del tmp
+    st = S.Stages(xs["q"], xs["k"], xs["v"], xs["gates"], w.block, w.topk, keep_o_sel=False,
                   keep_score=not folds, forced_blocks=w.forced)
     st.run_pool()
     st.run_lse()
     stage_ms = timed_stages(st, max(1, min(3, args.steps)))
+    if perm_ms is not None:
+        stage_ms["window_permute"] = perm_ms
     log(f"[bench] stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
     work = algorithmic_work(w, T, Nb)
     # pool stage = pool kernel + pack kernel; report the pool stage against both kernels' bytes
@@ -221,6 +252,8 @@ def main():
     for name, ms_k in stage_ms.items():
         if name == "pool":
             wk = {"bytes": work["pool"]["bytes"] + work["pack"]["bytes"], "bound": "hbm"}
+        elif name == "window_permute":  # 4 tensors, each read and written once
+            wk = {"bytes": 4 * 2 * T * H * D * 2, "bound": "hbm"}
         else:
             wk = work[name]
         if wk["bound"] == "hbm":
@@ -235,7 +268,7 @@ def main():
     roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
             "traffic": measured_traffic(w.name) if dom == "cmp_fused" else None}
-    del st
+    del st, xs
     torch.cuda.empty_cache()
 
     dense = None
