@@ -70,6 +70,10 @@ def lib():
             _i64, _i64, _f64p, _f64p, _f32p, _i64, _i64, _i32p, _i64p,
             ctypes.c_void_p, _f64p, _f64p, _f32p, _i32p, _f64p, _f64p]
         L.s3r_oracle_forward_rows.restype = None
+        L.s3r_oracle_backward.argtypes = [
+            _i64, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p, _i64, _i64, _f32p, _i64,
+            _i64, _f32p, _i64, _f32p, _i64, _i64, _i32p, _i32, _f64p, _f64p, _f64p, _f64p]
+        L.s3r_oracle_backward.restype = None
         L.s3r_oracle_num_threads.argtypes = []
         L.s3r_oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -221,6 +225,27 @@ def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = Non
     full["score"] = r["score"].reshape(H, Nb, Nb)
     full["sel"] = r["sel"].reshape(H, Nb, k_eff)
     return full
+
+
+def backward(q, k, v, gates, dout, B: int, sel, scale: Optional[float] = None):
+    """Gradients of the forward pass with the selection `sel` ([H, Nb, n_sel], e.g. the
+    forward's own choice) held fixed. dout is the gradient of out ([T, H, D]). Returns dq, dk,
+    dv ([T, H, D] float64) and dgates (the shape of gates: [H, 2] or [T, H, 2])."""
+    a, b, c = _f32(q), _f32(k), _f32(v)
+    T, H, D = a.shape
+    g = _f32(gates)
+    gate_st = 0 if g.ndim == 2 else H * 2
+    go = _f32(dout)
+    s = np.ascontiguousarray(np.asarray(sel, dtype=np.int32))
+    n_sel = s.shape[-1]
+    dq = np.empty((T, H, D), np.float64)
+    dk = np.empty((T, H, D), np.float64)
+    dv = np.empty((T, H, D), np.float64)
+    dg = np.empty(g.shape, np.float64)
+    lib().s3r_oracle_backward(T, H, D, B, default_scale(D) if scale is None else scale, a,
+                              H * D, D, b, H * D, D, c, H * D, D, g.reshape(-1), gate_st, go,
+                              H * D, D, s.reshape(-1), n_sel, dq, dk, dv, dg)
+    return {"dq": dq, "dk": dk, "dv": dv, "dgates": dg}
 
 
 def window_order(views: int, special: int, grid_h: int, grid_w: int, win_h: int,

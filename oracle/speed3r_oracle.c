@@ -32,7 +32,13 @@
  *     over the remaining blocks, so a row holds min(F, Nb) + min(k, Nb - min(F, Nb)) blocks;
  *   - the top-k decision is made on the scores rounded to float32 (the precision the GPU
  *     kernel decides in);
- *   - no masking (bidirectional attention), no forced blocks.
+ *   - no masking (bidirectional attention).
+ *
+ *  Backward pass (trainable sparse attention: the arXiv abstract and the README call the model
+ *  end-to-end trainable): s3r_oracle_backward differentiates the forward above with the
+ *  selection held fixed (top-k is piecewise constant, so no gradient flows through the block
+ *  scores), by the chain rule through each step: gated sum, both softmax attentions, and the
+ *  block means.
  *
  * Layout conventions: a token tensor x is addressed as x[t*st + h*sh + d] (float32), pooled
  * tensors as p[(h*Nb + j)*D + d] (float64). All outputs are caller-allocated.
@@ -293,3 +299,182 @@ int s3r_oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Gradient of the forward pass for one head h, with the selection sel ([Nb][nsel]) fixed.
+ * dout is the gradient of out ([T][H][D] addressed like the inputs, dst/dsh); dq, dk, dv are
+ * [T][H][D] (contiguous, only head h written, zero them first); dgate is [T][2] for per-token
+ * gates (gate_st != 0) or [2] for per-head gates, accumulated.
+ *   out_t      = g0 O_cmp_t + g1 O_sel_t
+ *   compression: c_tj = scale q_t.Kc_j, P = softmax_j, O_cmp_t = sum_j P_tj Vc_j
+ *     dO = g0 dout_t;  dg0 += dout_t.O_cmp_t;  dVc_j += P_tj dO;  dP_tj = dO.Vc_j
+ *     dc_tj = P_tj (dP_tj - sum_j' P_tj' dP_tj');  dq_t += scale sum_j dc_tj Kc_j;
+ *     dKc_j += scale dc_tj q_t;  then every token of block j gets dKc_j / n_j, dVc_j / n_j.
+ *   selection (tokens u of the union of the selected blocks): the same with k_u, v_u, g1. */
+void s3r_oracle_backward_head(int64_t T, int32_t H, int32_t D, int32_t B, double scale,
+                              const float* q, int64_t qst, int64_t qsh, const float* k,
+                              int64_t kst, int64_t ksh, const float* v, int64_t vst, int64_t vsh,
+                              const float* gates, int64_t gate_st, const float* dout,
+                              int64_t dst, int64_t dsh, const int32_t* sel, int32_t nsel,
+                              int32_t h, double* dq, double* dk, double* dv, double* dgate) {
+  const int64_t Nb = n_blocks(T, B);
+  double* kc = (double*)calloc((size_t)(Nb * D), sizeof(double));
+  double* vc = (double*)calloc((size_t)(Nb * D), sizeof(double));
+  double* dkc = (double*)calloc((size_t)(Nb * D), sizeof(double));
+  double* dvc = (double*)calloc((size_t)(Nb * D), sizeof(double));
+  double* c = (double*)malloc(sizeof(double) * (size_t)(T > Nb ? T : Nb));
+  double* dp = (double*)malloc(sizeof(double) * (size_t)(T > Nb ? T : Nb));
+  int64_t* u_tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)T);
+  char* chosen = (char*)malloc((size_t)Nb);
+  /* block means of this head */
+  for (int64_t j = 0; j < Nb; ++j) {
+    const int64_t n = block_len(T, B, j);
+    for (int32_t d = 0; d < D; ++d) {
+      double sk = 0.0, sv = 0.0;
+      for (int64_t t = j * B; t < j * B + n; ++t) {
+        sk += (double)k[t * kst + h * ksh + d];
+        sv += (double)v[t * vst + h * vsh + d];
+      }
+      kc[j * D + d] = sk / (double)n;
+      vc[j * D + d] = sv / (double)n;
+    }
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    const float* qt = q + t * qst + h * qsh;
+    const float* gt = dout + t * dst + h * dsh;
+    const double g0 = gates[t * gate_st + h * 2 + 0];
+    const double g1 = gates[t * gate_st + h * 2 + 1];
+    double* dqt = dq + (t * H + h) * D;
+    double* dg = dgate + (gate_st ? t * 2 : 0);
+    /* ---- compression branch ---- */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Nb; ++j) {
+      double dot = 0.0;
+      for (int32_t d = 0; d < D; ++d) dot += (double)qt[d] * kc[j * D + d];
+      c[j] = scale * dot;
+      if (c[j] > m) m = c[j];
+    }
+    double ssum = 0.0;
+    for (int64_t j = 0; j < Nb; ++j) ssum += exp(c[j] - m);
+    double delta = 0.0, go = 0.0;
+    for (int64_t j = 0; j < Nb; ++j) {
+      const double p = exp(c[j] - m) / ssum;
+      c[j] = p;
+      double dpj = 0.0, oj = 0.0;
+      for (int32_t d = 0; d < D; ++d) {
+        dpj += g0 * (double)gt[d] * vc[j * D + d];
+        oj += (double)gt[d] * vc[j * D + d];
+      }
+      dp[j] = dpj;
+      delta += p * dpj;
+      go += p * oj; /* dout_t . O_cmp_t */
+      for (int32_t d = 0; d < D; ++d) dvc[j * D + d] += p * g0 * (double)gt[d];
+    }
+    dg[0] += go;
+    for (int64_t j = 0; j < Nb; ++j) {
+      const double dcj = c[j] * (dp[j] - delta);
+      for (int32_t d = 0; d < D; ++d) {
+        dqt[d] += scale * dcj * kc[j * D + d];
+        dkc[j * D + d] += scale * dcj * (double)qt[d];
+      }
+    }
+    /* ---- selection branch over the union of the selected blocks of t's query block ---- */
+    const int64_t i = t / B;
+    memset(chosen, 0, (size_t)Nb);
+    for (int32_t a = 0; a < nsel; ++a) {
+      const int64_t j = sel[i * nsel + a];
+      if (j >= 0 && j < Nb) chosen[j] = 1;
+    }
+    int64_t n_u = 0;
+    for (int64_t j = 0; j < Nb; ++j)
+      if (chosen[j])
+        for (int64_t u = j * B; u < j * B + block_len(T, B, j); ++u) u_tok[n_u++] = u;
+    m = -INFINITY;
+    for (int64_t a = 0; a < n_u; ++a) {
+      const float* ku = k + u_tok[a] * kst + h * ksh;
+      double dot = 0.0;
+      for (int32_t d = 0; d < D; ++d) dot += (double)qt[d] * (double)ku[d];
+      c[a] = scale * dot;
+      if (c[a] > m) m = c[a];
+    }
+    ssum = 0.0;
+    for (int64_t a = 0; a < n_u; ++a) ssum += exp(c[a] - m);
+    delta = 0.0;
+    go = 0.0;
+    for (int64_t a = 0; a < n_u; ++a) {
+      const double p = exp(c[a] - m) / ssum;
+      c[a] = p;
+      const float* vu = v + u_tok[a] * vst + h * vsh;
+      double dpa = 0.0, oa = 0.0;
+      for (int32_t d = 0; d < D; ++d) {
+        dpa += g1 * (double)gt[d] * (double)vu[d];
+        oa += (double)gt[d] * (double)vu[d];
+      }
+      dp[a] = dpa;
+      delta += p * dpa;
+      go += p * oa; /* dout_t . O_sel_t */
+      double* dvu = dv + (u_tok[a] * H + h) * D;
+      for (int32_t d = 0; d < D; ++d) dvu[d] += p * g1 * (double)gt[d];
+    }
+    dg[1] += go;
+    for (int64_t a = 0; a < n_u; ++a) {
+      const double dsa = c[a] * (dp[a] - delta);
+      const float* ku = k + u_tok[a] * kst + h * ksh;
+      double* dku = dk + (u_tok[a] * H + h) * D;
+      for (int32_t d = 0; d < D; ++d) {
+        dqt[d] += scale * dsa * (double)ku[d];
+        dku[d] += scale * dsa * (double)qt[d];
+      }
+    }
+  }
+  /* block means: each token of block j receives 1/n_j of the pooled gradients */
+  for (int64_t j = 0; j < Nb; ++j) {
+    const int64_t n = block_len(T, B, j);
+    for (int64_t t = j * B; t < j * B + n; ++t)
+      for (int32_t d = 0; d < D; ++d) {
+        dk[(t * H + h) * D + d] += dkc[j * D + d] / (double)n;
+        dv[(t * H + h) * D + d] += dvc[j * D + d] / (double)n;
+      }
+  }
+  free(kc);
+  free(vc);
+  free(dkc);
+  free(dvc);
+  free(c);
+  free(dp);
+  free(u_tok);
+  free(chosen);
+}
+
+/* All heads (in parallel; each head writes only its own slices). dgates: [T][H][2] for
+ * per-token gates, [H][2] otherwise; every output is overwritten. */
+void s3r_oracle_backward(int64_t T, int32_t H, int32_t D, int32_t B, double scale,
+                         const float* q, int64_t qst, int64_t qsh, const float* k, int64_t kst,
+                         int64_t ksh, const float* v, int64_t vst, int64_t vsh,
+                         const float* gates, int64_t gate_st, const float* dout, int64_t dst,
+                         int64_t dsh, const int32_t* sel, int32_t nsel, double* dq, double* dk,
+                         double* dv, double* dgates) {
+  const int64_t Nb = n_blocks(T, B);
+  memset(dq, 0, sizeof(double) * (size_t)(T * H * D));
+  memset(dk, 0, sizeof(double) * (size_t)(T * H * D));
+  memset(dv, 0, sizeof(double) * (size_t)(T * H * D));
+  const int64_t n_dg = gate_st ? T * H * 2 : (int64_t)H * 2;
+  memset(dgates, 0, sizeof(double) * (size_t)n_dg);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t h = 0; h < H; ++h) {
+    double* dg = (double*)calloc((size_t)(gate_st ? T * 2 : 2), sizeof(double));
+    s3r_oracle_backward_head(T, H, D, B, scale, q, qst, qsh, k, kst, ksh, v, vst, vsh, gates,
+                             gate_st, dout, dst, dsh, sel + (int64_t)h * Nb * nsel, nsel, h, dq,
+                             dk, dv, dg);
+    if (gate_st) {
+      for (int64_t t = 0; t < T; ++t) {
+        dgates[(t * H + h) * 2 + 0] = dg[t * 2 + 0];
+        dgates[(t * H + h) * 2 + 1] = dg[t * 2 + 1];
+      }
+    } else {
+      dgates[h * 2 + 0] = dg[0];
+      dgates[h * 2 + 1] = dg[1];
+    }
+    free(dg);
+  }
+}
+

@@ -401,3 +401,101 @@ def test_window_forward_is_the_plain_forward_on_reordered_tokens():
     gd = g.double().numpy()
     np.testing.assert_allclose(d["out"], gd[..., :1] * d["ocmp"] + gd[..., 1:] * d["osel"],
                                atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- backward
+def _out_with_sel(q, k, v, g, B, sel):
+    """out [T, H, D] of the forward pass with the selection held fixed (oracle forward)."""
+    T, H, D = q.shape
+    Nb = -(-T // B)
+    r = O.forward_rows(q, k, v, g, B, sel.shape[-1], np.repeat(np.arange(H), Nb),
+                       np.tile(np.arange(Nb), H), sel_in=sel.reshape(H * Nb, -1))
+    return r["out"].reshape(H, Nb * B, D)[:, :T].transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("token_gates", [False, True])
+def test_backward_matches_finite_differences(token_gates):
+    """Central differences of the oracle's own forward (selection fixed, since top-k is
+    piecewise constant) against the backward, for every element of q, k, v and the gates.
+    Small width D = 8 and a ragged last block; steps of 2^-12 on bf16-valued inputs are exact
+    in float32. Catches any dropped term, sign or index slip of the chain rule."""
+    T, H, D, B, kk = 22, 2, 8, 4, 2
+    q, k, v = (bf16_tensor((T, H, D), 60 + i, 0.7).float().numpy() for i in range(3))
+    gshape = (T, H, 2) if token_gates else (H, 2)
+    g = torch.rand(gshape, generator=torch.Generator().manual_seed(64)).to(torch.bfloat16)
+    g = g.float().numpy()
+    W = bf16_tensor((T, H, D), 65).double().numpy()
+    sel = O.forward_all(q, k, v, g, B, kk)["sel"]
+    grads = O.backward(q, k, v, g, W, B, sel)
+    step = 2.0 ** -12
+
+    def loss(qq, kk_, vv, gg):
+        return float((_out_with_sel(qq, kk_, vv, gg, B, sel) * W).sum())
+
+    args = [q, k, v, g]
+    for which, name in enumerate(("dq", "dk", "dv", "dgates")):
+        x = args[which]
+        fd = np.empty(x.shape)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + step
+            up = loss(*args)
+            x[idx] = old - step
+            dn = loss(*args)
+            x[idx] = old
+            fd[idx] = (up - dn) / (2 * step)
+        np.testing.assert_allclose(grads[name], fd, rtol=1e-5, atol=1e-6, err_msg=name)
+
+
+def _sdpa_grads(q, k, v, dout, scale):
+    """Dense attention gradients by torch autograd in float64 (a library routine)."""
+    qh, kh, vh = (torch.from_numpy(np.ascontiguousarray(x)).double().permute(1, 0, 2)
+                  .requires_grad_() for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qh[None], kh[None], vh[None], scale=scale)[0]
+    o.backward(torch.from_numpy(np.ascontiguousarray(dout)).double().permute(1, 0, 2))
+    return [t.grad.permute(1, 0, 2).numpy() for t in (qh, kh, vh)], o.detach().permute(1, 0, 2)
+
+
+def test_backward_special_cases_are_dense_attention_backward():
+    """B = 1 with gates (1, 0): the compression branch is dense attention over all tokens;
+    k = all blocks with gates (0, 1): so is the selection branch. Both gradients must equal
+    torch's float64 SDPA backward, and the gate gradients are dout . O_branch."""
+    T, H, D = 40, 2, 64
+    q, k, v = (bf16_tensor((T, H, D), 70 + i, 0.8).float().numpy() for i in range(3))
+    dout = bf16_tensor((T, H, D), 73).float().numpy()
+    (gq, gk, gv), o = _sdpa_grads(q, k, v, dout, 1 / 8)
+    g10 = np.tile(np.array([[1.0, 0.0]], np.float32), (H, 1))
+    sel = O.forward_all(q, k, v, g10, 1, 3)["sel"]
+    r = O.backward(q, k, v, g10, dout, 1, sel)
+    for name, ref in (("dq", gq), ("dk", gk), ("dv", gv)):
+        np.testing.assert_allclose(r[name], ref, atol=1e-11, err_msg=f"B=1 {name}")
+    np.testing.assert_allclose(r["dgates"][:, 0], (dout * o.numpy()).sum(axis=(0, 2)),
+                               atol=1e-11)
+    g01 = np.tile(np.array([[0.0, 1.0]], np.float32), (H, 1))
+    B = 16
+    sel = O.forward_all(q, k, v, g01, B, 10)["sel"]     # k = all 3 blocks
+    r = O.backward(q, k, v, g01, dout, B, sel)
+    for name, ref in (("dq", gq), ("dk", gk), ("dv", gv)):
+        np.testing.assert_allclose(r[name], ref, atol=1e-11, err_msg=f"k=all {name}")
+    np.testing.assert_allclose(r["dgates"][:, 1], (dout * o.numpy()).sum(axis=(0, 2)),
+                               atol=1e-11)
+
+
+def test_backward_invariants():
+    """Shifting every key by one vector leaves every softmax unchanged, so sum_t dk_t = 0 per
+    head; the attention weights sum to one, so sum_t dv_t = sum_t (g0 + g1) dout_t."""
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=300)
+    dout = bf16_tensor((300, w.H, 64), 80)
+    f = O.forward_all(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk)
+    r = O.backward(x["q"], x["k"], x["v"], x["gates"], dout, w.block, f["sel"])
+    np.testing.assert_allclose(r["dk"].sum(axis=0), 0.0, atol=1e-10)
+    gsum = x["gates"].double().numpy().sum(axis=1)[None, :, None]
+    np.testing.assert_allclose(r["dv"].sum(axis=0), (gsum * dout.double().numpy()).sum(axis=0),
+                               atol=1e-10)
+    # per-token gates: dgates[t, h] = (dout_t . O_cmp_t, dout_t . O_sel_t)
+    gt = torch.rand(300, w.H, 2, generator=torch.Generator().manual_seed(81))
+    rt = O.backward(x["q"], x["k"], x["v"], gt, dout, w.block, f["sel"])
+    d = dout.double().numpy()
+    np.testing.assert_allclose(rt["dgates"][..., 0], (d * f["ocmp"]).sum(-1), atol=1e-11)
+    np.testing.assert_allclose(rt["dgates"][..., 1], (d * f["osel"]).sum(-1), atol=1e-11)
