@@ -179,6 +179,47 @@ s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Training: forward pass that keeps what the backward pass needs, and the backward pass.
+ * The model is trained end to end (arXiv abstract; README "Overview"). Gradients flow
+ * through both branches and the gates with the forward pass's selection held fixed: top-k is
+ * piecewise constant, so the block scores receive no gradient.
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of the training workspace: speed3r_workspace_size plus the block means, O_sel
+ * [T][H][64] f32 and the selection log-sum-exp [H][T] f32. 0 if p is invalid. */
+size_t speed3r_train_workspace_size(const s3r_params* p);
+
+/* speed3r_sparse_attn_fwd that leaves, in `workspace` (speed3r_train_workspace_size bytes),
+ * everything speed3r_sparse_attn_bwd reads: the packed tiles, both log-sum-exps, O_cmp, O_sel,
+ * the block means and the selection (also copied to sel_idx when it is not NULL). */
+s3r_status speed3r_sparse_attn_fwd_train(const s3r_params* p, const void* q, const void* k,
+                                         const void* v, const float* gates, void* out,
+                                         int32_t* sel_idx, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of scratch speed3r_sparse_attn_bwd needs: operand tiles of q, dout, k, v and the
+ * block means, per-token scalars, the pooled gradients, a [H][Nb][ceil(Nb/32)] selection
+ * bitmap and per-token gate gradients (about 19 GB at T = 1,374,000, H = 16, B = 64). */
+size_t speed3r_bwd_workspace_size(const s3r_params* p);
+
+/* Gradients of the sparse forward pass. q, k, v, gates and p must be those of the
+ * speed3r_sparse_attn_fwd_train call whose workspace is `train_workspace` (read only).
+ *   dout     bf16 [T][H][64], the gradient of out; element strides multiples of 8.
+ *   dq, dk, dv   f32 [T][H][64], contiguous; overwritten.
+ *   dgates   f32 with the layout of gates ([H][2], or gate(t, h, b) at t * gate_stride_t +
+ *            h * 2 + b for per-token gates); overwritten.
+ * Every output element is written by one thread in a fixed order: results are bitwise
+ * repeatable. Numerics: the recomputed logits use the same bf16 operands as the forward
+ * pass (pooled keys as hi + lo), probabilities use the saved log-sum-exps, the pooled values
+ * and the products feeding dq, dk, dv take bf16 operands with f32 accumulation. */
+s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const void* k,
+                                   const void* v, const float* gates, const void* dout,
+                                   int64_t dout_stride_t, int64_t dout_stride_h,
+                                   const void* train_workspace, size_t train_workspace_bytes,
+                                   float* dq, float* dk, float* dv, float* dgates,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * 2-D pooling windows. The compression branch pools by spatial downsampling of the patch grid
  * (summary "Methodologie" 1) and the model takes image sides in multiples of 56 pixels, i.e.
  * patch grids in multiples of 4 patches (README "Notice" 1). With contiguous blocks that is

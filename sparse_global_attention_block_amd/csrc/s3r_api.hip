@@ -145,6 +145,91 @@ s3r_status run_cmp_fused(const Dims& d, CmpArgs a, hipStream_t stream) {
   return hip_status(launch_cmp_fused(a, stream));
 }
 
+// Regions the training forward pass adds after the forward workspace: what the backward
+// pass needs beyond it (block means, O_sel and the selection log-sum-exp).
+struct TrainLayout {
+  size_t k_mean, v_mean, o_sel, lse_sel, end;
+};
+
+TrainLayout train_layout(const Dims& d) {
+  TrainLayout T;
+  size_t off = layout(d).end;
+  const size_t pooled = align256((size_t)d.H * d.Nb * kD * sizeof(float));
+  T.k_mean = off; off += pooled;
+  T.v_mean = off; off += pooled;
+  T.o_sel = off; off += align256((size_t)d.T * d.H * kD * sizeof(float));
+  T.lse_sel = off; off += align256((size_t)d.H * d.T * sizeof(float));
+  T.end = off;
+  return T;
+}
+
+// Backward workspace: operand tiles, per-token scalars, pooled gradients, selection bitmap
+// and the per-token gate gradients (reduced per head when the gates are per head).
+struct BwdLayout {
+  size_t qtiles, raw_bwd, pooled_bwd, qs, dkc, dvc, bitmap, dg_tok, end;
+  int64_t bm_words;
+};
+
+BwdLayout bwd_layout(const Dims& d) {
+  BwdLayout B;
+  size_t off = 0;
+  B.bm_words = (d.Nb + 31) / 32;
+  B.qtiles = off; off += align256((size_t)d.H * d.n_ktiles * kQTileBytes);
+  B.raw_bwd = off; off += align256((size_t)d.H * d.n_ktiles * kBwdTileBytes);
+  B.pooled_bwd = off; off += align256((size_t)d.H * d.n_ctiles * kBwdTileBytes);
+  B.qs = off; off += align256((size_t)d.H * d.T * 8 * sizeof(float));
+  B.dkc = off; off += align256((size_t)d.H * d.Nb * kD * sizeof(float));
+  B.dvc = off; off += align256((size_t)d.H * d.Nb * kD * sizeof(float));
+  B.bitmap = off; off += align256((size_t)d.H * d.Nb * B.bm_words * sizeof(uint32_t));
+  B.dg_tok = off; off += align256((size_t)d.T * d.H * 2 * sizeof(float));
+  B.end = off;
+  return B;
+}
+
+// The forward pass on a validated problem. With `train`, the pooling also writes the block
+// means, the selection kernel writes O_sel and its log-sum-exp, and the selection stays in
+// the workspace.
+s3r_status run_forward(const s3r_params* p, const Dims& d, const Layout& L, const void* q,
+                       const void* k, const void* v, const float* gates, void* out,
+                       int32_t* sel_idx, unsigned char* ws, const TrainLayout* train,
+                       hipStream_t stream) {
+  s3r_status st;
+  float* lse = (float*)(ws + L.lse);
+  float* o_cmp = (float*)(ws + L.o_cmp);
+  float* score = (float*)(ws + L.score);
+  int32_t* sel = sel_idx ? sel_idx : (int32_t*)(ws + L.sel);
+  float* k_mean = train ? (float*)(ws + train->k_mean) : nullptr;
+  float* v_mean = train ? (float*)(ws + train->v_mean) : nullptr;
+  if ((st = hip_status(launch_pool(pool_args(p, d, k, v, ws, L, k_mean, v_mean), stream))) !=
+      S3R_OK)
+    return st;
+  if ((st = hip_status(launch_pack(pack_args(p, d, k, v, ws + L.raw), stream))) != S3R_OK)
+    return st;
+  CmpArgs c = cmp_args(p, d, q, ws, L);
+  c.lse = lse;
+  if ((st = hip_status(launch_cmp_lse(c, stream))) != S3R_OK) return st;
+  c.lse_in = lse;
+  c.o_cmp = o_cmp;
+  if (d.fold_topk) {
+    c.sel = sel;
+    c.n_sel = (int32_t)d.k_eff;
+    c.forced = (int32_t)d.forced;
+    if ((st = hip_status(launch_cmp_fused_topk(c, stream))) != S3R_OK) return st;
+  } else {
+    c.score = score;
+    if ((st = run_cmp_fused(d, c, stream)) != S3R_OK) return st;
+    TopkArgs t;
+    t.score = score; t.ld = d.ld; t.Nb = d.Nb; t.n_rows = (int64_t)d.H * d.Nb;
+    t.n_sel = (int32_t)d.k_eff; t.forced = (int32_t)d.forced; t.sel = sel;
+    if ((st = hip_status(launch_topk(t, stream))) != S3R_OK) return st;
+  }
+  AttnArgs a = attn_args(p, d, q, ws + L.raw);
+  a.sel = sel; a.o_cmp = o_cmp; a.gates = gates; a.out = (uint16_t*)out;
+  a.o_sel = train ? (float*)(ws + train->o_sel) : nullptr;
+  a.lse_sel = train ? (float*)(ws + train->lse_sel) : nullptr;
+  return hip_status(launch_sel(a, stream));
+}
+
 // ---------------------------------------------------------------------------------------
 // 2-D windows: layout checks and the workspace of the windowed forward pass
 // ---------------------------------------------------------------------------------------
@@ -354,38 +439,129 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
     return S3R_ERR_INVALID_ARG;
   const Layout L = layout(d);
   if ((st = check_ws(workspace, workspace_bytes, L.end)) != S3R_OK) return st;
-  unsigned char* ws = (unsigned char*)workspace;
-  float* lse = (float*)(ws + L.lse);
-  float* o_cmp = (float*)(ws + L.o_cmp);
-  float* score = (float*)(ws + L.score);
-  int32_t* sel = sel_idx ? sel_idx : (int32_t*)(ws + L.sel);
+  return run_forward(p, d, L, q, k, v, gates, out, sel_idx, (unsigned char*)workspace, nullptr,
+                     stream);
+}
 
-  if ((st = hip_status(launch_pool(pool_args(p, d, k, v, ws, L, nullptr, nullptr), stream))) !=
-      S3R_OK)
+size_t speed3r_train_workspace_size(const s3r_params* p) {
+  Dims d;
+  return check_params(p, &d) == S3R_OK ? train_layout(d).end : 0;
+}
+
+s3r_status speed3r_sparse_attn_fwd_train(const s3r_params* p, const void* q, const void* k,
+                                         const void* v, const float* gates, void* out,
+                                         int32_t* sel_idx, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !out ||
+      !aligned(out, 8) || (sel_idx && !aligned(sel_idx, 4)))
+    return S3R_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  const TrainLayout TL = train_layout(d);
+  if ((st = check_ws(workspace, workspace_bytes, TL.end)) != S3R_OK) return st;
+  unsigned char* ws = (unsigned char*)workspace;
+  if ((st = run_forward(p, d, L, q, k, v, gates, out, nullptr, ws, &TL, stream)) != S3R_OK)
     return st;
-  if ((st = hip_status(launch_pack(pack_args(p, d, k, v, ws + L.raw), stream))) != S3R_OK)
+  if (sel_idx)
+    return hip_status(hipMemcpyAsync(sel_idx, ws + L.sel,
+                                     (size_t)d.H * d.Nb * d.k_eff * sizeof(int32_t),
+                                     hipMemcpyDeviceToDevice, stream));
+  return S3R_OK;
+}
+
+size_t speed3r_bwd_workspace_size(const s3r_params* p) {
+  Dims d;
+  return check_params(p, &d) == S3R_OK ? bwd_layout(d).end : 0;
+}
+
+s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const void* k,
+                                   const void* v, const float* gates, const void* dout,
+                                   int64_t dout_stride_t, int64_t dout_stride_h,
+                                   const void* train_workspace, size_t train_workspace_bytes,
+                                   float* dq, float* dk, float* dv, float* dgates,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !tok_ok(dout) ||
+      !valid_stride(dout_stride_t) || !valid_stride(dout_stride_h) || !dq || !aligned(dq, 16) ||
+      !dk || !aligned(dk, 16) || !dv || !aligned(dv, 16) || !dgates || !aligned(dgates, 4))
+    return S3R_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  const TrainLayout TL = train_layout(d);
+  const BwdLayout BL = bwd_layout(d);
+  if ((st = check_ws(train_workspace, train_workspace_bytes, TL.end)) != S3R_OK) return st;
+  if ((st = check_ws(workspace, workspace_bytes, BL.end)) != S3R_OK) return st;
+  const unsigned char* tw = (const unsigned char*)train_workspace;
+  unsigned char* ws = (unsigned char*)workspace;
+
+  // operand images of q, dout (query tiles), v, k (raw) and the block means (pooled)
+  RecPackArgs r;
+  r.H = d.H;
+  auto pack = [&](const void* src, int64_t st_, int64_t sh_, int64_t rows, int64_t n_tiles,
+                  unsigned char* dst, int64_t tile_bytes, int r_off, int tr_off, int kind) {
+    r.src = src; r.st = st_; r.sh = sh_; r.rows = rows; r.n_tiles = n_tiles; r.dst = dst;
+    r.tile_bytes = tile_bytes; r.r_off = r_off; r.tr_off = tr_off;
+    return hip_status(launch_rec_pack(r, kind, stream));
+  };
+  const int64_t nk = d.n_ktiles, nc = d.n_ctiles, Nb64 = d.Nb * kD;
+  if ((st = pack(q, p->q_stride_t, p->q_stride_h, d.T, nk, ws + BL.qtiles, kQTileBytes, 0, 4096,
+                 0)) != S3R_OK ||
+      (st = pack(dout, dout_stride_t, dout_stride_h, d.T, nk, ws + BL.qtiles, kQTileBytes, 8192,
+                 12288, 0)) != S3R_OK ||
+      (st = pack(v, p->v_stride_t, p->v_stride_h, d.T, nk, ws + BL.raw_bwd, kBwdTileBytes, 0, -1,
+                 0)) != S3R_OK ||
+      (st = pack(k, p->k_stride_t, p->k_stride_h, d.T, nk, ws + BL.raw_bwd, kBwdTileBytes, -1,
+                 4096, 0)) != S3R_OK ||
+      (st = pack(tw + TL.v_mean, kD, Nb64, d.Nb, nc, ws + BL.pooled_bwd, kBwdTileBytes, 0, -1,
+                 1)) != S3R_OK ||
+      (st = pack(tw + TL.k_mean, kD, Nb64, d.Nb, nc, ws + BL.pooled_bwd, kBwdTileBytes, -1, 4096,
+                 1)) != S3R_OK)
     return st;
-  CmpArgs c = cmp_args(p, d, q, ws, L);
-  c.lse = lse;
-  if ((st = hip_status(launch_cmp_lse(c, stream))) != S3R_OK) return st;
-  c.lse_in = lse;
-  c.o_cmp = o_cmp;
-  if (d.fold_topk) {
-    c.sel = sel;
-    c.n_sel = (int32_t)d.k_eff;
-    c.forced = (int32_t)d.forced;
-    if ((st = hip_status(launch_cmp_fused_topk(c, stream))) != S3R_OK) return st;
-  } else {
-    c.score = score;
-    if ((st = run_cmp_fused(d, c, stream)) != S3R_OK) return st;
-    TopkArgs t;
-    t.score = score; t.ld = d.ld; t.Nb = d.Nb; t.n_rows = (int64_t)d.H * d.Nb;
-    t.n_sel = (int32_t)d.k_eff; t.forced = (int32_t)d.forced; t.sel = sel;
-    if ((st = hip_status(launch_topk(t, stream))) != S3R_OK) return st;
-  }
-  AttnArgs a = attn_args(p, d, q, ws + L.raw);
-  a.sel = sel; a.o_cmp = o_cmp; a.gates = gates; a.o_sel = nullptr; a.out = (uint16_t*)out;
-  return hip_status(launch_sel(a, stream));
+
+  // per-token scalars and gate gradients
+  BwdScalarArgs sa;
+  sa.T = d.T; sa.H = d.H;
+  sa.lse_cmp = (const float*)(tw + L.lse);
+  sa.lse_sel = (const float*)(tw + TL.lse_sel);
+  sa.gates = gates; sa.gate_st = p->gate_stride_t;
+  sa.dout = (const uint16_t*)dout; sa.d_st = dout_stride_t; sa.d_sh = dout_stride_h;
+  sa.o_cmp = (const float*)(tw + L.o_cmp);
+  sa.o_sel = (const float*)(tw + TL.o_sel);
+  sa.qs = (float*)(ws + BL.qs);
+  const bool token_gates = p->gate_stride_t != 0;
+  sa.dg_tok = token_gates ? dgates : (float*)(ws + BL.dg_tok);
+  sa.dg_st = token_gates ? p->gate_stride_t : 2 * (int64_t)d.H;
+  if ((st = hip_status(launch_bwd_scalars(sa, stream))) != S3R_OK) return st;
+  if (!token_gates &&
+      (st = hip_status(launch_gate_reduce(sa.dg_tok, d.T, d.H, dgates, stream))) != S3R_OK)
+    return st;
+
+  BwdArgs b;
+  memset(&b, 0, sizeof(b));
+  b.T = d.T; b.Nb = d.Nb; b.n_ctiles = nc; b.n_ktiles = nk; b.H = d.H; b.B = d.B;
+  b.scale = d.scale; b.logit_mult = d.scale * kLog2e;
+  b.pooled = tw + L.pooled; b.pooled_bwd = ws + BL.pooled_bwd;
+  b.raw = tw + L.raw; b.raw_bwd = ws + BL.raw_bwd;
+  b.qtiles = ws + BL.qtiles; b.qs = (const float*)(ws + BL.qs);
+  b.q = (const uint16_t*)q; b.q_st = p->q_stride_t; b.q_sh = p->q_stride_h;
+  b.dout = (const uint16_t*)dout; b.d_st = dout_stride_t; b.d_sh = dout_stride_h;
+  b.sel = (const int32_t*)(tw + L.sel); b.n_sel = (int32_t)d.k_eff;
+  b.bitmap = (const uint32_t*)(ws + BL.bitmap); b.bm_words = BL.bm_words;
+  b.dkc = (float*)(ws + BL.dkc); b.dvc = (float*)(ws + BL.dvc);
+  b.dq = dq; b.dk = dk; b.dv = dv;
+
+  // selection bitmap (cleared with a kernel, not a memset)
+  if ((st = hip_status(launch_fill_zero((float*)(ws + BL.bitmap),
+                                        (int64_t)d.H * d.Nb * BL.bm_words, stream))) != S3R_OK ||
+      (st = hip_status(launch_sel_bitmap(b, (uint32_t*)(ws + BL.bitmap), stream))) != S3R_OK)
+    return st;
+  if ((st = hip_status(launch_cmp_dq(b, stream))) != S3R_OK) return st;
+  if ((st = hip_status(launch_cmp_dkv(b, stream))) != S3R_OK) return st;
+  if ((st = hip_status(launch_sel_dq(b, stream))) != S3R_OK) return st;
+  return hip_status(launch_sel_dkv(b, stream));
 }
 
 s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void* k,

@@ -219,6 +219,9 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     const int64_t t = q0 + 16 * nt + li;
     if (t >= a.T || 16 * nt + li + 64 * part >= a.B) continue;
+    if (a.lse_sel && g == 0)  // saved for the backward pass
+      a.lse_sel[(int64_t)h * a.T + t] =
+          (f.l[nt][0] > 0.f) ? f.m[nt] + __log2f(f.l[nt][0]) : INFINITY;
     const float* gp = a.gates + t * a.gate_st + (int64_t)h * 2;
     const float g_cmp = gp[0], g_sel = gp[1];
 #pragma unroll

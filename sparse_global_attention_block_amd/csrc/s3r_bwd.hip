@@ -1,0 +1,830 @@
+// Backward pass of the dual-branch sparse attention (gradients of q, k, v and the gates).
+//
+// The model is trained end to end (arXiv abstract; README "Overview"). The selection is held
+// fixed: top-k is piecewise constant, so no gradient flows through the block scores. With
+// out_t = g0 O_cmp_t + g1 O_sel_t (summary "Methodologie" 2), each branch is a softmax
+// attention and the chain rule gives, per branch,
+//   P = softmax(logits), dP_tu = (g dout_t) . v_u, D_t = sum_u P_tu dP_tu = g dout_t . O_t,
+//   dS_tu = P_tu (dP_tu - D_t),  dq_t += scale sum_u dS_tu k_u,
+//   dk_u += scale sum_t dS_tu q_t,  dv_u += sum_t P_tu g dout_t,
+// with, for the compression branch, keys and values the block means Kc_j, Vc_j (whose
+// gradients are spread back as 1/n_j over the tokens of block j), and for the selection
+// branch the tokens of the selected blocks. The probabilities are recomputed from the
+// log-sum-exps the forward pass saved.
+//
+// Kernels (all deterministic: every output element is written by one wave, in a fixed order):
+//   rec_pack      operand images of q, dout (query tiles), v, k (raw) and the means (pooled)
+//   bwd_scalars   per (token, head): D_cmp, D_sel and the per-token gate gradients
+//   cmp_dq        compression dq, query-centric over all pooled tiles (S^T layout)
+//   cmp_dkv       compression dKc, dVc, key-centric over all query tiles (S layout)
+//   sel_dq        selection dq, query-centric over the selected blocks
+//   sel_dkv       selection dk, dv plus the spread-back pooled gradients, key-centric over the
+//                 query blocks that selected the key block (from a selection bitmap)
+#include "s3r_common.hpp"
+#include "s3r_launch.hpp"
+
+namespace s3r {
+
+// ---------------------------------------------------------------------------------------
+// Operand images. Thread (row m, dims 8*d8..+7) of a 256-thread work-group; the TR group is
+// assembled in LDS and written linearly.
+// ---------------------------------------------------------------------------------------
+template <int kKind>
+__global__ __launch_bounds__(256) void rec_pack_kernel(RecPackArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 stage[4 * kRecBytes / 2];
+  const int tid = threadIdx.x;
+  const int m = tid >> 3, d8 = tid & 7;
+  const int h = blockIdx.y;
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const int64_t row = tile * kTileKeys + m;
+    float x[8];
+    if (row < a.rows) {
+      if constexpr (kKind == 0) {
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const u16*>(a.src) + row * a.st + (int64_t)h * a.sh + d8 * 8);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __builtin_bit_cast(float, ws[e] << 16);
+          x[2 * e + 1] = __builtin_bit_cast(float, ws[e] & 0xFFFF0000u);
+        }
+      } else {
+        const float4* f = reinterpret_cast<const float4*>(
+            reinterpret_cast<const float*>(a.src) + row * a.st + (int64_t)h * a.sh + d8 * 8);
+        const float4 lo = f[0], hi = f[1];
+        x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+        x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    unsigned char* out = a.dst + ((int64_t)h * a.n_tiles + tile) * a.tile_bytes;
+    if (a.r_off >= 0) {
+      uint4 w;
+      w.x = bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
+      w.y = bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
+      w.z = bf16_bits(x[4]) | ((uint32_t)bf16_bits(x[5]) << 16);
+      w.w = bf16_bits(x[6]) | ((uint32_t)bf16_bits(x[7]) << 16);
+      *reinterpret_cast<uint4*>(out + a.r_off + k_chunk_offset(m, d8)) = w;
+    }
+    if (a.tr_off >= 0) {  // uniform over the work-group
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int rec, lane, slot;
+        vt_position(m, d8 * 8 + e, rec, lane, slot);
+        stage[(rec * 64 + lane) * 8 + slot] = bf16_bits(x[e]);
+      }
+      __syncthreads();
+      reinterpret_cast<uint4*>(out + a.tr_off)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_rec_pack(const RecPackArgs& a, int kind, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n_tiles < 2048 ? a.n_tiles : 2048), (unsigned)a.H);
+  if (kind == 0) hipLaunchKernelGGL((rec_pack_kernel<0>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((rec_pack_kernel<1>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Per (token, head) scalars: 8 lanes per pair, 8 dims each.
+//   qs = {L_cmp*log2(e), g0, g0 dout.O_cmp, L_sel (base 2), g1, g1 dout.O_sel, 0, 0}
+//   dg_tok[t][h] = {dout.O_cmp, dout.O_sel} (the gate gradients of token t)
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdScalarArgs a) {
+  const int sub = threadIdx.x & 7;
+  const int64_t n = a.T * a.H;
+  const int64_t stride = ((int64_t)gridDim.x * 256) >> 3;
+  for (int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3; idx < n; idx += stride) {
+    const int64_t t = idx / a.H;
+    const int h = (int)(idx - t * a.H);
+    const uint4 w = *reinterpret_cast<const uint4*>(a.dout + t * a.d_st + (int64_t)h * a.d_sh +
+                                                    sub * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const float4* oc = reinterpret_cast<const float4*>(a.o_cmp + idx * kD + sub * 8);
+    const float4* os = reinterpret_cast<const float4*>(a.o_sel + idx * kD + sub * 8);
+    const float4 c0 = oc[0], c1 = oc[1], s0 = os[0], s1 = os[1];
+    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float dc = 0.f, ds = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = __builtin_bit_cast(float, (e & 1) ? (ws[e >> 1] & 0xFFFF0000u)
+                                                       : (ws[e >> 1] << 16));
+      dc = fmaf(d, cv[e], dc);
+      ds = fmaf(d, sv[e], ds);
+    }
+#pragma unroll
+    for (int x = 1; x < 8; x <<= 1) {
+      dc += __shfl_xor(dc, x);
+      ds += __shfl_xor(ds, x);
+    }
+    if (sub == 0) {
+      const float g0 = a.gates[t * a.gate_st + (int64_t)h * 2];
+      const float g1 = a.gates[t * a.gate_st + (int64_t)h * 2 + 1];
+      float4* q = reinterpret_cast<float4*>(a.qs + ((int64_t)h * a.T + t) * 8);
+      q[0] = make_float4(a.lse_cmp[(int64_t)h * a.T + t] * kLog2e, g0, g0 * dc,
+                         a.lse_sel[(int64_t)h * a.T + t]);
+      q[1] = make_float4(g1, g1 * ds, 0.f, 0.f);
+      a.dg_tok[t * a.dg_st + (int64_t)h * 2] = dc;
+      a.dg_tok[t * a.dg_st + (int64_t)h * 2 + 1] = ds;
+    }
+  }
+}
+
+hipError_t launch_bwd_scalars(const BwdScalarArgs& a, hipStream_t s) {
+  const int64_t want = (a.T * a.H + 31) / 32;
+  hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(want < 16384 ? want : 16384)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Per-head gate gradients: sum over tokens in a fixed order (float64 partial sums).
+__global__ __launch_bounds__(256) void gate_reduce_kernel(const float* dg_tok, int64_t T,
+                                                          int32_t H, float* dgates) {
+  __shared__ double part[2][256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  double s0 = 0.0, s1 = 0.0;
+  for (int64_t t = tid; t < T; t += 256) {
+    s0 += dg_tok[(t * H + h) * 2];
+    s1 += dg_tok[(t * H + h) * 2 + 1];
+  }
+  part[0][tid] = s0;
+  part[1][tid] = s1;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      part[0][tid] += part[0][tid + w];
+      part[1][tid] += part[1][tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    dgates[h * 2] = (float)part[0][0];
+    dgates[h * 2 + 1] = (float)part[1][0];
+  }
+}
+
+hipError_t launch_gate_reduce(const float* dg_tok, int64_t T, int32_t H, float* dgates,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(gate_reduce_kernel, dim3((unsigned)H), dim3(256), 0, s, dg_tok, T, H,
+                     dgates);
+  return hipGetLastError();
+}
+
+// Bit i of bitmap row (h, u) <- query block i selected key block u (bitmap zeroed before).
+__global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* sel, int64_t Nb,
+                                                         int32_t n_sel, int64_t n, int64_t words,
+                                                         uint32_t* bm) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += stride) {
+    const int64_t row = idx / n_sel;  // h * Nb + i
+    const int64_t h = row / Nb, i = row - h * Nb;
+    const int64_t u = sel[idx];
+    if (u >= 0 && u < Nb) atomicOr(&bm[(h * Nb + u) * words + (i >> 5)], 1u << (i & 31));
+  }
+}
+
+hipError_t launch_sel_bitmap(const BwdArgs& a, uint32_t* bitmap, hipStream_t s) {
+  const int64_t n = (int64_t)a.H * a.Nb * a.n_sel;
+  const int64_t want = (n + 255) / 256;
+  hipLaunchKernelGGL(sel_bitmap_kernel, dim3((unsigned)(want < 65536 ? want : 65536)),
+                     dim3(256), 0, s, a.sel, a.Nb, a.n_sel, n, a.bm_words, bitmap);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Compression dq. A work-group of 4 waves owns 256 queries of one head (64 per wave, held as
+// B operands with their dout rows); the pooled tiles stream through a 2-slot LDS ring, 16 KB
+// per tile: [K hi][K lo] of the forward tile and [R(Vc)][TR(Kc)] of the backward tile.
+// Per tile: S^T (hi + lo, minus the saved log-sum-exp in the C operand), dP^T = Vc . dout^T,
+// dS = P (g0 dP - D) in registers, dq^T += Kc^T . dS^T.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cmp_dq_kernel(
+    BwdArgs a) {
+  constexpr int kStepU4 = 16 * kRecBytes / 16;  // 1024 uint4 per tile step
+  __shared__ uint4 lds[2][kStepU4];
+  const int64_t n_qtiles = (a.T + 255) / 256;
+  const int64_t total = (int64_t)a.H * n_qtiles;
+  const int64_t logical = xcd_logical_id(blockIdx.x, total);
+  if (logical >= total) return;
+  const int h = (int)(logical / n_qtiles);
+  const int64_t qt = logical % n_qtiles;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t q0 = qt * 256 + wave * 64;
+
+  bf16x8 qb[4][2], ob[4][2];
+  float g0[4], dl[4];
+  floatx4 cneg[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t t = q0 + 16 * nt + li;
+    const bool ok = t < a.T;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      qb[nt][c] = ok ? *reinterpret_cast<const bf16x8*>(a.q + t * a.q_st + (int64_t)h * a.q_sh +
+                                                        32 * c + 8 * g)
+                     : bf16x8{};
+      ob[nt][c] = ok ? *reinterpret_cast<const bf16x8*>(a.dout + t * a.d_st +
+                                                        (int64_t)h * a.d_sh + 32 * c + 8 * g)
+                     : bf16x8{};
+    }
+    float L = INFINITY;
+    g0[nt] = 0.f;
+    dl[nt] = 0.f;
+    if (ok) {
+      const float4 s = *reinterpret_cast<const float4*>(a.qs + ((int64_t)h * a.T + t) * 8);
+      L = s.x;
+      g0[nt] = s.y;
+      dl[nt] = s.z;
+    }
+    cneg[nt] = floatx4{-L, -L, -L, -L};
+  }
+  floatx4 dqa[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) dqa[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t n = a.n_ctiles;
+  const uint4* fwd = reinterpret_cast<const uint4*>(a.pooled) +
+                     (int64_t)h * n * (kPooledTileBytes / 16);
+  const uint4* bwd = reinterpret_cast<const uint4*>(a.pooled_bwd) +
+                     (int64_t)h * n * (kBwdTileBytes / 16);
+  uint4 s0, s1, s2, s3;
+  auto fetch = [&](int64_t t) {
+    const uint4* f = fwd + t * (kPooledTileBytes / 16);
+    const uint4* b = bwd + t * (kBwdTileBytes / 16);
+    s0 = f[tid];
+    s1 = f[256 + tid];
+    s2 = b[tid];
+    s3 = b[256 + tid];
+  };
+  auto stash = [&](int slot) {
+    lds[slot][tid] = s0;
+    lds[slot][256 + tid] = s1;
+    lds[slot][512 + tid] = s2;
+    lds[slot][768 + tid] = s3;
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int64_t tau = 0; tau < n; ++tau) {
+    fetch(tau + 1 < n ? tau + 1 : tau);
+    const uint4* L = lds[(int)(tau & 1)];
+    // one 16-key half at a time: its dS values wait in d0 until the second half completes the
+    // 32-key B operand of the dq product
+    float d0[4][4];
+#pragma unroll
+    for (int s2_ = 0; s2_ < 2; ++s2_) {
+      const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(&L[(2 * s2_) * 64 + lane]);
+      const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(&L[(2 * s2_ + 1) * 64 + lane]);
+      const bf16x8 l0 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2_) * 64 + lane]);
+      const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2_ + 1) * 64 + lane]);
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&L[512 + (2 * s2_) * 64 + lane]);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&L[512 + (2 * s2_ + 1) * 64 + lane]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        floatx4 x = mfma16(h0, qb[nt][0], cneg[nt]);
+        x = mfma16(h1, qb[nt][1], x);
+        x = mfma16(l0, qb[nt][0], x);
+        x = mfma16(l1, qb[nt][1], x);
+        floatx4 y = mfma16(v0, ob[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        y = mfma16(v1, ob[nt][1], y);
+        float d[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // keys past the last pooled token carry no probability
+          const bool live = tau * kTileKeys + 16 * s2_ + 4 * g + r < a.Nb;
+          d[r] = live ? fast_exp2(x[r]) * fmaf(g0[nt], y[r], -dl[nt]) : 0.f;
+        }
+        if (s2_ == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d0[nt][r] = d[r];
+        } else {
+          const bf16x8 pb = pack8(d0[nt][0], d0[nt][1], d0[nt][2], d0[nt][3], d[0], d[1], d[2],
+                                  d[3]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const bf16x8 kt = *reinterpret_cast<const bf16x8*>(&L[768 + mt * 64 + lane]);
+            dqa[mt][nt] = mfma16(kt, pb, dqa[mt][nt]);
+          }
+        }
+      }
+    }
+    stash((int)((tau + 1) & 1));
+    __syncthreads();
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t t = q0 + 16 * nt + li;
+    if (t >= a.T) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t base = (t * a.H + h) * kD + 16 * mt + 4 * g;
+      *reinterpret_cast<float4*>(a.dq + base) =
+          make_float4(a.scale * dqa[mt][nt][0], a.scale * dqa[mt][nt][1],
+                      a.scale * dqa[mt][nt][2], a.scale * dqa[mt][nt][3]);
+    }
+  }
+}
+
+hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H * ((a.T + 255) / 256);
+  hipLaunchKernelGGL(cmp_dq_kernel, dim3((unsigned)(((total + 7) / 8) * 8)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Compression dKc, dVc. A work-group of kWaves waves owns kWaves pooled tiles (32 pooled keys
+// per wave, held as B operands: K hi, K lo, Vc rows) and streams every query tile of the head
+// (16 KB + the 32 queries' scalars) through a 2-slot LDS ring. Per query tile: S (queries x
+// keys, so that P^T and dS^T come out with queries in the k-slots), dP = dout . Vc^T,
+// dVc += (g0 P)^T . dout, dKc += dS^T . q.
+// ---------------------------------------------------------------------------------------
+constexpr int kDkvWaves = 8;
+
+__global__ __launch_bounds__(64 * kDkvWaves) __attribute__((amdgpu_waves_per_eu(2))) void
+cmp_dkv_kernel(BwdArgs a) {
+  constexpr int kThreads = 64 * kDkvWaves;
+  constexpr int kQU4 = kQTileBytes / 16;  // 1024
+  constexpr int kSU4 = kTileKeys * 8 / 4;  // 64: 8 floats per query
+  __shared__ uint4 lds[2][kQU4 + kSU4];
+  const int64_t n_groups = (a.n_ctiles + kDkvWaves - 1) / kDkvWaves;
+  const int64_t total = (int64_t)a.H * n_groups;
+  const int64_t logical = xcd_logical_id(blockIdx.x, total);
+  if (logical >= total) return;
+  const int h = (int)(logical / n_groups);
+  const int64_t grp = logical % n_groups;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t ct = grp * kDkvWaves + wave;
+  const bool active = ct < a.n_ctiles;
+
+  bf16x8 kh[2][2], kl[2][2], vc[2][2];
+  {
+    const int64_t c = active ? ct : 0;
+    const bf16x8* P = reinterpret_cast<const bf16x8*>(
+        a.pooled + ((int64_t)h * a.n_ctiles + c) * kPooledTileBytes);
+    const bf16x8* PB = reinterpret_cast<const bf16x8*>(
+        a.pooled_bwd + ((int64_t)h * a.n_ctiles + c) * kBwdTileBytes);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        kh[s][c2] = P[(2 * s + c2) * 64 + lane];
+        kl[s][c2] = P[256 + (2 * s + c2) * 64 + lane];
+        vc[s][c2] = PB[(2 * s + c2) * 64 + lane];
+      }
+  }
+  floatx4 dV[2][4], dK[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      dV[s][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dK[s][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int64_t n = a.n_ktiles;  // query tiles
+  const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) + (int64_t)h * n * kQU4;
+  const float* qs = a.qs + (int64_t)h * a.T * 8;
+  uint4 r0, r1, r2;
+  auto fetch = [&](int64_t t) {
+    r0 = qtl[t * kQU4 + tid];
+    r1 = qtl[t * kQU4 + kThreads + tid];
+    if (tid < kSU4) {
+      const int64_t qi = t * kTileKeys + (tid >> 1);
+      r2 = (qi < a.T) ? reinterpret_cast<const uint4*>(qs + qi * 8)[tid & 1]
+           : ((tid & 1) ? make_uint4(0, 0, 0, 0)
+                        : make_uint4(__builtin_bit_cast(uint32_t, INFINITY), 0, 0,
+                                     __builtin_bit_cast(uint32_t, INFINITY)));
+    }
+  };
+  auto stash = [&](int slot) {
+    lds[slot][tid] = r0;
+    lds[slot][kThreads + tid] = r1;
+    if (tid < kSU4) lds[slot][kQU4 + tid] = r2;
+  };
+  static_assert(2 * kThreads == kQU4, "two loads per thread cover a query tile");
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int64_t tau = 0; tau < n; ++tau) {
+    fetch(tau + 1 < n ? tau + 1 : tau);
+    if (active) {
+      const uint4* L = lds[(int)(tau & 1)];
+      const float* S = reinterpret_cast<const float*>(L + kQU4);
+      float l2[2][4], g0[2][4], dl[2][4];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 v = *reinterpret_cast<const float4*>(S + (16 * qh + 4 * g + r) * 8);
+          l2[qh][r] = v.x;
+          g0[qh][r] = v.y;
+          dl[qh][r] = v.z;
+        }
+      float pg[2][2][4], dc[2][2][4];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const bf16x8 qa0 = *reinterpret_cast<const bf16x8*>(&L[(2 * qh) * 64 + lane]);
+        const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(&L[(2 * qh + 1) * 64 + lane]);
+        const bf16x8 oa0 = *reinterpret_cast<const bf16x8*>(&L[512 + (2 * qh) * 64 + lane]);
+        const bf16x8 oa1 = *reinterpret_cast<const bf16x8*>(&L[512 + (2 * qh + 1) * 64 + lane]);
+        const floatx4 cq = {-l2[qh][0], -l2[qh][1], -l2[qh][2], -l2[qh][3]};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          floatx4 x = mfma16(qa0, kh[s][0], cq);
+          x = mfma16(qa1, kh[s][1], x);
+          x = mfma16(qa0, kl[s][0], x);
+          x = mfma16(qa1, kl[s][1], x);
+          floatx4 y = mfma16(oa0, vc[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          y = mfma16(oa1, vc[s][1], y);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(x[r]);
+            pg[qh][s][r] = g0[qh][r] * p;
+            dc[qh][s][r] = p * fmaf(g0[qh][r], y[r], -dl[qh][r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 ap = pack8(pg[0][s][0], pg[0][s][1], pg[0][s][2], pg[0][s][3], pg[1][s][0],
+                                pg[1][s][1], pg[1][s][2], pg[1][s][3]);
+        const bf16x8 ac = pack8(dc[0][s][0], dc[0][s][1], dc[0][s][2], dc[0][s][3], dc[1][s][0],
+                                dc[1][s][1], dc[1][s][2], dc[1][s][3]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8 tro = *reinterpret_cast<const bf16x8*>(&L[768 + mt * 64 + lane]);
+          const bf16x8 trq = *reinterpret_cast<const bf16x8*>(&L[256 + mt * 64 + lane]);
+          dV[s][mt] = mfma16(ap, tro, dV[s][mt]);
+          dK[s][mt] = mfma16(ac, trq, dK[s][mt]);
+        }
+      }
+    }
+    stash((int)((tau + 1) & 1));
+    __syncthreads();
+  }
+  if (!active) return;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t j = ct * kTileKeys + 16 * s + 4 * g + r;
+      if (j >= a.Nb) continue;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int64_t o = ((int64_t)h * a.Nb + j) * kD + 16 * mt + li;
+        a.dkc[o] = a.scale * dK[s][mt][r];
+        a.dvc[o] = dV[s][mt][r];
+      }
+    }
+}
+
+hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H * ((a.n_ctiles + kDkvWaves - 1) / kDkvWaves);
+  hipLaunchKernelGGL(cmp_dkv_kernel, dim3((unsigned)(((total + 7) / 8) * 8)),
+                     dim3(64 * kDkvWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection dq: one wave per 32 queries of a query block (16 for B = 16), walking the block's
+// selection as the forward selection kernel does. For each selected tile: S^T = K . q^T, dP^T = V . dout^T (rows of v from
+// the backward raw tile), dS = P (g1 dP - D), dq^T += K^T . dS^T; added onto the compression
+// dq already in dq.
+// ---------------------------------------------------------------------------------------
+struct BwdSelIter {
+  int idx;
+  int64_t prev, tile, tile_end, blk_lo, blk_hi;
+};
+
+__device__ __forceinline__ bool bwd_next_block(const BwdArgs& a, const int32_t* row,
+                                               BwdSelIter& it) {
+  while (it.idx < a.n_sel) {
+    const int64_t j = row[it.idx++];
+    if (j < 0 || j >= a.Nb || j == it.prev) continue;
+    it.prev = j;
+    it.blk_lo = j * a.B;
+    it.blk_hi = (it.blk_lo + a.B < a.T) ? it.blk_lo + a.B : a.T;
+    it.tile = it.blk_lo / kTileKeys;
+    it.tile_end = (it.blk_hi - 1) / kTileKeys + 1;
+    return true;
+  }
+  return false;
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sel_dq_kernel(
+    BwdArgs a) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int parts = (a.B > 32) ? a.B / 32 : 1;  // 32 queries per wave
+  const int64_t n_items = (int64_t)a.H * a.Nb * parts;
+  const int64_t n_wg = (n_items + 3) / 4;
+  const int64_t wg = xcd_logical_id(blockIdx.x, n_wg);
+  const int64_t item = wg * 4 + wave;
+  if (wg >= n_wg || item >= n_items) return;
+  const int part = (int)(item % parts);
+  const int64_t hi_ = item / parts;
+  const int h = (int)(hi_ / a.Nb);
+  const int64_t i = hi_ % a.Nb;
+  const int64_t q0 = i * a.B + 32 * part;
+
+  bf16x8 qb[NT][2], ob[NT][2];
+  float l2[NT], g1[NT], dl[NT];
+  bool ok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t t = q0 + 16 * nt + li;
+    ok[nt] = t < a.T && 16 * nt + li + 32 * part < a.B;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      qb[nt][c] = ok[nt] ? *reinterpret_cast<const bf16x8*>(a.q + t * a.q_st +
+                                                            (int64_t)h * a.q_sh + 32 * c + 8 * g)
+                         : bf16x8{};
+      ob[nt][c] = ok[nt] ? *reinterpret_cast<const bf16x8*>(a.dout + t * a.d_st +
+                                                            (int64_t)h * a.d_sh + 32 * c + 8 * g)
+                         : bf16x8{};
+    }
+    l2[nt] = INFINITY;
+    g1[nt] = 0.f;
+    dl[nt] = 0.f;
+    if (ok[nt]) {
+      const float4 s = *reinterpret_cast<const float4*>(a.qs + ((int64_t)h * a.T + t) * 8);
+      const float4 s2 = *reinterpret_cast<const float4*>(a.qs + ((int64_t)h * a.T + t) * 8 + 4);
+      l2[nt] = s.w;
+      g1[nt] = s2.x;
+      dl[nt] = s2.y;
+    }
+  }
+  floatx4 dqa[4][NT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dqa[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* row = a.sel + ((int64_t)h * a.Nb + i) * a.n_sel;
+  const unsigned char* raw = a.raw + (int64_t)h * a.n_ktiles * kRawTileBytes;
+  const unsigned char* rawb = a.raw_bwd + (int64_t)h * a.n_ktiles * kBwdTileBytes;
+  BwdSelIter it{0, -1, 0, 0, 0, 0};
+  bool valid = bwd_next_block(a, row, it);
+  while (valid) {
+    const bf16x8* K = reinterpret_cast<const bf16x8*>(raw + it.tile * kRawTileBytes);
+    const bf16x8* RB = reinterpret_cast<const bf16x8*>(rawb + it.tile * kBwdTileBytes);
+    bf16x8 kr[4], vr[4], tk[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      kr[x] = K[x * 64 + lane];
+      vr[x] = RB[x * 64 + lane];
+      tk[x] = RB[256 + x * 64 + lane];
+    }
+    const int64_t t0 = it.tile * kTileKeys;
+    const int lo = (int)((it.blk_lo > t0) ? it.blk_lo - t0 : 0);
+    const int hi = (int)((it.blk_hi < t0 + kTileKeys) ? it.blk_hi - t0 : kTileKeys);
+    floatx4 acc[2][NT], dp[2][NT];
+#pragma unroll
+    for (int s2_ = 0; s2_ < 2; ++s2_)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const floatx4 x = mfma16(kr[2 * s2_], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[s2_][nt] = mfma16(kr[2 * s2_ + 1], qb[nt][1], x);
+        const floatx4 y = mfma16(vr[2 * s2_], ob[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        dp[s2_][nt] = mfma16(vr[2 * s2_ + 1], ob[nt][1], y);
+      }
+#pragma unroll
+    for (int s2_ = 0; s2_ < 2; ++s2_)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * s2_ + 4 * g + r;
+        if (key < lo || key >= hi) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[s2_][nt][r] = -INFINITY;
+        }
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float d[2][4];
+#pragma unroll
+      for (int s2_ = 0; s2_ < 2; ++s2_)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          d[s2_][r] = fast_exp2(fmaf(acc[s2_][nt][r], a.logit_mult, -l2[nt])) *
+                      fmaf(g1[nt], dp[s2_][nt][r], -dl[nt]);
+      const bf16x8 pb = pack8(d[0][0], d[0][1], d[0][2], d[0][3], d[1][0], d[1][1], d[1][2],
+                              d[1][3]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) dqa[mt][nt] = mfma16(tk[mt], pb, dqa[mt][nt]);
+    }
+    if (it.tile + 1 < it.tile_end) {
+      ++it.tile;
+    } else {
+      valid = bwd_next_block(a, row, it);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!ok[nt]) continue;
+    const int64_t t = q0 + 16 * nt + li;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float4* p = reinterpret_cast<float4*>(a.dq + (t * a.H + h) * kD + 16 * mt + 4 * g);
+      const float4 o = *p;
+      *p = make_float4(o.x + a.scale * dqa[mt][nt][0], o.y + a.scale * dqa[mt][nt][1],
+                       o.z + a.scale * dqa[mt][nt][2], o.w + a.scale * dqa[mt][nt][3]);
+    }
+  }
+}
+
+hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s) {
+  const int parts = (a.B > 32) ? a.B / 32 : 1;
+  const int64_t n_wg = ((int64_t)a.H * a.Nb * parts + 3) / 4;
+  const dim3 g3((unsigned)(((n_wg + 7) / 8) * 8)), b3(256);
+  if (a.B == 16) hipLaunchKernelGGL((sel_dq_kernel<1>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((sel_dq_kernel<2>), g3, b3, 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection dk, dv. One work-group of 4 waves per (head, key block u). The block's key tiles
+// (1, 2 or 4 of 32 keys) are spread over the waves; waves that share a tile split the query
+// blocks that selected u (read in ascending order from the bitmap row) by rank, and their
+// partial sums are added in LDS in a fixed order. Per selecting query tile: S = q . K^T,
+// dP = dout . V^T, dv += (g1 P)^T . dout, dk += dS^T . q. The epilogue adds the compression
+// branch's pooled gradients spread over the block, dKc_u / n_u and dVc_u / n_u, and writes dk,
+// dv for every token of the block.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sel_dkv_kernel(
+    BwdArgs a) {
+  __shared__ floatx4 red[3][16][64];
+  const int64_t total = (int64_t)a.H * a.Nb;
+  const int64_t logical = xcd_logical_id(blockIdx.x, total);
+  if (logical >= total) return;
+  const int h = (int)(logical / a.Nb);
+  const int64_t u = logical % a.Nb;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int kt_per = (a.B <= kTileKeys) ? 1 : a.B / kTileKeys;
+  const int nsplit = 4 / kt_per;
+  const int kt = wave % kt_per, split = wave / kt_per;
+  const int64_t k_lo = u * a.B;
+  const int64_t k_hi = (k_lo + a.B < a.T) ? k_lo + a.B : a.T;
+  const int64_t tile = k_lo / kTileKeys + kt;
+  const bool active = tile * kTileKeys < k_hi;
+
+  bf16x8 kr[2][2], vr[2][2];
+  {
+    const int64_t tt = active ? tile : k_lo / kTileKeys;
+    const bf16x8* K = reinterpret_cast<const bf16x8*>(
+        a.raw + ((int64_t)h * a.n_ktiles + tt) * kRawTileBytes);
+    const bf16x8* RB = reinterpret_cast<const bf16x8*>(
+        a.raw_bwd + ((int64_t)h * a.n_ktiles + tt) * kBwdTileBytes);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        kr[s][c] = K[(2 * s + c) * 64 + lane];
+        vr[s][c] = RB[(2 * s + c) * 64 + lane];
+      }
+  }
+  floatx4 dK[2][4], dV[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      dK[s][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dV[s][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) +
+                     (int64_t)h * a.n_ktiles * (kQTileBytes / 16);
+  const float* qs = a.qs + (int64_t)h * a.T * 8;
+  auto process = [&](int64_t i) {
+    const int64_t b_lo = i * a.B;
+    const int64_t b_hi = (b_lo + a.B < a.T) ? b_lo + a.B : a.T;
+    for (int64_t qt = b_lo / kTileKeys; qt * kTileKeys < b_hi; ++qt) {
+      const bf16x8* Q = reinterpret_cast<const bf16x8*>(qtl + qt * (kQTileBytes / 16));
+      float l2[2][4], g1[2][4], dl[2][4];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = qt * kTileKeys + 16 * qh + 4 * g + r;
+          l2[qh][r] = INFINITY;
+          g1[qh][r] = 0.f;
+          dl[qh][r] = 0.f;
+          if (t >= b_lo && t < b_hi) {
+            l2[qh][r] = qs[t * 8 + 3];
+            g1[qh][r] = qs[t * 8 + 4];
+            dl[qh][r] = qs[t * 8 + 5];
+          }
+        }
+      float pg[2][2][4], ds[2][2][4];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const bf16x8 qa0 = Q[(2 * qh) * 64 + lane];
+        const bf16x8 qa1 = Q[(2 * qh + 1) * 64 + lane];
+        const bf16x8 oa0 = Q[512 + (2 * qh) * 64 + lane];
+        const bf16x8 oa1 = Q[512 + (2 * qh + 1) * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          floatx4 x = mfma16(qa0, kr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          x = mfma16(qa1, kr[s][1], x);
+          floatx4 y = mfma16(oa0, vr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          y = mfma16(oa1, vr[s][1], y);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(x[r], a.logit_mult, -l2[qh][r]));
+            pg[qh][s][r] = g1[qh][r] * p;
+            ds[qh][s][r] = p * fmaf(g1[qh][r], y[r], -dl[qh][r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 ap = pack8(pg[0][s][0], pg[0][s][1], pg[0][s][2], pg[0][s][3], pg[1][s][0],
+                                pg[1][s][1], pg[1][s][2], pg[1][s][3]);
+        const bf16x8 as = pack8(ds[0][s][0], ds[0][s][1], ds[0][s][2], ds[0][s][3], ds[1][s][0],
+                                ds[1][s][1], ds[1][s][2], ds[1][s][3]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8 tro = Q[768 + mt * 64 + lane];
+          const bf16x8 trq = Q[256 + mt * 64 + lane];
+          dV[s][mt] = mfma16(ap, tro, dV[s][mt]);
+          dK[s][mt] = mfma16(as, trq, dK[s][mt]);
+        }
+      }
+    }
+  };
+
+  if (active) {
+    const uint32_t* bm = a.bitmap + ((int64_t)h * a.Nb + u) * a.bm_words;
+    int64_t rank = 0;
+    for (int64_t w = 0; w < a.bm_words; ++w) {
+      uint32_t bits = bm[w];
+      while (bits) {
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1;
+        if (rank++ % nsplit == split) process(w * 32 + b);
+      }
+    }
+  }
+  if (nsplit > 1) {  // add the partial sums of the waves that share a tile, in split order
+    if (split > 0) {
+      const int slot = (split - 1) * kt_per + kt;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          red[slot][s * 4 + mt][lane] = dK[s][mt];
+          red[slot][8 + s * 4 + mt][lane] = dV[s][mt];
+        }
+    }
+    __syncthreads();
+    if (split == 0) {
+      for (int sp = 1; sp < nsplit; ++sp) {
+        const int slot = (sp - 1) * kt_per + kt;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            dK[s][mt] += red[slot][s * 4 + mt][lane];
+            dV[s][mt] += red[slot][8 + s * 4 + mt][lane];
+          }
+      }
+    }
+  }
+  if (split != 0 || !active) return;
+  const float inv_n = 1.0f / (float)(k_hi - k_lo);
+  const float* dkc = a.dkc + ((int64_t)h * a.Nb + u) * kD;
+  const float* dvc = a.dvc + ((int64_t)h * a.Nb + u) * kD;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = tile * kTileKeys + 16 * s + 4 * g + r;
+      if (t < k_lo || t >= k_hi) continue;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int dim = 16 * mt + li;
+        const int64_t o = (t * a.H + h) * kD + dim;
+        a.dk[o] = a.scale * dK[s][mt][r] + dkc[dim] * inv_n;
+        a.dv[o] = dV[s][mt][r] + dvc[dim] * inv_n;
+      }
+    }
+}
+
+hipError_t launch_sel_dkv(const BwdArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H * a.Nb;
+  hipLaunchKernelGGL(sel_dkv_kernel, dim3((unsigned)(((total + 7) / 8) * 8)), dim3(256), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace s3r

@@ -63,6 +63,8 @@ struct AttnArgs {
   const float* o_cmp;
   const float* gates; int64_t gate_st;
   float* o_sel;            // optional
+  float* lse_sel;          // optional [H][T]: base-2 log-sum-exp of the selection softmax
+                           // in units of the scaled logit (scale*log2(e)*q.k); +inf if empty
   uint16_t* out;           // bf16 [T][H][64]
 };
 
@@ -102,6 +104,66 @@ struct WindowCopyArgs {
   unsigned char* dst;
   int64_t dst_st, dst_sh;
 };
+
+// ---- backward pass ----------------------------------------------------------------------
+// Operand-image record groups of 32 rows x 64 dims (4 KB each, bf16):
+//   R  (rows as lanes):  record (s, c), lane l -> row 16s + l%16, dims 32c + 8(l/16) + 0..7;
+//   TR (dims as lanes):  record mt, lane l -> dim 16mt + l%16, slot e -> row vkey(l/16, e).
+// Query tile (16 KB per 32 queries): [R(q)][TR(q)][R(dout)][TR(dout)].
+// Raw backward tile (8 KB per 32 keys): [R(v)][TR(k)].
+// Pooled backward tile (8 KB per 32 pooled keys): [R(Vc)][TR(Kc)], from the f32 means.
+constexpr int kQTileBytes = 16 * 1024;
+constexpr int kBwdTileBytes = 8 * 1024;
+
+struct RecPackArgs {
+  const void* src;         // bf16 (kind 0) or f32 (kind 1) rows
+  int64_t st, sh;          // element strides between rows / heads
+  int64_t rows, n_tiles;   // valid rows; tiles of 32 rows
+  int32_t H;
+  unsigned char* dst;      // tile base of head 0
+  int64_t tile_bytes;      // distance between consecutive tiles of one head
+  int32_t r_off, tr_off;   // byte offsets of the R and TR groups inside a tile (-1: skip)
+};
+
+struct BwdScalarArgs {
+  int64_t T; int32_t H;
+  const float* lse_cmp;    // [H][T], natural log
+  const float* lse_sel;    // [H][T], base 2 (selection kernel units)
+  const float* gates; int64_t gate_st;
+  const uint16_t* dout; int64_t d_st, d_sh;
+  const float* o_cmp; const float* o_sel;  // [T][H][64]
+  float* qs;               // [H][T][8]: L2c, g0, Dc, L2s, g1, Ds, 0, 0
+  float* dg_tok; int64_t dg_st;  // gradient of the gates, per token: dg_tok[t*dg_st + h*2 + b]
+};
+
+struct BwdArgs {
+  int64_t T, Nb, n_ctiles, n_ktiles;
+  int32_t H, B;
+  float scale;             // softmax scale
+  float logit_mult;        // scale * log2(e)
+  const unsigned char* pooled;      // forward pooled tiles (12 KB: K hi, K lo, V^T)
+  const unsigned char* pooled_bwd;  // [R(Vc)][TR(Kc)]
+  const unsigned char* raw;         // forward raw tiles (8 KB: K, V^T)
+  const unsigned char* raw_bwd;     // [R(v)][TR(k)]
+  const unsigned char* qtiles;      // query tiles
+  const float* qs;                  // per-query scalars
+  const uint16_t* q; int64_t q_st, q_sh;     // queries (resident operands of the dq kernels)
+  const uint16_t* dout; int64_t d_st, d_sh;
+  const int32_t* sel; int32_t n_sel;
+  const uint32_t* bitmap; int64_t bm_words;  // [H][Nb][bm_words]: bit i of row u = i selected u
+  float* dkc; float* dvc;           // [H][Nb][64]
+  float* dq; float* dk; float* dv;  // [T][H][64]
+};
+
+hipError_t launch_rec_pack(const RecPackArgs& a, int kind, hipStream_t s);
+hipError_t launch_bwd_scalars(const BwdScalarArgs& a, hipStream_t s);
+hipError_t launch_gate_reduce(const float* dg_tok, int64_t T, int32_t H, float* dgates,
+                              hipStream_t s);
+hipError_t launch_sel_bitmap(const BwdArgs& a, uint32_t* bitmap, hipStream_t s);
+hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s);
+hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s);
+hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s);
+hipError_t launch_sel_dkv(const BwdArgs& a, hipStream_t s);
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);

@@ -74,6 +74,15 @@ EXPORTS = {
                             [ctypes.c_void_p] * 6),
     "speed3r_dense_attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 5 +
                                [ctypes.c_size_t, ctypes.c_void_p]),
+    "speed3r_train_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "speed3r_sparse_attn_fwd_train": (ctypes.c_int, [ctypes.POINTER(Params)] +
+                                      [ctypes.c_void_p] * 6 +
+                                      [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "speed3r_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "speed3r_sparse_attn_bwd": (ctypes.c_int, [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 5 +
+                                [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_size_t] + [ctypes.c_void_p] * 5 +
+                                [ctypes.c_size_t, ctypes.c_void_p]),
     "speed3r_window_source": (ctypes.c_int64, [ctypes.POINTER(Windows), ctypes.c_int64]),
     "speed3r_window_permute": (ctypes.c_int, [ctypes.POINTER(Windows), ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
@@ -231,6 +240,58 @@ def dense_attn_fwd(q, k, v, scale: float = 0.0, out=None, workspace=None):
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream()))
     return out
+
+
+def train_workspace_size(p: Params) -> int:
+    return int(lib().speed3r_train_workspace_size(ctypes.byref(p)))
+
+
+def bwd_workspace_size(p: Params) -> int:
+    return int(lib().speed3r_bwd_workspace_size(ctypes.byref(p)))
+
+
+class Trained:
+    """State of a training forward pass: the output, the selection and the workspace the
+    backward pass reads."""
+
+    def __init__(self, p, q, k, v, gates, out, sel, workspace):
+        self.p, self.q, self.k, self.v, self.gates = p, q, k, v, gates
+        self.out, self.sel, self.workspace = out, sel, workspace
+
+
+def sparse_attn_fwd_train(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
+                          forced_blocks: int = 0, workspace: Optional[torch.Tensor] = None
+                          ) -> Trained:
+    """Forward pass that keeps the state speed3r_sparse_attn_bwd needs."""
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    sel = torch.empty(q.shape[1], num_blocks(p), num_selected(p), dtype=torch.int32,
+                      device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(train_workspace_size(p), q.device)
+    _check("speed3r_sparse_attn_fwd_train", lib().speed3r_sparse_attn_fwd_train(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(out), _ptr(sel),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return Trained(p, q, k, v, gates, out, sel, workspace)
+
+
+def sparse_attn_bwd(st: Trained, dout: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv f32 [T, H, 64], dgates f32 shaped like the gates) of the forward
+    pass recorded in `st`, for the output gradient dout (bf16 [T, H, 64])."""
+    if dout.dtype != torch.bfloat16 or tuple(dout.shape) != tuple(st.q.shape) or \
+            dout.stride(2) != 1:
+        raise ValueError("dout must be bf16 [T, H, 64] with a contiguous last dimension")
+    f32 = dict(dtype=torch.float32, device=st.q.device)
+    dq, dk, dv = (torch.empty(st.q.shape, **f32) for _ in range(3))
+    dg = torch.empty(st.gates.shape, **f32) if st.gates.dim() == 2 else \
+        torch.empty_strided(st.gates.shape, st.gates.stride(), **f32)
+    if workspace is None:
+        workspace = alloc_workspace(bwd_workspace_size(st.p), st.q.device)
+    _check("speed3r_sparse_attn_bwd", lib().speed3r_sparse_attn_bwd(
+        ctypes.byref(st.p), _ptr(st.q), _ptr(st.k), _ptr(st.v), _ptr(st.gates), _ptr(dout),
+        dout.stride(0), dout.stride(1), _ptr(st.workspace), st.workspace.numel(), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(dg), _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, dg
 
 
 def make_windows(layout) -> Windows:
