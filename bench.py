@@ -149,6 +149,43 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
         "out_mean_abs": err_sum / max(1, n)}
 
 
+def time_backward(w: W.Workload, x, reps: int):
+    """Times the training forward pass and the backward pass on the same inputs (HIP events
+    on the library's stream). Algorithmic flops of the backward: per (query, key) pair and
+    head, the compression and selection branches each recompute the logits (2D) and dP (2D)
+    and form dq, dk, dv (2D each): 10D per pair, over T*Nb pooled pairs and T*(k*B) selected
+    pairs."""
+    T, H, D = x["q"].shape
+    gen = torch.Generator(device=x["q"].device).manual_seed(29)
+    dout = torch.randn(T, H, D, device=x["q"].device, generator=gen).to(torch.bfloat16)
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced)
+    tws = S.alloc_workspace(S.train_workspace_size(p), x["q"].device)
+    bws = S.alloc_workspace(S.bwd_workspace_size(p), x["q"].device)
+    st = S.sparse_attn_fwd_train(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
+                                 forced_blocks=w.forced, workspace=tws)
+    S.sparse_attn_bwd(st, dout, workspace=bws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    f_ms = b_ms = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        st = S.sparse_attn_fwd_train(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
+                                     forced_blocks=w.forced, workspace=tws)
+        ev[1].record()
+        S.sparse_attn_bwd(st, dout, workspace=bws)
+        ev[2].record()
+        torch.cuda.synchronize()
+        f_ms += ev[0].elapsed_time(ev[1]) / reps
+        b_ms += ev[1].elapsed_time(ev[2]) / reps
+    Nb = -(-T // w.block)
+    sel_keys = w.k_eff * w.block
+    flops = 10 * D * T * H * (Nb + sel_keys)
+    del tws, bws, st
+    return {"ms": b_ms, "fwd_train_ms": f_ms, "flops": flops, "achieved": flops / (b_ms * 1e-3) / 1e12,
+            "unit": "TFLOP/s", "frac": flops / (b_ms * 1e-3) / PEAK_BF16,
+            "note": "algorithmic flops 10*D per (query, key) pair and head, pooled and selected pairs"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +194,7 @@ def main():
     ap.add_argument("--workload", default="v1000_k16", choices=sorted(W.WORKLOADS))
     ap.add_argument("--dense-reps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (the reference kernel "
@@ -271,6 +309,13 @@ def main():
     del st, xs
     torch.cuda.empty_cache()
 
+    backward = None
+    if not args.no_backward and not layout:
+        backward = time_backward(w, x, max(1, min(3, args.steps)))
+        log(f"[bench] training forward {backward['fwd_train_ms']:.1f} ms, backward "
+            f"{backward['ms']:.1f} ms ({backward['achieved']:.0f} TFLOP/s algorithmic)")
+        torch.cuda.empty_cache()
+
     dense = None
     if not args.no_dense:
         small = W.make_inputs(W.WORKLOADS["tiny"], device=dev)
@@ -303,6 +348,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "backward": backward,
         "dense": dense,
         "x_vs_dense": (dense["ms"] / ms) if dense else None,
         "parity_sampled": parity,

@@ -533,7 +533,8 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
   sa.qs = (float*)(ws + BL.qs);
   const bool token_gates = p->gate_stride_t != 0;
   sa.dg_tok = token_gates ? dgates : (float*)(ws + BL.dg_tok);
-  sa.dg_st = token_gates ? p->gate_stride_t : 2 * (int64_t)d.H;
+  sa.dg_st = token_gates ? p->gate_stride_t : 2;          // scratch: [H][T][2]
+  sa.dg_sh = token_gates ? 2 : 2 * d.T;
   if ((st = hip_status(launch_bwd_scalars(sa, stream))) != S3R_OK) return st;
   if (!token_gates &&
       (st = hip_status(launch_gate_reduce(sa.dg_tok, d.T, d.H, dgates, stream))) != S3R_OK)

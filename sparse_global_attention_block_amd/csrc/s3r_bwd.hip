@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdScalarArgs a) {
       q[0] = make_float4(a.lse_cmp[(int64_t)h * a.T + t] * kLog2e, g0, g0 * dc,
                          a.lse_sel[(int64_t)h * a.T + t]);
       q[1] = make_float4(g1, g1 * ds, 0.f, 0.f);
-      a.dg_tok[t * a.dg_st + (int64_t)h * 2] = dc;
-      a.dg_tok[t * a.dg_st + (int64_t)h * 2 + 1] = ds;
+      a.dg_tok[t * a.dg_st + (int64_t)h * a.dg_sh] = dc;
+      a.dg_tok[t * a.dg_st + (int64_t)h * a.dg_sh + 1] = ds;
     }
   }
 }
@@ -142,15 +142,18 @@ hipError_t launch_bwd_scalars(const BwdScalarArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Per-head gate gradients: sum over tokens in a fixed order (float64 partial sums).
+// Per-head gate gradients from [H][T][2] per-token values: sum over tokens in a fixed order
+// (float64 partial sums).
 __global__ __launch_bounds__(256) void gate_reduce_kernel(const float* dg_tok, int64_t T,
                                                           int32_t H, float* dgates) {
   __shared__ double part[2][256];
   const int h = blockIdx.x, tid = threadIdx.x;
+  const float2* src = reinterpret_cast<const float2*>(dg_tok) + (int64_t)h * T;
   double s0 = 0.0, s1 = 0.0;
   for (int64_t t = tid; t < T; t += 256) {
-    s0 += dg_tok[(t * H + h) * 2];
-    s1 += dg_tok[(t * H + h) * 2 + 1];
+    const float2 v = src[t];
+    s0 += v.x;
+    s1 += v.y;
   }
   part[0][tid] = s0;
   part[1][tid] = s1;
@@ -342,19 +345,23 @@ hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------------------
 // Compression dKc, dVc. A work-group of kWaves waves owns kWaves pooled tiles (32 pooled keys
 // per wave, held as B operands: K hi, K lo, Vc rows) and streams every query tile of the head
-// (16 KB + the 32 queries' scalars) through a 2-slot LDS ring. Per query tile: S (queries x
+// (its 8 KB of row images + the 32 queries' scalars) through a 2-slot LDS ring. Per query tile: S (queries x
 // keys, so that P^T and dS^T come out with queries in the k-slots), dP = dout . Vc^T,
 // dVc += (g0 P)^T . dout, dKc += dS^T . q.
 // ---------------------------------------------------------------------------------------
 constexpr int kDkvWaves = 8;
+constexpr int kDkvAhead = 1;  // query tiles in flight beyond the one being computed on
 
-__global__ __launch_bounds__(64 * kDkvWaves) __attribute__((amdgpu_waves_per_eu(2))) void
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
 cmp_dkv_kernel(BwdArgs a) {
-  constexpr int kThreads = 64 * kDkvWaves;
+  constexpr int kThreads = 64 * kWaves;
   constexpr int kQU4 = kQTileBytes / 16;  // 1024
   constexpr int kSU4 = kTileKeys * 8 / 4;  // 64: 8 floats per query
+  constexpr int kChunks = 512 / kThreads;  // 16-byte row chunks staged per thread
+  static_assert(kDkvAhead == 1 || kDkvAhead == 2, "one or two tiles in flight");
   __shared__ uint4 lds[2][kQU4 + kSU4];
-  const int64_t n_groups = (a.n_ctiles + kDkvWaves - 1) / kDkvWaves;
+  const int64_t n_groups = (a.n_ctiles + kWaves - 1) / kWaves;
   const int64_t total = (int64_t)a.H * n_groups;
   const int64_t logical = xcd_logical_id(blockIdx.x, total);
   if (logical >= total) return;
@@ -362,7 +369,7 @@ cmp_dkv_kernel(BwdArgs a) {
   const int64_t grp = logical % n_groups;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t ct = grp * kDkvWaves + wave;
+  const int64_t ct = grp * kWaves + wave;
   const bool active = ct < a.n_ctiles;
 
   bf16x8 kh[2][2], kl[2][2], vc[2][2];
@@ -393,29 +400,55 @@ cmp_dkv_kernel(BwdArgs a) {
   const int64_t n = a.n_ktiles;  // query tiles
   const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) + (int64_t)h * n * kQU4;
   const float* qs = a.qs + (int64_t)h * a.T * 8;
-  uint4 r0, r1, r2;
-  auto fetch = [&](int64_t t) {
-    r0 = qtl[t * kQU4 + tid];
-    r1 = qtl[t * kQU4 + kThreads + tid];
+  // Only the row images R(q), R(dout) (8 KB) are read; each thread scatters its 16-byte
+  // chunks into the transposed images TR(q), TR(dout) while staging, which halves the bytes
+  // streamed.
+  int rsrc[kChunks], tr_pos[kChunks][8];
+#pragma unroll
+  for (int x = 0; x < kChunks; ++x) {
+    const int c = tid + x * kThreads;                      // chunk 0..511
+    rsrc[x] = (c < 256) ? c : 512 + (c - 256);             // uint4 index of the chunk
+    const int trbase = (c < 256) ? 256 : 768;              // its TR group
+    const int rec = (c & 255) >> 6, lp = c & 63;
+    const int m = 16 * (rec >> 1) + (lp & 15), d0 = 32 * (rec & 1) + 8 * (lp >> 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int trec, tlane, tslot;
+      vt_position(m, d0 + j, trec, tlane, tslot);
+      tr_pos[x][j] = trbase * 8 + (trec * 64 + tlane) * 8 + tslot;  // in u16 units
+    }
+  }
+  // staging registers; with kDkvAhead = 2 two tiles are in flight and the loop is unrolled
+  // by two so that the buffers stay in named registers
+  uint4 r0[2][kChunks], r2[2];
+  auto fetch = [&](int b, int64_t t) {
+    t = t < n ? t : n - 1;  // past the end the last tile is re-read (and never used)
+#pragma unroll
+    for (int x = 0; x < kChunks; ++x) r0[b][x] = qtl[t * kQU4 + rsrc[x]];
     if (tid < kSU4) {
       const int64_t qi = t * kTileKeys + (tid >> 1);
-      r2 = (qi < a.T) ? reinterpret_cast<const uint4*>(qs + qi * 8)[tid & 1]
-           : ((tid & 1) ? make_uint4(0, 0, 0, 0)
-                        : make_uint4(__builtin_bit_cast(uint32_t, INFINITY), 0, 0,
-                                     __builtin_bit_cast(uint32_t, INFINITY)));
+      r2[b] = (qi < a.T) ? reinterpret_cast<const uint4*>(qs + qi * 8)[tid & 1]
+              : ((tid & 1) ? make_uint4(0, 0, 0, 0)
+                           : make_uint4(__builtin_bit_cast(uint32_t, INFINITY), 0, 0,
+                                        __builtin_bit_cast(uint32_t, INFINITY)));
     }
   };
-  auto stash = [&](int slot) {
-    lds[slot][tid] = r0;
-    lds[slot][kThreads + tid] = r1;
-    if (tid < kSU4) lds[slot][kQU4 + tid] = r2;
+  auto stash = [&](int b, int slot) {
+    u16* tr = reinterpret_cast<u16*>(lds[slot]);
+#pragma unroll
+    for (int x = 0; x < kChunks; ++x) {
+      lds[slot][rsrc[x]] = r0[b][x];
+      const uint32_t w[4] = {r0[b][x].x, r0[b][x].y, r0[b][x].z, r0[b][x].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        tr[tr_pos[x][j]] = (u16)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
+    }
+    if (tid < kSU4) lds[slot][kQU4 + tid] = r2[b];
   };
-  static_assert(2 * kThreads == kQU4, "two loads per thread cover a query tile");
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int64_t tau = 0; tau < n; ++tau) {
-    fetch(tau + 1 < n ? tau + 1 : tau);
+  auto body = [&](int64_t tau, int ld, int st) {
+    // load tile tau + kDkvAhead into buffer ld; compute on tile tau; stage tile tau + 1 from
+    // buffer st
+    fetch(ld, tau + kDkvAhead);
     if (active) {
       const uint4* L = lds[(int)(tau & 1)];
       const float* S = reinterpret_cast<const float*>(L + kQU4);
@@ -468,8 +501,20 @@ cmp_dkv_kernel(BwdArgs a) {
         }
       }
     }
-    stash((int)((tau + 1) & 1));
+    stash(st, (int)((tau + 1) & 1));
     __syncthreads();
+  };
+  fetch(0, 0);
+  stash(0, 0);
+  if constexpr (kDkvAhead == 2) fetch(0, 1);
+  __syncthreads();
+  if constexpr (kDkvAhead == 1) {
+    for (int64_t tau = 0; tau < n; ++tau) body(tau, 0, 0);
+  } else {
+    for (int64_t tau = 0; tau < n; tau += 2) {
+      body(tau, 1, 0);
+      if (tau + 1 < n) body(tau + 1, 0, 1);
+    }
   }
   if (!active) return;
 #pragma unroll
@@ -489,7 +534,7 @@ cmp_dkv_kernel(BwdArgs a) {
 
 hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.H * ((a.n_ctiles + kDkvWaves - 1) / kDkvWaves);
-  hipLaunchKernelGGL(cmp_dkv_kernel, dim3((unsigned)(((total + 7) / 8) * 8)),
+  hipLaunchKernelGGL((cmp_dkv_kernel<kDkvWaves>), dim3((unsigned)(((total + 7) / 8) * 8)),
                      dim3(64 * kDkvWaves), 0, s, a);
   return hipGetLastError();
 }

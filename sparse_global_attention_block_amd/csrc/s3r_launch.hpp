@@ -133,7 +133,7 @@ struct BwdScalarArgs {
   const uint16_t* dout; int64_t d_st, d_sh;
   const float* o_cmp; const float* o_sel;  // [T][H][64]
   float* qs;               // [H][T][8]: L2c, g0, Dc, L2s, g1, Ds, 0, 0
-  float* dg_tok; int64_t dg_st;  // gradient of the gates, per token: dg_tok[t*dg_st + h*2 + b]
+  float* dg_tok; int64_t dg_st, dg_sh;  // per-token gate gradients: dg_tok[t*dg_st + h*dg_sh + b]
 };
 
 struct BwdArgs {
