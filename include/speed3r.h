@@ -15,12 +15,14 @@
  *   gated aggregation    out_t = g[h][0] * O_cmp_t + g[h][1] * O_sel_t.
  *
  * Conventions shared by every entry point
- *   - Token tensors q, k, v are bf16 [T][H][D] with D = 64 contiguous; token and head strides
+ *   - Token tensors q, k, v are bf16 or fp16 (params.dtype) [T][H][D] with D = 64
+ *     contiguous, and out has their type; token and head strides
  *     are given in elements and must be multiples of 8 (16-byte rows); base pointers must be
  *     16-byte aligned. Query blocks and key blocks both have size B = params.block.
- *   - Numerics: logits are bf16 x bf16 products accumulated in f32 (the pooled keys as a
- *     bf16 hi + lo pair); softmax runs in f32 with base-2 exponentials; the P.V products take
- *     fp16 operands with f32 accumulation, so values of v must stay below 65504 in magnitude.
+ *   - Numerics: logits are products of the input type accumulated in f32 (the pooled keys as a
+ *     hi + lo pair of the input type); softmax runs in f32 with base-2 exponentials; the P.V
+ *     products take fp16 operands with f32 accumulation, so values of v must stay below 65504
+ *     in magnitude.
  *   - Every pointer is device memory owned by the caller; the library never allocates, frees
  *     or synchronises. All work is enqueued on `stream` (NULL = the default stream) and the
  *     call returns before it completes. Asynchronous faults surface at the caller's next
@@ -54,6 +56,9 @@ typedef enum {
   S3R_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } s3r_status;
 
+/* Element type of q, k, v and out. The model runs in bf16 or fp16 (README "Notice" 3). */
+typedef enum { S3R_BF16 = 0, S3R_FP16 = 1 } s3r_dtype;
+
 typedef struct {
   int64_t T;            /* number of tokens (all views concatenated), >= 1 */
   int32_t H;            /* number of heads, >= 1 */
@@ -70,6 +75,8 @@ typedef struct {
   int64_t v_stride_t, v_stride_h;
   int64_t gate_stride_t; /* 0: gates are [H][2]; otherwise per-token gates with
                             gate(t, h, b) = gates[t * gate_stride_t + h * 2 + b] */
+  int32_t dtype;        /* s3r_dtype of q, k, v and out; 0 (zero-initialised) is bf16 */
+  int32_t pad;          /* unused */
 } s3r_params;
 
 /* Human-readable name of a status code (static storage). */
@@ -105,7 +112,7 @@ size_t speed3r_dense_workspace_size(const s3r_params* p);
  * (speed3r_cmp_fused_topk); otherwise they go through the score matrix and speed3r_topk.
  *   gates    f32, [H][2] or per token (see gate_stride_t); column 0 multiplies the
  *            compression branch, column 1 the selection branch.
- *   out      bf16 [T][H][64], contiguous.
+ *   out      [T][H][64] of the input type, contiguous.
  *   sel_idx  optional int32 [H][Nb][n_sel] (speed3r_num_selected); NULL keeps it in the
  *            workspace.
  *   workspace / workspace_bytes: at least speed3r_workspace_size(p) bytes, 256-byte aligned.
@@ -128,7 +135,7 @@ s3r_status speed3r_pool(const s3r_params* p, const void* k, const void* v, void*
                         hipStream_t stream);
 
 /* Compression branch, first pass: lse[h][t] = log sum_j exp(scale * q_t . Kc_j) (natural log,
- * f32 [H][T]). The pooled keys enter as the sum of two bf16 terms (hi + lo) of
+ * f32 [H][T]). The pooled keys enter as the sum of two terms of the input type (hi + lo) of
  * Kc * scale * log2(e), accumulated in f32. */
 s3r_status speed3r_cmp_lse(const s3r_params* p, const void* q, const void* workspace,
                            size_t workspace_bytes, float* lse, hipStream_t stream);
@@ -162,7 +169,7 @@ s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_id
 
 /* Selection branch plus gated aggregation (summary "Methodologie" 1 selection branch and 2
  * gated aggregation): for every query of block i, softmax attention over the tokens of the
- * blocks sel_idx[h][i][0..k_eff), then out = g0 * o_cmp + g1 * O_sel rounded to bf16
+ * blocks sel_idx[h][i][0..k_eff), then out = g0 * o_cmp + g1 * O_sel rounded to the input type
  * [T][H][64]. Rows are read in order; an index outside [0, Nb) or equal to the previous index
  * of its row is skipped, so an ascending row (as speed3r_topk writes) attends to the union of
  * its blocks. o_sel (optional, f32 [T][H][64]) receives O_sel itself. */
@@ -172,7 +179,7 @@ s3r_status speed3r_sel_combine(const s3r_params* p, const void* q, const void* w
                                float* o_sel, hipStream_t stream);
 
 /* Dense global attention, the quadratic baseline the method replaces (summary
- * "Probleemstelling"): out = softmax(scale * q k^T) v over all T tokens per head, bf16
+ * "Probleemstelling"): out = softmax(scale * q k^T) v over all T tokens per head, input type
  * [T][H][64]. Workspace: speed3r_dense_workspace_size(p) bytes. */
 s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void* k,
                                   const void* v, void* out, void* workspace,
@@ -212,6 +219,7 @@ size_t speed3r_bwd_workspace_size(const s3r_params* p);
  * repeatable. Numerics: the recomputed logits use the same bf16 operands as the forward
  * pass (pooled keys as hi + lo), probabilities use the saved log-sum-exps, the pooled values
  * and the products feeding dq, dk, dv take bf16 operands with f32 accumulation. */
+/* fp16 inputs: S3R_ERR_UNSUPPORTED (the backward pass is built for bf16). */
 s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const void* k,
                                    const void* v, const float* gates, const void* dout,
                                    int64_t dout_stride_t, int64_t dout_stride_h,
@@ -242,7 +250,7 @@ typedef struct {
  * tokens (host function). -1 if w is invalid or pos is outside [0, T). */
 int64_t speed3r_window_source(const s3r_windows* w, int64_t pos);
 
-/* Reorders a bf16 [T][H][64] tensor into window order (inverse = 0: dst[pos] =
+/* Reorders a [T][H][64] tensor of 2-byte elements (bf16 or fp16) into window order (inverse = 0: dst[pos] =
  * src[source(pos)]) or back (inverse = 1: dst[source(pos)] = src[pos]), T = V * (S + grid).
  * Strides are in elements, multiples of 8; src and dst must not overlap. Byte-exact copy. */
 s3r_status speed3r_window_permute(const s3r_windows* w, int32_t H, const void* src,
@@ -257,7 +265,7 @@ size_t speed3r_windows_workspace_size(const s3r_params* p, const s3r_windows* w)
 
 /* The sparse forward pass with 2-D windows as blocks: reorders q, k, v (and per-token gates)
  * into window order inside the workspace, runs speed3r_sparse_attn_fwd on them, and writes
- * out (bf16 [T][H][64], contiguous) back in the caller's token order. sel_idx (optional,
+ * out ([T][H][64] of the input type, contiguous) back in the caller's token order. sel_idx (optional,
  * [H][Nb][n_sel]) and forced_blocks refer to blocks of the window order: forced blocks
  * 0..F-1 are the first view's first windows. Arguments are checked as for
  * speed3r_sparse_attn_fwd; on any error nothing is launched. */

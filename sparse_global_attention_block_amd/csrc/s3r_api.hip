@@ -20,6 +20,7 @@ struct Dims {
   int64_t k_eff;   // entries per selection row: forced prefix + chosen blocks (n_sel)
   int64_t forced;  // F' = min(forced_blocks, Nb)
   int32_t H, B;
+  int32_t half;    // q, k, v (and out) are fp16; else bf16
   float scale;
   bool fold_topk;  // selection folded into the compression pass (no score matrix)
 };
@@ -36,6 +37,7 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   if (!p) return S3R_ERR_INVALID_ARG;
   if (p->T < 1 || p->H < 1 || p->topk < 1 || p->forced_blocks < 0) return S3R_ERR_INVALID_ARG;
   if (p->block < 1 || p->D < 1) return S3R_ERR_INVALID_ARG;
+  if (p->dtype != S3R_BF16 && p->dtype != S3R_FP16) return S3R_ERR_INVALID_ARG;
   if (!(p->scale >= 0.f) || isinf(p->scale)) return S3R_ERR_INVALID_ARG;
   if (!valid_stride(p->q_stride_t) || !valid_stride(p->q_stride_h) ||
       !valid_stride(p->k_stride_t) || !valid_stride(p->k_stride_h) ||
@@ -47,6 +49,7 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   if (p->H > 65535 || p->T > ((int64_t)1 << 31) - 1) return S3R_ERR_UNSUPPORTED;
   d->T = p->T;
   d->H = p->H;
+  d->half = p->dtype == S3R_FP16;
   d->B = p->block;
   d->Nb = (p->T + p->block - 1) / p->block;
   d->n_ctiles = (d->Nb + kTileKeys - 1) / kTileKeys;
@@ -96,7 +99,7 @@ PoolArgs pool_args(const s3r_params* p, const Dims& d, const void* k, const void
   PoolArgs a;
   a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.k_st = p->k_stride_t; a.k_sh = p->k_stride_h; a.v_st = p->v_stride_t; a.v_sh = p->v_stride_h;
-  a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B;
+  a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.key_mult = d.scale * kLog2e;
   a.k_mean = k_mean; a.v_mean = v_mean;
   a.tiles = (unsigned char*)ws + L.pooled;
@@ -108,7 +111,7 @@ PackArgs pack_args(const s3r_params* p, const Dims& d, const void* k, const void
   PackArgs a;
   a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.k_st = p->k_stride_t; a.k_sh = p->k_stride_h; a.v_st = p->v_stride_t; a.v_sh = p->v_stride_h;
-  a.T = d.T; a.n_tiles = d.n_ktiles; a.H = d.H;
+  a.T = d.T; a.n_tiles = d.n_ktiles; a.H = d.H; a.half = d.half;
   a.tiles = tiles;
   return a;
 }
@@ -118,7 +121,7 @@ CmpArgs cmp_args(const s3r_params* p, const Dims& d, const void* q, const void* 
   CmpArgs a;
   memset(&a, 0, sizeof(a));
   a.q = (const uint16_t*)q; a.q_st = p->q_stride_t; a.q_sh = p->q_stride_h;
-  a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B;
+  a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.tiles = (const unsigned char*)ws + L.pooled;
   a.ld = d.ld;
   return a;
@@ -129,7 +132,7 @@ AttnArgs attn_args(const s3r_params* p, const Dims& d, const void* q,
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.q = (const uint16_t*)q; a.q_st = p->q_stride_t; a.q_sh = p->q_stride_h;
-  a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ktiles; a.H = d.H; a.B = d.B;
+  a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ktiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.logit_mult = d.scale * kLog2e;
   a.tiles = raw_tiles;
   a.k_eff = (int32_t)d.k_eff;
@@ -485,6 +488,7 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
   Dims d;
   s3r_status st = check_params(p, &d);
   if (st != S3R_OK) return st;
+  if (d.half) return S3R_ERR_UNSUPPORTED;
   if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !tok_ok(dout) ||
       !valid_stride(dout_stride_t) || !valid_stride(dout_stride_h) || !dq || !aligned(dq, 16) ||
       !dk || !aligned(dk, 16) || !dv || !aligned(dv, 16) || !dgates || !aligned(dgates, 4))

@@ -19,7 +19,7 @@ namespace s3r {
 
 constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the offset must move
 
-template <int NT>
+template <int NT, bool kHalf = false>
 struct Flash {
   float m[NT];          // per-query offset (base 2), identical in the 4 lanes of a query
   floatx4 l[NT];        // sum over keys of the bf16-rounded weights (all 4 entries equal)
@@ -46,8 +46,8 @@ struct Flash {
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        floatx4 x = mfma16(rec[2 * s2], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
-        acc[s2][nt] = mfma16(rec[2 * s2 + 1], qb[nt][1], x);
+        floatx4 x = mfma_in<kHalf>(rec[2 * s2], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[s2][nt] = mfma_in<kHalf>(rec[2 * s2 + 1], qb[nt][1], x);
       }
     if (lo > 0 || hi < kTileKeys) {
 #pragma unroll
@@ -169,7 +169,7 @@ __device__ __forceinline__ bool sel_advance(const AttnArgs& a, const int32_t* ro
   return sel_next_block(a, row, it);
 }
 
-template <int NT>
+template <int NT, bool kHalf>
 __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   const int32_t* row = a.sel + ((int64_t)h * a.Nb + i) * a.k_eff;
   const unsigned char* tiles = a.tiles + (int64_t)h * a.n_tiles * kRawTileBytes;
 
-  Flash<NT> f;
+  Flash<NT, kHalf> f;
   f.init();
   SelIter it{0, -1, 0, 0, 0, 0};
   bool valid = sel_next_block(a, row, it);
@@ -232,8 +232,10 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
       const float s2 = f.o[mt][nt][2] * inv[nt], s3 = f.o[mt][nt][3] * inv[nt];
       if (a.o_sel) *reinterpret_cast<float4*>(a.o_sel + base) = make_float4(s0, s1, s2, s3);
       uint2 w;
-      w.x = bf16_bits(g_cmp * oc.x + g_sel * s0) | ((uint32_t)bf16_bits(g_cmp * oc.y + g_sel * s1) << 16);
-      w.y = bf16_bits(g_cmp * oc.z + g_sel * s2) | ((uint32_t)bf16_bits(g_cmp * oc.w + g_sel * s3) << 16);
+      w.x = float_to_in<kHalf>(g_cmp * oc.x + g_sel * s0) |
+            ((uint32_t)float_to_in<kHalf>(g_cmp * oc.y + g_sel * s1) << 16);
+      w.y = float_to_in<kHalf>(g_cmp * oc.z + g_sel * s2) |
+            ((uint32_t)float_to_in<kHalf>(g_cmp * oc.w + g_sel * s3) << 16);
       *reinterpret_cast<uint2*>(a.out + base) = w;
     }
   }
@@ -243,6 +245,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
 // Dense attention. A work-group of 4 waves owns 256 queries of one head and streams every
 // raw tile of that head through a double-buffered LDS ring (8 KB per tile).
 // ---------------------------------------------------------------------------------------
+template <bool kHalf>
 __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
   constexpr int kTileU4 = kRawTileBytes / 16;  // 512
   __shared__ uint4 lds[2][kTileU4];
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
   load_q<4>(a, h, q0, g, li, qb);
   const uint4* tiles = reinterpret_cast<const uint4*>(a.tiles) + (int64_t)h * a.n_tiles * kTileU4;
 
-  Flash<4> f;
+  Flash<4, kHalf> f;
   f.init();
   uint4 s0 = tiles[tid], s1 = tiles[256 + tid];
   lds[0][tid] = s0;
@@ -295,8 +298,10 @@ __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
     for (int mt = 0; mt < 4; ++mt) {
       const int64_t base = (t * a.H + h) * kD + 16 * mt + 4 * g;
       uint2 w;
-      w.x = bf16_bits(f.o[mt][nt][0] * inv[nt]) | ((uint32_t)bf16_bits(f.o[mt][nt][1] * inv[nt]) << 16);
-      w.y = bf16_bits(f.o[mt][nt][2] * inv[nt]) | ((uint32_t)bf16_bits(f.o[mt][nt][3] * inv[nt]) << 16);
+      w.x = float_to_in<kHalf>(f.o[mt][nt][0] * inv[nt]) |
+            ((uint32_t)float_to_in<kHalf>(f.o[mt][nt][1] * inv[nt]) << 16);
+      w.y = float_to_in<kHalf>(f.o[mt][nt][2] * inv[nt]) |
+            ((uint32_t)float_to_in<kHalf>(f.o[mt][nt][3] * inv[nt]) << 16);
       *reinterpret_cast<uint2*>(a.out + base) = w;
     }
   }
@@ -308,16 +313,27 @@ hipError_t launch_sel(const AttnArgs& a, hipStream_t s) {
   const int64_t n_wg = (n_items + 3) / 4;
   const dim3 g3((unsigned)(((n_wg + 7) / 8) * 8)), b3(256);
   switch (a.B) {
-    case 16: hipLaunchKernelGGL((sel_kernel<1>), g3, b3, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((sel_kernel<2>), g3, b3, 0, s, a); break;
-    default: hipLaunchKernelGGL((sel_kernel<4>), g3, b3, 0, s, a); break;
+    case 16:
+      if (a.half) hipLaunchKernelGGL((sel_kernel<1, true>), g3, b3, 0, s, a);
+      else hipLaunchKernelGGL((sel_kernel<1, false>), g3, b3, 0, s, a);
+      break;
+    case 32:
+      if (a.half) hipLaunchKernelGGL((sel_kernel<2, true>), g3, b3, 0, s, a);
+      else hipLaunchKernelGGL((sel_kernel<2, false>), g3, b3, 0, s, a);
+      break;
+    default:
+      if (a.half) hipLaunchKernelGGL((sel_kernel<4, true>), g3, b3, 0, s, a);
+      else hipLaunchKernelGGL((sel_kernel<4, false>), g3, b3, 0, s, a);
+      break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_dense(const AttnArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.H * ((a.T + 255) / 256);
-  hipLaunchKernelGGL(dense_kernel, dim3((unsigned)(((total + 7) / 8) * 8)), dim3(256), 0, s, a);
+  const dim3 g3((unsigned)(((total + 7) / 8) * 8)), b3(256);
+  if (a.half) hipLaunchKernelGGL((dense_kernel<true>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((dense_kernel<false>), g3, b3, 0, s, a);
   return hipGetLastError();
 }
 

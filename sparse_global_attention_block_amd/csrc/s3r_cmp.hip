@@ -43,7 +43,7 @@ constexpr int kFusedWaves = 4;
 // indices at the end. The entries are ordered by (score desc, block index asc), a total order,
 // so the final set does not depend on the order in which blocks arrive, and the decision is
 // made on exactly the f32 column sums the score matrix would have held.
-template <bool kFused, int kQB, int kWaves, bool kPipe, bool kTopk = false>
+template <bool kFused, int kQB, int kWaves, bool kPipe, bool kTopk = false, bool kHalf = false>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void cmp_kernel(CmpArgs a) {
   constexpr int kRing = kPipe ? 3 : 2;
   constexpr int kThreads = 64 * kWaves;
@@ -149,10 +149,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int nt = 0; nt < 4; ++nt) {
         // the pipelined pass 2 subtracts its fixed offset on the VALU (its second accumulator
         // set leaves no room to hold the offset as a C operand across tiles)
-        floatx4 x = mfma16(h0, qb[nt][0], kOffsetOnValu ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[nt]);
-        x = mfma16(h1, qb[nt][1], x);
-        x = mfma16(l0, qb[nt][0], x);
-        acc[s2][nt] = mfma16(l1, qb[nt][1], x);
+        floatx4 x = mfma_in<kHalf>(h0, qb[nt][0],
+                                   kOffsetOnValu ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[nt]);
+        x = mfma_in<kHalf>(h1, qb[nt][1], x);
+        x = mfma_in<kHalf>(l0, qb[nt][0], x);
+        acc[s2][nt] = mfma_in<kHalf>(l1, qb[nt][1], x);
       }
     }
   };
@@ -390,32 +391,38 @@ static dim3 cmp_grid(const CmpArgs& a, int waves) {
   return dim3((unsigned)(((total + 7) / 8) * 8));
 }
 
-static hipError_t launch_cmp(const CmpArgs& a, hipStream_t s, bool fused) {
+template <bool kHalf>
+static hipError_t launch_cmp_t(const CmpArgs& a, hipStream_t s, bool fused, bool topk) {
   if (fused) {
     const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
-    switch (a.B) {
-      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false>), g3, b3, 0, s, a); break;
-      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false>), g3, b3, 0, s, a); break;
-      default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false>), g3, b3, 0, s, a); break;
+    if (topk) {
+      switch (a.B) {
+        case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, true, kHalf>), g3, b3, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, true, kHalf>), g3, b3, 0, s, a); break;
+        default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, true, kHalf>), g3, b3, 0, s, a); break;
+      }
+    } else {
+      switch (a.B) {
+        case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, false, kHalf>), g3, b3, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, false, kHalf>), g3, b3, 0, s, a); break;
+        default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, false, kHalf>), g3, b3, 0, s, a); break;
+      }
     }
   } else {
-    hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false>), cmp_grid(a, kLseWaves),
+    hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false, false, kHalf>), cmp_grid(a, kLseWaves),
                        dim3(64 * kLseWaves), 0, s, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, false); }
-hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, true); }
+static hipError_t launch_cmp(const CmpArgs& a, hipStream_t s, bool fused, bool topk) {
+  return a.half ? launch_cmp_t<true>(a, s, fused, topk) : launch_cmp_t<false>(a, s, fused, topk);
+}
 
+hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, false, false); }
+hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, true, false); }
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s) {
-  const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
-  switch (a.B) {
-    case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, true>), g3, b3, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, true>), g3, b3, 0, s, a); break;
-    default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, true>), g3, b3, 0, s, a); break;
-  }
-  return hipGetLastError();
+  return launch_cmp(a, s, true, true);
 }
 
 }  // namespace s3r

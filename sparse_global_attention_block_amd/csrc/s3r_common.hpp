@@ -71,6 +71,48 @@ __device__ __forceinline__ floatx4 mfma16h(const halfx8& a, const halfx8& b, con
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Element type of the caller's q, k, v (and of the output): bf16 (kHalf = false) or fp16.
+// Operands stay 16-byte bit patterns; the matrix product picks the instruction.
+template <bool kHalf>
+__device__ __forceinline__ floatx4 mfma_in(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  if constexpr (kHalf) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                  __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+}
+
+template <bool kHalf>
+__device__ __forceinline__ float in_to_float(uint32_t bits16) {
+  if constexpr (kHalf) {
+    return (float)__builtin_bit_cast(_Float16, (u16)bits16);
+  } else {
+    return __builtin_bit_cast(float, bits16 << 16);
+  }
+}
+
+// round to nearest even
+template <bool kHalf>
+__device__ __forceinline__ u16 float_to_in(float x) {
+  if constexpr (kHalf) {
+    return __builtin_bit_cast(u16, (_Float16)x);
+  } else {
+    return __builtin_bit_cast(u16, (__bf16)x);
+  }
+}
+
+// the 8 elements of a 16-byte chunk
+template <bool kHalf>
+__device__ __forceinline__ void unpack8(const uint4& w, float (&x)[8]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = in_to_float<kHalf>(ws[e] & 0xFFFFu);
+    x[2 * e + 1] = in_to_float<kHalf>(ws[e] >> 16);
+  }
+}
+
 __device__ __forceinline__ u16 bf16_bits(float x) {
   __bf16 b = (__bf16)x;  // round to nearest even
   return __builtin_bit_cast(u16, b);

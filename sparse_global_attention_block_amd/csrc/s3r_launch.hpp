@@ -12,6 +12,7 @@ struct PoolArgs {
   int64_t k_st, k_sh, v_st, v_sh;
   int64_t T, Nb, n_tiles;
   int32_t H, B;
+  int32_t half;            // inputs are fp16 (else bf16)
   float key_mult;          // scale * log2(e), folded into the packed pooled keys
   float* k_mean; float* v_mean;  // optional f32 [H][Nb][64]
   unsigned char* tiles;    // [H][n_tiles][12 KB]
@@ -22,6 +23,7 @@ struct PackArgs {
   int64_t k_st, k_sh, v_st, v_sh;
   int64_t T, n_tiles;
   int32_t H;
+  int32_t half;            // inputs are fp16 (else bf16)
   unsigned char* tiles;    // [H][n_tiles][8 KB]
 };
 
@@ -30,6 +32,7 @@ struct CmpArgs {
   int64_t q_st, q_sh;
   int64_t T, Nb, n_tiles;  // n_tiles = ceil(Nb / 32)
   int32_t H, B;
+  int32_t half;            // q and the pooled key records are fp16 (else bf16)
   const unsigned char* tiles;  // pooled tiles
   float* lse;              // [H][T] natural log (written by the LSE pass, read by the fused pass)
   const float* lse_in;
@@ -56,6 +59,7 @@ struct AttnArgs {
   int64_t q_st, q_sh;
   int64_t T, Nb, n_tiles;  // raw tiles: n_tiles = ceil(T / 32)
   int32_t H, B;
+  int32_t half;            // q, k and out are fp16 (else bf16)
   float logit_mult;        // scale * log2(e)
   const unsigned char* tiles;  // raw packed k/v tiles
   // selection only
@@ -65,7 +69,7 @@ struct AttnArgs {
   float* o_sel;            // optional
   float* lse_sel;          // optional [H][T]: base-2 log-sum-exp of the selection softmax
                            // in units of the scaled logit (scale*log2(e)*q.k); +inf if empty
-  uint16_t* out;           // bf16 [T][H][64]
+  uint16_t* out;           // [T][H][64], the input type
 };
 
 // Token layout of the window order (see s3r_window.hip): views x (special + grid_h*grid_w).

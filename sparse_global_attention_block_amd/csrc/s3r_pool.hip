@@ -12,8 +12,10 @@ namespace s3r {
 // One work-group per (head, tile of 32 consecutive blocks). Thread (slot m = tid/8, dim group
 // d8 = tid%8) sums block 32*tile + m over its tokens, 8 dims of k and of v at a time, in f32,
 // then divides by the block's token count (IEEE division). Writes the f32 means (optional)
-// and one pooled tile: the mean keys scaled by key_mult = scale*log2(e) as bf16 hi + bf16 lo
-// (hi = bf16(x), lo = bf16(x - hi)), and the mean values as fp16 V^T records.
+// and one pooled tile: the mean keys scaled by key_mult = scale*log2(e) as a hi + lo pair in the
+// input type (hi = round(x), lo = round(x - hi); bf16 or fp16), and the mean values as fp16
+// V^T records.
+template <bool kHalf>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[kPooledTileBytes];
   const int tid = threadIdx.x;
@@ -34,14 +36,13 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     for (int64_t t = 0; t < n; ++t) {
       const uint4 kk = *reinterpret_cast<const uint4*>(kp + t * a.k_st);
       const uint4 vv = *reinterpret_cast<const uint4*>(vp + t * a.v_st);
-      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+      float kx[8], vx[8];
+      unpack8<kHalf>(kk, kx);
+      unpack8<kHalf>(vv, vx);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ks[2 * e] += __builtin_bit_cast(float, kw[e] << 16);
-        ks[2 * e + 1] += __builtin_bit_cast(float, kw[e] & 0xFFFF0000u);
-        vs[2 * e] += __builtin_bit_cast(float, vw[e] << 16);
-        vs[2 * e + 1] += __builtin_bit_cast(float, vw[e] & 0xFFFF0000u);
+      for (int e = 0; e < 8; ++e) {
+        ks[e] += kx[e];
+        vs[e] += vx[e];
       }
     }
     const float fn = (float)n;
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = ks[e] * a.key_mult;
-    hi[e] = bf16_bits(x);
-    lo[e] = bf16_bits(x - bf16_to_float(hi[e]));
+    hi[e] = float_to_in<kHalf>(x);
+    lo[e] = float_to_in<kHalf>(x - in_to_float<kHalf>(hi[e]));
   }
   const int koff = k_chunk_offset(m, d8);
   uint4 hv, lv;
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 // copies 16 bytes of k into its K record slot and scatters 8 values of v, converted to fp16,
 // into the V^T records through LDS. Tokens beyond T are zero.
 constexpr int kPackTiles = 4;
+template <bool kHalf>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[4 * kRecBytes];
   const int tid = threadIdx.x;
@@ -110,13 +112,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     unsigned char* out = a.tiles + ((int64_t)h * a.n_tiles + tile) * kRawTileBytes;
     *reinterpret_cast<uint4*>(out + k_chunk_offset(m, d8)) = kk;
     u16* vt = reinterpret_cast<u16*>(stage);
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    float vx[8];
+    unpack8<kHalf>(vv, vx);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       int rec, lane, slot;
       vt_position(m, d8 * 8 + e, rec, lane, slot);
-      const uint32_t b = (e & 1) ? (vw[e >> 1] & 0xFFFF0000u) : (vw[e >> 1] << 16);
-      vt[(rec * 64 + lane) * 8 + slot] = f16_bits(__builtin_bit_cast(float, b));
+      vt[(rec * 64 + lane) * 8 + slot] = f16_bits(vx[e]);  // exact for fp16 inputs
     }
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(out + 4 * kRecBytes);
@@ -127,13 +129,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_tiles, (unsigned)a.H);
-  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, s, a);
+  if (a.half) hipLaunchKernelGGL((pool_kernel<true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((pool_kernel<false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.n_tiles + kPackTiles - 1) / kPackTiles), (unsigned)a.H);
-  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, a);
+  if (a.half) hipLaunchKernelGGL((pack_kernel<true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((pack_kernel<false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ class Params(ctypes.Structure):
         ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
         ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
         ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
-        ("gate_stride_t", ctypes.c_int64),
+        ("gate_stride_t", ctypes.c_int64), ("dtype", ctypes.c_int32), ("pad", ctypes.c_int32),
     ]
 
 
@@ -38,6 +38,9 @@ class Windows(ctypes.Structure):
         ("views", ctypes.c_int64), ("special", ctypes.c_int32), ("grid_h", ctypes.c_int32),
         ("grid_w", ctypes.c_int32), ("win_h", ctypes.c_int32), ("win_w", ctypes.c_int32),
     ]
+
+
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1}  # s3r_dtype
 
 
 class Speed3RError(RuntimeError):
@@ -135,18 +138,20 @@ def _stream():
 def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
                 scale: float = 0.0, gates: Optional[torch.Tensor] = None,
                 forced_blocks: int = 0) -> Params:
-    """Params for [T, H, 64] bf16 token tensors (any token/head strides, last dim contiguous).
-    ``forced_blocks`` key blocks 0..F-1 are selected for every query block on top of the
-    top-k of the rest."""
+    """Params for [T, H, 64] bf16 or fp16 token tensors (one type for q, k, v; any token/head
+    strides, last dim contiguous). ``forced_blocks`` key blocks 0..F-1 are selected for every
+    query block on top of the top-k of the rest."""
     T, H, D = q.shape
     for x in (q, k, v):
-        if x.dtype != torch.bfloat16 or tuple(x.shape) != (T, H, D) or x.stride(2) != 1:
-            raise ValueError("q, k, v must be bf16 [T, H, D] with a contiguous last dimension")
+        if x.dtype not in _DTYPES or x.dtype != q.dtype or tuple(x.shape) != (T, H, D) or \
+                x.stride(2) != 1:
+            raise ValueError("q, k, v must be one of bf16/fp16, [T, H, D] with a contiguous "
+                             "last dimension")
     gst = 0
     if gates is not None and gates.dim() == 3:
         gst = gates.stride(0)
     return Params(T, H, D, block, topk, float(scale), forced_blocks, q.stride(0), q.stride(1),
-                  k.stride(0), k.stride(1), v.stride(0), v.stride(1), gst)
+                  k.stride(0), k.stride(1), v.stride(0), v.stride(1), gst, _DTYPES[q.dtype], 0)
 
 
 def num_blocks(p: Params) -> int:
@@ -183,10 +188,10 @@ def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Full forward pass. Returns (out [T, H, 64] bf16, sel_idx or None)."""
+    """Full forward pass. Returns (out [T, H, 64] in the input type, sel_idx or None)."""
     p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(workspace_size(p), q.device)
     st = lib().speed3r_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gates),
@@ -233,7 +238,7 @@ def sel_combine(p: Params, q, workspace, sel_idx, o_cmp, gates, out, o_sel=None)
 def dense_attn_fwd(q, k, v, scale: float = 0.0, out=None, workspace=None):
     p = make_params(q, k, v, 64, 1, scale)
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(dense_workspace_size(p), q.device)
     _check("speed3r_dense_attn_fwd", lib().speed3r_dense_attn_fwd(
@@ -264,7 +269,7 @@ def sparse_attn_fwd_train(q, k, v, gates, block: int, topk: int, scale: float = 
                           ) -> Trained:
     """Forward pass that keeps the state speed3r_sparse_attn_bwd needs."""
     p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     sel = torch.empty(q.shape[1], num_blocks(p), num_selected(p), dtype=torch.int32,
                       device=q.device)
     if workspace is None:
@@ -305,7 +310,7 @@ def window_source(layout, pos: int) -> int:
 
 def window_permute(layout, src: torch.Tensor, dst: Optional[torch.Tensor] = None,
                    inverse: bool = False) -> torch.Tensor:
-    """Reorder a bf16 [T, H, 64] tensor into window order (or back, inverse=True)."""
+    """Reorder a [T, H, 64] bf16/fp16 tensor into window order (or back, inverse=True)."""
     w = make_windows(layout)
     if dst is None:
         dst = torch.empty(src.shape, dtype=src.dtype, device=src.device)
@@ -330,7 +335,7 @@ def sparse_attn_fwd_windows(q, k, v, gates, block: int, topk: int, layout, scale
     p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
     w = make_windows(layout)
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(windows_workspace_size(p, layout), q.device)
     _check("speed3r_sparse_attn_fwd_windows", lib().speed3r_sparse_attn_fwd_windows(
@@ -343,7 +348,7 @@ class Stages:
     """Runs the forward pass one stage at a time and keeps every intermediate result:
     k_mean, v_mean [H, Nb, 64] f32, lse [H, T] f32, o_cmp [T, H, 64] f32,
     score [H, Nb, ld] f32, sel [H, Nb, k_eff] int32 (k_eff = forced prefix + chosen blocks),
-    o_sel [T, H, 64] f32, out bf16."""
+    o_sel [T, H, 64] f32, out (input type)."""
 
     def __init__(self, q, k, v, gates, block: int, topk_: int, scale: float = 0.0,
                  keep_o_sel: bool = True, keep_score: bool = True, forced_blocks: int = 0):
@@ -364,7 +369,7 @@ class Stages:
         self.score = torch.empty(H, self.Nb, self.ld, **f32) if keep_score else None
         self.sel = torch.empty(H, self.Nb, self.k_eff, dtype=torch.int32, device=dev)
         self.o_sel = torch.empty(T, H, D, **f32) if keep_o_sel else None
-        self.out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(T, H, D, dtype=q.dtype, device=dev)
 
     def run_pool(self):
         pool(self.p, self.k, self.v, self.ws, self.k_mean, self.v_mean)

@@ -24,7 +24,7 @@ Generators:
     compression branch, column 1 the selection branch).
 
 Everything is drawn in float32 with a ``torch.Generator`` seeded per tensor, then rounded once
-to bfloat16 (round to nearest even). Both sides of a parity check consume the same bfloat16
+to bfloat16 (or float16 for ``dtype="fp16"``; round to nearest even). Both sides of a parity check consume the same bfloat16
 values: the GPU path directly, the oracle after an exact upcast to float.
 """
 from __future__ import annotations
@@ -57,6 +57,7 @@ class Workload:
     grid: Optional[Tuple[int, int]] = None    # patch grid (rows, cols) after the specials
     window: Optional[Tuple[int, int]] = None  # 2-D pooling window (rows, cols): window order
     spatial: float = 0.0  # weight of the smooth 2-D position term (grid workloads only)
+    dtype: str = "bf16"   # element type of q, k, v: "bf16" or "fp16"
 
     @property
     def T(self) -> int:
@@ -83,6 +84,7 @@ class Workload:
             "workload": self.name, "views": self.views, "tokens_per_view": self.tokens_per_view,
             "T": self.T, "H": self.H, "D": self.D, "block": self.block, "topk": self.topk,
             "generator": self.gen, "seed": self.seed,
+            "dtype": self.dtype,
             **({"forced_blocks": self.forced} if self.forced else {}),
             **({"grid": list(self.grid)} if self.grid else {}),
             **({"window": list(self.window), "spatial": self.spatial} if self.window else {}),
@@ -109,6 +111,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     # by every query block in addition to its top-16
     Workload("v1000_k16_ref", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
              special_mult=3.0, forced=22),
+    # the same in fp16 (the model runs in bf16 or fp16)
+    Workload("v1000_k16_fp16", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
+             special_mult=3.0, dtype="fp16"),
     # 2-D windows: 560x560 images (a multiple of 56) give a 40x40 patch grid; 8x8 windows are
     # the 64-token blocks; a smooth position term makes nearby patches alike
     Workload("v1000_win8", 1000, 5 + 40 * 40, 5, 16, 64, 16, "structured", seed=1001,
@@ -132,7 +137,8 @@ def _randn(shape, seed, stream, device, std=1.0):
 
 def make_inputs(w: Workload, device="cpu", T: Optional[int] = None,
                 views: Optional[int] = None) -> Dict[str, torch.Tensor]:
-    """Return q, k, v as contiguous [T, H, 64] bfloat16 tensors and gates [H, 2] float32.
+    """Return q, k, v as contiguous [T, H, 64] tensors of the workload's type (bfloat16 or
+    float16) and gates [H, 2] float32.
 
     ``views`` (or ``T``) overrides the length of the sequence while keeping the recipe, which
     is how tests build small instances of a large workload.
@@ -142,11 +148,12 @@ def make_inputs(w: Workload, device="cpu", T: Optional[int] = None,
     nv = max(1, -(-TT // w.tokens_per_view))
     H, D = w.H, w.D
     dev = torch.device(device)
+    elt = {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
     out = {}
     if w.gen == "iid":
         for i, name in enumerate(("q", "k", "v")):
             x = _randn((TT, H, D), w.seed, i, dev, w.iid_scale)
-            out[name] = x.to(torch.bfloat16)
+            out[name] = x.to(elt)
     elif w.gen == "structured":
         e = _randn((nv, 8), w.seed, 10, dev)                         # view embeddings
         w_qk = _randn((H, 8, D), w.seed, 11, dev, math.sqrt(1.0 / 8.0))
@@ -177,7 +184,7 @@ def make_inputs(w: Workload, device="cpu", T: Optional[int] = None,
                 x.add_(torch.einsum("tf,hfd->thd", *pos_qk), alpha=w.spatial)
             if name in ("k", "v") and special is not None and w.special_mult != 1.0:
                 x[special] *= w.special_mult
-            out[name] = x.to(torch.bfloat16)
+            out[name] = x.to(elt)
             del x
     else:
         raise ValueError(f"unknown generator {w.gen!r}")

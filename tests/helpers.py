@@ -68,17 +68,29 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(ax)) - 8)
 
 
+def fp16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of float16 numbers at |x| (11 significant bits; 2^-25 below the
+    smallest normal)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(ax)) - 11)
+
+
 def check_out(gpu_out: torch.Tensor, ref: np.ndarray, what="out",
               max_abs=OUT_MAX_ABS, mean_abs=OUT_MEAN_ABS):
-    """Compare a GPU result with the float64 oracle. For a bf16 result both bounds apply to
-    the error beyond the final rounding to bf16, excess = max(0, |gpu - ref| - half_ulp(ref)):
+    """Compare a GPU result with the float64 oracle. For a bf16 (fp16) result both bounds apply
+    to the error beyond the final rounding, excess = max(0, |gpu - ref| - half_ulp(ref)):
     the rounding alone reaches 2e-2 once |x| >= 8 and averages ~|x|/1024, so outputs of
     magnitude > 2 would fail a plain mean-abs bound of 2e-3 even if computed exactly.
     f32 results are held to the plain difference. Returns the plain max and mean."""
     g = gpu_out.detach().float().cpu().numpy().astype(np.float64)
     d = np.abs(g - ref)
     assert np.isfinite(d).all(), f"{what}: non-finite values"
-    excess = np.maximum(d - bf16_half_ulp(ref), 0.0) if gpu_out.dtype == torch.bfloat16 else d
+    if gpu_out.dtype == torch.bfloat16:
+        excess = np.maximum(d - bf16_half_ulp(ref), 0.0)
+    elif gpu_out.dtype == torch.float16:
+        excess = np.maximum(d - fp16_half_ulp(ref), 0.0)
+    else:
+        excess = d
     assert excess.max() <= max_abs, \
         f"{what}: max-abs {d.max():.3e} (beyond output rounding {excess.max():.3e}) > {max_abs}"
     assert excess.mean() <= mean_abs, \

@@ -38,9 +38,10 @@ def test_status_strings():
     assert S.status_string(99) == "S3R_ERR_UNKNOWN"
 
 
-def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0):
+def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0, dtype=0):
     st = st or (H * D, D)
-    return S.Params(T, H, D, B, k, scale, forced, st[0], st[1], st[0], st[1], st[0], st[1], 0)
+    return S.Params(T, H, D, B, k, scale, forced, st[0], st[1], st[0], st[1], st[0], st[1], 0,
+                    dtype, 0)
 
 
 def test_size_queries():
@@ -74,6 +75,7 @@ def test_size_queries():
     (dict(st=(-256, 64)), S.S3R_ERR_INVALID_ARG),
     (dict(T=24577 * 16, B=16, k=65), S.S3R_ERR_UNSUPPORTED),  # > 24576 blocks, not folded
     (dict(forced=-1), S.S3R_ERR_INVALID_ARG),
+    (dict(dtype=2), S.S3R_ERR_INVALID_ARG),
 ])
 def test_bad_params_rejected_everywhere(kw, code):
     p = params(**kw)
@@ -217,3 +219,17 @@ def test_window_forward_checks():
     assert L.speed3r_sparse_attn_fwd_windows(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, FAKE,
                                              FAKE, FAKE, None, ws, ctypes.c_size_t(need - 1),
                                              None) == S.S3R_ERR_WORKSPACE
+
+
+def test_params_layout_matches_header():
+    """The ctypes mirror of s3r_params has the C layout: 96 bytes, dtype at offset 88."""
+    assert ctypes.sizeof(S.Params) == 96
+    assert S.Params.dtype.offset == 88 and S.Params.gate_stride_t.offset == 80
+
+
+def test_backward_rejects_fp16():
+    p = params(dtype=1)
+    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
+    assert S.lib().speed3r_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 256, 64,
+                                          ws, big, FAKE, FAKE, FAKE, FAKE, ws, big, None) \
+        == S.S3R_ERR_UNSUPPORTED

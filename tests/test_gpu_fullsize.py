@@ -23,7 +23,8 @@ def sample_rows(w: W.Workload, n_random: int, seed: int):
     return sorted(r for r in rows if r < Nb)
 
 
-@pytest.mark.parametrize("name", ["v32", "v100", "v1000_k16", "v1000_k32", "v1000_k16_ref"])
+@pytest.mark.parametrize("name", ["v32", "v100", "v1000_k16", "v1000_k32", "v1000_k16_ref",
+                                  "v1000_k16_fp16"])
 def test_fullsize_sampled_rows(name):
     w = W.WORKLOADS[name]
     print(f"[fullsize {name}] T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}", flush=True)

@@ -32,6 +32,11 @@ CASES = {
                                         forced=2), 1100),
     "forced_all": (dataclasses.replace(_tiny_s, name="forced_all", H=2, block=32, topk=5,
                                        forced=100), 1000),
+    # fp16 inputs and output (f16 matrix products, fp16 hi + lo pooled keys)
+    "tiny_s_fp16": (dataclasses.replace(_tiny_s, name="tiny_s_fp16", dtype="fp16"), None),
+    "v3_fp16": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_fp16", dtype="fp16"), 3 * 1374),
+    "b128_fp16": (dataclasses.replace(_tiny_s, name="b128_fp16", H=2, block=128, topk=3,
+                                      dtype="fp16"), 1100),
 }
 
 _cache = {}
@@ -225,9 +230,10 @@ def test_deterministic_and_strided_inputs():
     assert torch.equal(a, d)
 
 
-def test_dense_against_oracle():
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_dense_against_oracle(dtype):
     for name, T in (("tiny", None), ("v8", 3 * 1374 + 7)):
-        w = W.WORKLOADS[name]
+        w = dataclasses.replace(W.WORKLOADS[name], dtype=dtype)
         x = cuda_inputs(w, T=T)
         out = S.dense_attn_fwd(x["q"], x["k"], x["v"])
         torch.cuda.synchronize()
