@@ -191,6 +191,15 @@ __device__ __forceinline__ int reduced_key(int lane) {
 
 // Work-group id remapped so that consecutive logical ids share an XCD: the dispatcher hands
 // work-groups to the 8 XCDs round-robin, so logical id x*per + s runs on XCD x.
+// Work-group barrier that orders LDS only: waits for this wave's LDS operations, not for its
+// global loads, so a prefetch for a later step stays in flight across it (__syncthreads
+// waits for every outstanding memory operation).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int64_t xcd_logical_id(int64_t b, int64_t total) {
   const int64_t per = (total + 7) / 8;
   return (b % 8) * per + b / 8;
