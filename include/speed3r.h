@@ -211,15 +211,17 @@ size_t speed3r_bwd_workspace_size(const s3r_params* p);
 
 /* Gradients of the sparse forward pass. q, k, v, gates and p must be those of the
  * speed3r_sparse_attn_fwd_train call whose workspace is `train_workspace` (read only).
- *   dout     bf16 [T][H][64], the gradient of out; element strides multiples of 8.
+ *   dout     [T][H][64] of the input type (bf16 or fp16), the gradient of out; element
+ *            strides multiples of 8.
  *   dq, dk, dv   f32 [T][H][64], contiguous; overwritten.
  *   dgates   f32 with the layout of gates ([H][2], or gate(t, h, b) at t * gate_stride_t +
  *            h * 2 + b for per-token gates); overwritten.
  * Every output element is written by one thread in a fixed order: results are bitwise
- * repeatable. Numerics: the recomputed logits use the same bf16 operands as the forward
- * pass (pooled keys as hi + lo), probabilities use the saved log-sum-exps, the pooled values
- * and the products feeding dq, dk, dv take bf16 operands with f32 accumulation. */
-/* fp16 inputs: S3R_ERR_UNSUPPORTED (the backward pass is built for bf16). */
+ * repeatable. Numerics: the recomputed logits use the same operands as the forward pass
+ * (the input type; pooled keys as hi + lo), probabilities use the saved log-sum-exps, dP takes
+ * dout and the values in the input type, and the products feeding dq, dk, dv take bf16
+ * operands (P, dS and transposed images of q, k, dout, the pooled keys), all with f32
+ * accumulation. */
 s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const void* k,
                                    const void* v, const float* gates, const void* dout,
                                    int64_t dout_stride_t, int64_t dout_stride_h,

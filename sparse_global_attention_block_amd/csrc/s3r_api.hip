@@ -488,7 +488,6 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
   Dims d;
   s3r_status st = check_params(p, &d);
   if (st != S3R_OK) return st;
-  if (d.half) return S3R_ERR_UNSUPPORTED;
   if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !tok_ok(dout) ||
       !valid_stride(dout_stride_t) || !valid_stride(dout_stride_h) || !dq || !aligned(dq, 16) ||
       !dk || !aligned(dk, 16) || !dv || !aligned(dv, 16) || !dgates || !aligned(dgates, 4))
@@ -504,6 +503,7 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
   // operand images of q, dout (query tiles), v, k (raw) and the block means (pooled)
   RecPackArgs r;
   r.H = d.H;
+  r.half = d.half;
   auto pack = [&](const void* src, int64_t st_, int64_t sh_, int64_t rows, int64_t n_tiles,
                   unsigned char* dst, int64_t tile_bytes, int r_off, int tr_off, int kind) {
     r.src = src; r.st = st_; r.sh = sh_; r.rows = rows; r.n_tiles = n_tiles; r.dst = dst;
@@ -527,7 +527,7 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
 
   // per-token scalars and gate gradients
   BwdScalarArgs sa;
-  sa.T = d.T; sa.H = d.H;
+  sa.T = d.T; sa.H = d.H; sa.half = d.half;
   sa.lse_cmp = (const float*)(tw + L.lse);
   sa.lse_sel = (const float*)(tw + TL.lse_sel);
   sa.gates = gates; sa.gate_st = p->gate_stride_t;
@@ -547,6 +547,7 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
   BwdArgs b;
   memset(&b, 0, sizeof(b));
   b.T = d.T; b.Nb = d.Nb; b.n_ctiles = nc; b.n_ktiles = nk; b.H = d.H; b.B = d.B;
+  b.half = d.half;
   b.scale = d.scale; b.logit_mult = d.scale * kLog2e;
   b.pooled = tw + L.pooled; b.pooled_bwd = ws + BL.pooled_bwd;
   b.raw = tw + L.raw; b.raw_bwd = ws + BL.raw_bwd;

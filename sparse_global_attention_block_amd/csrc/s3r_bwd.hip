@@ -29,7 +29,9 @@ namespace s3r {
 // Operand images. Thread (row m, dims 8*d8..+7) of a 256-thread work-group; the TR group is
 // assembled in LDS and written linearly.
 // ---------------------------------------------------------------------------------------
-template <int kKind>
+// kKind 0: 2-byte source of type kHalf; 1: f32 source. R records are written in the input
+// type (kHalf), TR records in bf16.
+template <int kKind, bool kHalf>
 __global__ __launch_bounds__(256) void rec_pack_kernel(RecPackArgs a) {
   __shared__ __attribute__((aligned(16))) u16 stage[4 * kRecBytes / 2];
   const int tid = threadIdx.x;
@@ -42,12 +44,7 @@ __global__ __launch_bounds__(256) void rec_pack_kernel(RecPackArgs a) {
       if constexpr (kKind == 0) {
         const uint4 w = *reinterpret_cast<const uint4*>(
             reinterpret_cast<const u16*>(a.src) + row * a.st + (int64_t)h * a.sh + d8 * 8);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = __builtin_bit_cast(float, ws[e] << 16);
-          x[2 * e + 1] = __builtin_bit_cast(float, ws[e] & 0xFFFF0000u);
-        }
+        unpack8<kHalf>(w, x);
       } else {
         const float4* f = reinterpret_cast<const float4*>(
             reinterpret_cast<const float*>(a.src) + row * a.st + (int64_t)h * a.sh + d8 * 8);
@@ -62,10 +59,10 @@ __global__ __launch_bounds__(256) void rec_pack_kernel(RecPackArgs a) {
     unsigned char* out = a.dst + ((int64_t)h * a.n_tiles + tile) * a.tile_bytes;
     if (a.r_off >= 0) {
       uint4 w;
-      w.x = bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
-      w.y = bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
-      w.z = bf16_bits(x[4]) | ((uint32_t)bf16_bits(x[5]) << 16);
-      w.w = bf16_bits(x[6]) | ((uint32_t)bf16_bits(x[7]) << 16);
+      w.x = float_to_in<kHalf>(x[0]) | ((uint32_t)float_to_in<kHalf>(x[1]) << 16);
+      w.y = float_to_in<kHalf>(x[2]) | ((uint32_t)float_to_in<kHalf>(x[3]) << 16);
+      w.z = float_to_in<kHalf>(x[4]) | ((uint32_t)float_to_in<kHalf>(x[5]) << 16);
+      w.w = float_to_in<kHalf>(x[6]) | ((uint32_t)float_to_in<kHalf>(x[7]) << 16);
       *reinterpret_cast<uint4*>(out + a.r_off + k_chunk_offset(m, d8)) = w;
     }
     if (a.tr_off >= 0) {  // uniform over the work-group
@@ -84,8 +81,13 @@ __global__ __launch_bounds__(256) void rec_pack_kernel(RecPackArgs a) {
 
 hipError_t launch_rec_pack(const RecPackArgs& a, int kind, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_tiles < 2048 ? a.n_tiles : 2048), (unsigned)a.H);
-  if (kind == 0) hipLaunchKernelGGL((rec_pack_kernel<0>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((rec_pack_kernel<1>), grid, dim3(256), 0, s, a);
+  if (kind == 0) {
+    if (a.half) hipLaunchKernelGGL((rec_pack_kernel<0, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rec_pack_kernel<0, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.half) hipLaunchKernelGGL((rec_pack_kernel<1, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rec_pack_kernel<1, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -94,6 +96,7 @@ hipError_t launch_rec_pack(const RecPackArgs& a, int kind, hipStream_t s) {
 //   qs = {L_cmp*log2(e), g0, g0 dout.O_cmp, L_sel (base 2), g1, g1 dout.O_sel, 0, 0}
 //   dg_tok[t][h] = {dout.O_cmp, dout.O_sel} (the gate gradients of token t)
 // ---------------------------------------------------------------------------------------
+template <bool kHalf>
 __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdScalarArgs a) {
   const int sub = threadIdx.x & 7;
   const int64_t n = a.T * a.H;
@@ -103,7 +106,8 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdScalarArgs a) {
     const int h = (int)(idx - t * a.H);
     const uint4 w = *reinterpret_cast<const uint4*>(a.dout + t * a.d_st + (int64_t)h * a.d_sh +
                                                     sub * 8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float dv8[8];
+    unpack8<kHalf>(w, dv8);
     const float4* oc = reinterpret_cast<const float4*>(a.o_cmp + idx * kD + sub * 8);
     const float4* os = reinterpret_cast<const float4*>(a.o_sel + idx * kD + sub * 8);
     const float4 c0 = oc[0], c1 = oc[1], s0 = os[0], s1 = os[1];
@@ -112,10 +116,8 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdScalarArgs a) {
     float dc = 0.f, ds = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float d = __builtin_bit_cast(float, (e & 1) ? (ws[e >> 1] & 0xFFFF0000u)
-                                                       : (ws[e >> 1] << 16));
-      dc = fmaf(d, cv[e], dc);
-      ds = fmaf(d, sv[e], ds);
+      dc = fmaf(dv8[e], cv[e], dc);
+      ds = fmaf(dv8[e], sv[e], ds);
     }
 #pragma unroll
     for (int x = 1; x < 8; x <<= 1) {
@@ -137,8 +139,9 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdScalarArgs a) {
 
 hipError_t launch_bwd_scalars(const BwdScalarArgs& a, hipStream_t s) {
   const int64_t want = (a.T * a.H + 31) / 32;
-  hipLaunchKernelGGL(bwd_scalars_kernel, dim3((unsigned)(want < 16384 ? want : 16384)),
-                     dim3(256), 0, s, a);
+  const dim3 g3((unsigned)(want < 16384 ? want : 16384)), b3(256);
+  if (a.half) hipLaunchKernelGGL((bwd_scalars_kernel<true>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((bwd_scalars_kernel<false>), g3, b3, 0, s, a);
   return hipGetLastError();
 }
 
@@ -206,6 +209,7 @@ hipError_t launch_sel_bitmap(const BwdArgs& a, uint32_t* bitmap, hipStream_t s) 
 // Per tile: S^T (hi + lo, minus the saved log-sum-exp in the C operand), dP^T = Vc . dout^T,
 // dS = P (g0 dP - D) in registers, dq^T += Kc^T . dS^T.
 // ---------------------------------------------------------------------------------------
+template <bool kHalf>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cmp_dq_kernel(
     BwdArgs a) {
   constexpr int kStepU4 = 16 * kRecBytes / 16;  // 1024 uint4 per tile step
@@ -292,12 +296,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
       const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&L[512 + (2 * s2_ + 1) * 64 + lane]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        floatx4 x = mfma16(h0, qb[nt][0], cneg[nt]);
-        x = mfma16(h1, qb[nt][1], x);
-        x = mfma16(l0, qb[nt][0], x);
-        x = mfma16(l1, qb[nt][1], x);
-        floatx4 y = mfma16(v0, ob[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
-        y = mfma16(v1, ob[nt][1], y);
+        floatx4 x = mfma_in<kHalf>(h0, qb[nt][0], cneg[nt]);
+        x = mfma_in<kHalf>(h1, qb[nt][1], x);
+        x = mfma_in<kHalf>(l0, qb[nt][0], x);
+        x = mfma_in<kHalf>(l1, qb[nt][1], x);
+        floatx4 y = mfma_in<kHalf>(v0, ob[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        y = mfma_in<kHalf>(v1, ob[nt][1], y);
         float d[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -338,7 +342,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 
 hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.H * ((a.T + 255) / 256);
-  hipLaunchKernelGGL(cmp_dq_kernel, dim3((unsigned)(((total + 7) / 8) * 8)), dim3(256), 0, s, a);
+  const dim3 g3((unsigned)(((total + 7) / 8) * 8)), b3(256);
+  if (a.half) hipLaunchKernelGGL((cmp_dq_kernel<true>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((cmp_dq_kernel<false>), g3, b3, 0, s, a);
   return hipGetLastError();
 }
 
@@ -353,7 +359,7 @@ constexpr int kDkvWaves = 8;
 constexpr int kDkvAhead = 1;  // query tiles in flight beyond the one being computed on (2 is
                               // built and measured 5 % slower)
 
-template <int kWaves>
+template <int kWaves, bool kHalf>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
 cmp_dkv_kernel(BwdArgs a) {
   constexpr int kThreads = 64 * kWaves;
@@ -441,8 +447,11 @@ cmp_dkv_kernel(BwdArgs a) {
       lds[slot][rsrc[x]] = r0[b][x];
       const uint32_t w[4] = {r0[b][x].x, r0[b][x].y, r0[b][x].z, r0[b][x].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        tr[tr_pos[x][j]] = (u16)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+        // TR images are bf16 (they meet bf16 P and dS in the dKc, dVc products)
+        tr[tr_pos[x][j]] = kHalf ? bf16_bits(in_to_float<true>(e)) : (u16)e;
+      }
     }
     if (tid < kSU4) lds[slot][kQU4 + tid] = r2[b];
   };
@@ -473,12 +482,12 @@ cmp_dkv_kernel(BwdArgs a) {
         const floatx4 cq = {-l2[qh][0], -l2[qh][1], -l2[qh][2], -l2[qh][3]};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          floatx4 x = mfma16(qa0, kh[s][0], cq);
-          x = mfma16(qa1, kh[s][1], x);
-          x = mfma16(qa0, kl[s][0], x);
-          x = mfma16(qa1, kl[s][1], x);
-          floatx4 y = mfma16(oa0, vc[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          y = mfma16(oa1, vc[s][1], y);
+          floatx4 x = mfma_in<kHalf>(qa0, kh[s][0], cq);
+          x = mfma_in<kHalf>(qa1, kh[s][1], x);
+          x = mfma_in<kHalf>(qa0, kl[s][0], x);
+          x = mfma_in<kHalf>(qa1, kl[s][1], x);
+          floatx4 y = mfma_in<kHalf>(oa0, vc[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          y = mfma_in<kHalf>(oa1, vc[s][1], y);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(x[r]);
@@ -535,8 +544,9 @@ cmp_dkv_kernel(BwdArgs a) {
 
 hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.H * ((a.n_ctiles + kDkvWaves - 1) / kDkvWaves);
-  hipLaunchKernelGGL((cmp_dkv_kernel<kDkvWaves>), dim3((unsigned)(((total + 7) / 8) * 8)),
-                     dim3(64 * kDkvWaves), 0, s, a);
+  const dim3 g3((unsigned)(((total + 7) / 8) * 8)), b3(64 * kDkvWaves);
+  if (a.half) hipLaunchKernelGGL((cmp_dkv_kernel<kDkvWaves, true>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((cmp_dkv_kernel<kDkvWaves, false>), g3, b3, 0, s, a);
   return hipGetLastError();
 }
 
@@ -566,7 +576,7 @@ __device__ __forceinline__ bool bwd_next_block(const BwdArgs& a, const int32_t* 
   return false;
 }
 
-template <int NT>
+template <int NT, bool kHalf>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sel_dq_kernel(
     BwdArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -639,10 +649,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int s2_ = 0; s2_ < 2; ++s2_)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const floatx4 x = mfma16(kr[2 * s2_], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
-        acc[s2_][nt] = mfma16(kr[2 * s2_ + 1], qb[nt][1], x);
-        const floatx4 y = mfma16(vr[2 * s2_], ob[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
-        dp[s2_][nt] = mfma16(vr[2 * s2_ + 1], ob[nt][1], y);
+        const floatx4 x = mfma_in<kHalf>(kr[2 * s2_], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[s2_][nt] = mfma_in<kHalf>(kr[2 * s2_ + 1], qb[nt][1], x);
+        const floatx4 y = mfma_in<kHalf>(vr[2 * s2_], ob[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        dp[s2_][nt] = mfma_in<kHalf>(vr[2 * s2_ + 1], ob[nt][1], y);
       }
 #pragma unroll
     for (int s2_ = 0; s2_ < 2; ++s2_)
@@ -692,8 +702,13 @@ hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s) {
   const int parts = (a.B > 32) ? a.B / 32 : 1;
   const int64_t n_wg = ((int64_t)a.H * a.Nb * parts + 3) / 4;
   const dim3 g3((unsigned)(((n_wg + 7) / 8) * 8)), b3(256);
-  if (a.B == 16) hipLaunchKernelGGL((sel_dq_kernel<1>), g3, b3, 0, s, a);
-  else hipLaunchKernelGGL((sel_dq_kernel<2>), g3, b3, 0, s, a);
+  if (a.B == 16) {
+    if (a.half) hipLaunchKernelGGL((sel_dq_kernel<1, true>), g3, b3, 0, s, a);
+    else hipLaunchKernelGGL((sel_dq_kernel<1, false>), g3, b3, 0, s, a);
+  } else {
+    if (a.half) hipLaunchKernelGGL((sel_dq_kernel<2, true>), g3, b3, 0, s, a);
+    else hipLaunchKernelGGL((sel_dq_kernel<2, false>), g3, b3, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -706,6 +721,7 @@ hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s) {
 // branch's pooled gradients spread over the block, dKc_u / n_u and dVc_u / n_u, and writes dk,
 // dv for every token of the block.
 // ---------------------------------------------------------------------------------------
+template <bool kHalf>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sel_dkv_kernel(
     BwdArgs a) {
   __shared__ floatx4 red[3][16][64];
@@ -780,10 +796,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         const bf16x8 oa1 = Q[512 + (2 * qh + 1) * 64 + lane];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          floatx4 x = mfma16(qa0, kr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          x = mfma16(qa1, kr[s][1], x);
-          floatx4 y = mfma16(oa0, vr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          y = mfma16(oa1, vr[s][1], y);
+          floatx4 x = mfma_in<kHalf>(qa0, kr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          x = mfma_in<kHalf>(qa1, kr[s][1], x);
+          floatx4 y = mfma_in<kHalf>(oa0, vr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          y = mfma_in<kHalf>(oa1, vr[s][1], y);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(fmaf(x[r], a.logit_mult, -l2[qh][r]));
@@ -868,8 +884,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
 hipError_t launch_sel_dkv(const BwdArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.H * a.Nb;
-  hipLaunchKernelGGL(sel_dkv_kernel, dim3((unsigned)(((total + 7) / 8) * 8)), dim3(256), 0, s,
-                     a);
+  const dim3 g3((unsigned)(((total + 7) / 8) * 8)), b3(256);
+  if (a.half) hipLaunchKernelGGL((sel_dkv_kernel<true>), g3, b3, 0, s, a);
+  else hipLaunchKernelGGL((sel_dkv_kernel<false>), g3, b3, 0, s, a);
   return hipGetLastError();
 }
 

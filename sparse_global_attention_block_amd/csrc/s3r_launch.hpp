@@ -113,6 +113,8 @@ struct WindowCopyArgs {
 // Operand-image record groups of 32 rows x 64 dims (4 KB each, bf16):
 //   R  (rows as lanes):  record (s, c), lane l -> row 16s + l%16, dims 32c + 8(l/16) + 0..7;
 //   TR (dims as lanes):  record mt, lane l -> dim 16mt + l%16, slot e -> row vkey(l/16, e).
+// R images are in the input type (bf16 or fp16: they meet q, k in the logits and dP
+// products), TR images always bf16 (they meet P and dS in the dq, dk, dv products).
 // Query tile (16 KB per 32 queries): [R(q)][TR(q)][R(dout)][TR(dout)].
 // Raw backward tile (8 KB per 32 keys): [R(v)][TR(k)].
 // Pooled backward tile (8 KB per 32 pooled keys): [R(Vc)][TR(Kc)], from the f32 means.
@@ -127,10 +129,12 @@ struct RecPackArgs {
   unsigned char* dst;      // tile base of head 0
   int64_t tile_bytes;      // distance between consecutive tiles of one head
   int32_t r_off, tr_off;   // byte offsets of the R and TR groups inside a tile (-1: skip)
+  int32_t half;            // 2-byte sources and R records are fp16 (else bf16); TR is bf16
 };
 
 struct BwdScalarArgs {
   int64_t T; int32_t H;
+  int32_t half;            // dout is fp16 (else bf16)
   const float* lse_cmp;    // [H][T], natural log
   const float* lse_sel;    // [H][T], base 2 (selection kernel units)
   const float* gates; int64_t gate_st;
@@ -143,6 +147,7 @@ struct BwdScalarArgs {
 struct BwdArgs {
   int64_t T, Nb, n_ctiles, n_ktiles;
   int32_t H, B;
+  int32_t half;            // q, k, v, dout and the R images are fp16 (else bf16)
   float scale;             // softmax scale
   float logit_mult;        // scale * log2(e)
   const unsigned char* pooled;      // forward pooled tiles (12 KB: K hi, K lo, V^T)

@@ -282,10 +282,11 @@ def sparse_attn_fwd_train(q, k, v, gates, block: int, topk: int, scale: float = 
 
 def sparse_attn_bwd(st: Trained, dout: torch.Tensor, workspace: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv f32 [T, H, 64], dgates f32 shaped like the gates) of the forward
-    pass recorded in `st`, for the output gradient dout (bf16 [T, H, 64])."""
-    if dout.dtype != torch.bfloat16 or tuple(dout.shape) != tuple(st.q.shape) or \
+    pass recorded in `st`, for the output gradient dout ([T, H, 64], the type of q)."""
+    if dout.dtype != st.q.dtype or tuple(dout.shape) != tuple(st.q.shape) or \
             dout.stride(2) != 1:
-        raise ValueError("dout must be bf16 [T, H, 64] with a contiguous last dimension")
+        raise ValueError("dout must have the type and shape of q ([T, H, 64]) with a "
+                         "contiguous last dimension")
     f32 = dict(dtype=torch.float32, device=st.q.device)
     dq, dk, dv = (torch.empty(st.q.shape, **f32) for _ in range(3))
     dg = torch.empty(st.gates.shape, **f32) if st.gates.dim() == 2 else \

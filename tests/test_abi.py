@@ -225,11 +225,3 @@ def test_params_layout_matches_header():
     """The ctypes mirror of s3r_params has the C layout: 96 bytes, dtype at offset 88."""
     assert ctypes.sizeof(S.Params) == 96
     assert S.Params.dtype.offset == 88 and S.Params.gate_stride_t.offset == 80
-
-
-def test_backward_rejects_fp16():
-    p = params(dtype=1)
-    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
-    assert S.lib().speed3r_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 256, 64,
-                                          ws, big, FAKE, FAKE, FAKE, FAKE, ws, big, None) \
-        == S.S3R_ERR_UNSUPPORTED

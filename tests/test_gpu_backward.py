@@ -33,6 +33,12 @@ CASES = {
     "token_gates": (_tiny_s, 700, {"token_gates": True}),
     "strided_dout": (dataclasses.replace(_tiny_s, name="b64", H=2, block=64, topk=4), 900,
                      {"strided": True}),
+    # fp16 inputs and output gradient
+    "tiny_s_fp16": (dataclasses.replace(_tiny_s, name="tiny_s_fp16", dtype="fp16"), None, {}),
+    "v3_fp16": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_fp16", dtype="fp16"), 3 * 1374,
+                {}),
+    "b128_fp16": (dataclasses.replace(_tiny_s, name="b128_fp16", H=2, block=128, topk=3,
+                                      dtype="fp16"), 1100, {}),
 }
 
 
@@ -70,9 +76,9 @@ def run_case(name):
         gates = torch.rand(T, w.H, 2, device="cuda",
                            generator=torch.Generator(device="cuda").manual_seed(5))
     gen = torch.Generator(device="cuda").manual_seed(17)
-    dout = torch.randn(T, w.H, 64, device="cuda", generator=gen).to(torch.bfloat16)
+    dout = torch.randn(T, w.H, 64, device="cuda", generator=gen).to(x["q"].dtype)
     if opt.get("strided"):
-        big = torch.zeros(T, w.H, 2, 64, dtype=torch.bfloat16, device="cuda")
+        big = torch.zeros(T, w.H, 2, 64, dtype=dout.dtype, device="cuda")
         big[:, :, 1] = dout
         dout = big[:, :, 1]
     st = S.sparse_attn_fwd_train(x["q"], x["k"], x["v"], gates, w.block, w.topk,
