@@ -63,10 +63,11 @@ def lib():
                                             _i64, _i64, _f32p, _i64, _i64, _i32, _i64, _i64,
                                             _f64p]
         L.s3r_oracle_dense_rows.restype = None
-        L.s3r_oracle_num_selected.argtypes = [_i64, _i32, _i32, _i32]
+        L.s3r_oracle_num_selected.argtypes = [_i64, _i32, _i32, _i32, _i32]
         L.s3r_oracle_num_selected.restype = _i32
         L.s3r_oracle_forward_rows.argtypes = [
-            _i64, _i32, _i32, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p, _i64, _i64, _f32p,
+            _i64, _i32, _i32, _i32, _i32, _i32, _i32, _dbl, _f32p, _i64, _i64, _f32p, _i64, _i64,
+            _f32p,
             _i64, _i64, _f64p, _f64p, _f32p, _i64, _i64, _i32p, _i64p,
             ctypes.c_void_p, _f64p, _f64p, _f32p, _i32p, _f64p, _f64p]
         L.s3r_oracle_forward_rows.restype = None
@@ -160,25 +161,27 @@ def dense_rows(q, k, v, h: int, t0: int, nt: int, scale: Optional[float] = None)
     return out
 
 
-def num_selected(T: int, B: int, topk_: int, forced: int = 0) -> int:
-    return int(lib().s3r_oracle_num_selected(T, B, topk_, forced))
+def num_selected(T: int, B: int, topk_: int, forced: int = 0, own: bool = False) -> int:
+    return int(lib().s3r_oracle_num_selected(T, B, topk_, forced, int(own)))
 
 
 def forward_rows(q, k, v, gates, B: int, topk_: int, rows_h: Sequence[int],
                  rows_i: Sequence[int], kc: Optional[np.ndarray] = None,
                  vc: Optional[np.ndarray] = None, sel_in: Optional[np.ndarray] = None,
-                 scale: Optional[float] = None, forced: int = 0) -> Dict[str, np.ndarray]:
+                 scale: Optional[float] = None, forced: int = 0,
+                 own: bool = False) -> Dict[str, np.ndarray]:
     """Whole forward pass for the listed (head, query block) rows.
 
     Returns per-row arrays: lse [R, B], ocmp [R, B, D], score [R, Nb] (float32), sel
     [R, n_sel], osel [R, B, D], out [R, B, D]; rows of a short last block are valid for their
     first n_i entries only. ``kc``/``vc`` may be passed in to reuse a pooling. ``forced``
-    blocks (the first F) are always selected and top-k runs over the rest.
+    blocks (the first F) are always selected, with ``own`` each query block's own key block
+    too, and top-k runs over the rest (rows that hold fewer blocks end with -1).
     """
     a, b, c = _f32(q), _f32(k), _f32(v)
     T, H, D = a.shape
     Nb = n_blocks(T, B)
-    k_eff = num_selected(T, B, topk_, forced)
+    k_eff = num_selected(T, B, topk_, forced, own)
     if kc is None:
         kc = pool(b, B)
     if vc is None:
@@ -198,7 +201,8 @@ def forward_rows(q, k, v, gates, B: int, topk_: int, rows_h: Sequence[int],
         sel_in = np.ascontiguousarray(np.asarray(sel_in, dtype=np.int32).reshape(R, k_eff))
         sel_ptr = sel_in.ctypes.data
     lib().s3r_oracle_forward_rows(
-        T, H, D, B, topk_, forced, default_scale(D) if scale is None else scale, a, H * D, D,
+        T, H, D, B, topk_, forced, int(own), default_scale(D) if scale is None else scale, a,
+        H * D, D,
         b, H * D,
         D, c, H * D, D, np.ascontiguousarray(kc), np.ascontiguousarray(vc), g.reshape(-1),
         gate_st, R, rh, ri, sel_ptr, res["lse"], res["ocmp"], res["score"], res["sel"],
@@ -207,7 +211,7 @@ def forward_rows(q, k, v, gates, B: int, topk_: int, rows_h: Sequence[int],
 
 
 def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = None,
-                forced: int = 0):
+                forced: int = 0, own: bool = False):
     """Forward pass over every row, reassembled into token-major tensors:
     out/ocmp/osel [T, H, D], lse [H, T], score [H, Nb, Nb] float32, sel [H, Nb, n_sel]."""
     a = _f32(q)
@@ -215,7 +219,8 @@ def forward_all(q, k, v, gates, B: int, topk_: int, scale: Optional[float] = Non
     Nb = n_blocks(T, B)
     rows_h = np.repeat(np.arange(H), Nb)
     rows_i = np.tile(np.arange(Nb), H)
-    r = forward_rows(q, k, v, gates, B, topk_, rows_h, rows_i, scale=scale, forced=forced)
+    r = forward_rows(q, k, v, gates, B, topk_, rows_h, rows_i, scale=scale, forced=forced,
+                     own=own)
     k_eff = r["sel"].shape[1]
     full = {}
     for name in ("ocmp", "osel", "out"):
@@ -277,7 +282,7 @@ def window_order(views: int, special: int, grid_h: int, grid_w: int, win_h: int,
 
 
 def forward_windows(q, k, v, gates, B: int, topk_: int, layout: Sequence[int],
-                    scale: Optional[float] = None, forced: int = 0):
+                    scale: Optional[float] = None, forced: int = 0, own: bool = False):
     """The forward pass on window-ordered tokens: reorder q, k, v (and per-token gates) by
     window_order(*layout), run forward_all, and put out/ocmp/osel back in the caller's token
     order. lse stays in the caller's order too; score and sel refer to blocks of the
@@ -288,7 +293,8 @@ def forward_windows(q, k, v, gates, B: int, topk_: int, layout: Sequence[int],
         raise ValueError("layout does not match the token count")
     g = _f32(gates)
     gp = g[order] if g.ndim == 3 else g
-    r = forward_all(a[order], b[order], c[order], gp, B, topk_, scale=scale, forced=forced)
+    r = forward_all(a[order], b[order], c[order], gp, B, topk_, scale=scale, forced=forced,
+                    own=own)
     inv = np.empty_like(order)
     inv[order] = np.arange(order.size)
     for name in ("out", "ocmp", "osel"):

@@ -30,6 +30,8 @@
  *   - optional forced blocks (the VGGT variant keeps the reference frame's tokens dense,
  *     summary "Methodologie" 3): the first F key blocks are always selected and top-k is taken
  *     over the remaining blocks, so a row holds min(F, Nb) + min(k, Nb - min(F, Nb)) blocks;
+ *     optionally each query block's own key block is always selected as well (top-k then runs
+ *     over the blocks that are neither forced nor its own);
  *   - the top-k decision is made on the scores rounded to float32 (the precision the GPU
  *     kernel decides in);
  *   - no masking (bidirectional attention).
@@ -229,12 +231,51 @@ void s3r_oracle_dense_rows(int64_t T, int32_t H, int32_t D, double scale, const 
   }
 }
 
-/* Number of selected blocks per row: the forced prefix plus top-k of the rest. */
-int32_t s3r_oracle_num_selected(int64_t T, int32_t B, int32_t topk, int32_t forced) {
+/* Length of a selection row: the forced prefix, the query block's own block when `own` asks
+ * for it (and it is not forced already), plus top-k of the rest. Rows whose own block lies in
+ * the prefix hold one block fewer and end with -1. */
+int32_t s3r_oracle_num_selected(int64_t T, int32_t B, int32_t topk, int32_t forced,
+                                int32_t own) {
   const int64_t Nb = n_blocks(T, B);
   const int64_t f = (forced < Nb) ? forced : Nb;
-  const int64_t rest = Nb - f;
-  return (int32_t)(f + ((topk < rest) ? topk : rest));
+  const int64_t o = (own && f < Nb) ? 1 : 0;
+  const int64_t rest = Nb - f - o;
+  return (int32_t)(f + o + ((topk < rest) ? topk : rest));
+}
+
+static int int32_asc_sel(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Selection row of query block i: blocks 0..f-1, then (own) block i, then the top-k of the
+ * remaining blocks by f32 score, all in ascending order, padded with -1 to n_sel. */
+static void select_row(const float* score, int64_t Nb, int64_t i, int32_t f, int32_t own,
+                       int32_t topk, int32_t n_sel, int32_t* out) {
+  int32_t n = 0;
+  for (int32_t a = 0; a < f; ++a) out[n++] = a;
+  const int own_here = own && i >= f;
+  if (own_here) out[n++] = (int32_t)i;
+  /* candidates: blocks f..Nb-1 except i */
+  float* cs = (float*)malloc(sizeof(float) * (size_t)(Nb > 0 ? Nb : 1));
+  int32_t* cj = (int32_t*)malloc(sizeof(int32_t) * (size_t)(Nb > 0 ? Nb : 1));
+  int32_t* pick = (int32_t*)malloc(sizeof(int32_t) * (size_t)(Nb > 0 ? Nb : 1));
+  int64_t nc = 0;
+  for (int64_t j = f; j < Nb; ++j) {
+    if (own_here && j == i) continue;
+    cs[nc] = score[j];
+    cj[nc] = (int32_t)j;
+    ++nc;
+  }
+  if (nc > 0) {
+    const int32_t got = s3r_oracle_topk(cs, nc, topk, pick);
+    for (int32_t a = 0; a < got; ++a) out[n++] = cj[pick[a]];
+  }
+  qsort(out, (size_t)n, sizeof(int32_t), int32_asc_sel);
+  while (n < n_sel) out[n++] = -1;
+  free(cs);
+  free(cj);
+  free(pick);
 }
 
 /* The whole forward pass for a list of (head, query block) rows, given the pooled tensors.
@@ -244,7 +285,7 @@ int32_t s3r_oracle_num_selected(int64_t T, int32_t B, int32_t topk, int32_t forc
  * If sel_in is not NULL it supplies the selected blocks ([r][n_sel]) instead of top-k.
  * Gate of (t, h, branch b) is gates[t*gate_st + h*2 + b] (gate_st = 0: per-head gates). */
 void s3r_oracle_forward_rows(int64_t T, int32_t H, int32_t D, int32_t B, int32_t topk,
-                             int32_t forced, double scale, const float* q, int64_t qst, int64_t qsh,
+                             int32_t forced, int32_t own, double scale, const float* q, int64_t qst, int64_t qsh,
                              const float* k, int64_t kst, int64_t ksh, const float* v,
                              int64_t vst, int64_t vsh, const double* kc, const double* vc,
                              const float* gates, int64_t gate_st, int64_t n_rows,
@@ -252,7 +293,7 @@ void s3r_oracle_forward_rows(int64_t T, int32_t H, int32_t D, int32_t B, int32_t
                              double* lse, double* ocmp, float* score, int32_t* sel,
                              double* osel, double* out) {
   const int64_t Nb = n_blocks(T, B);
-  const int32_t k_eff = s3r_oracle_num_selected(T, B, topk, forced);
+  const int32_t k_eff = s3r_oracle_num_selected(T, B, topk, forced, own);
   const int32_t f = (int32_t)((forced < Nb) ? forced : Nb);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
@@ -269,12 +310,7 @@ void s3r_oracle_forward_rows(int64_t T, int32_t H, int32_t D, int32_t B, int32_t
     if (sel_in) {
       memcpy(my_sel, sel_in + r * k_eff, sizeof(int32_t) * (size_t)k_eff);
     } else {
-      /* forced prefix, then top-k over blocks f..Nb-1 (indices shifted back by f) */
-      for (int32_t a = 0; a < f; ++a) my_sel[a] = a;
-      if (f < Nb) {
-        const int32_t got = s3r_oracle_topk(my_score + f, Nb - f, topk, my_sel + f);
-        for (int32_t a = 0; a < got; ++a) my_sel[f + a] += f;
-      }
+      select_row(my_score, Nb, i, f, own, topk, k_eff, my_sel);
     }
     double* my_osel = osel + r * B * D;
     s3r_oracle_sel_row(T, H, D, B, scale, q, qst, qsh, k, kst, ksh, v, vst, vsh, h, i, my_sel,

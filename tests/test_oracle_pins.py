@@ -499,3 +499,40 @@ def test_backward_invariants():
     d = dout.double().numpy()
     np.testing.assert_allclose(rt["dgates"][..., 0], (d * f["ocmp"]).sum(-1), atol=1e-11)
     np.testing.assert_allclose(rt["dgates"][..., 1], (d * f["osel"]).sum(-1), atol=1e-11)
+
+
+@pytest.mark.parametrize("forced", [0, 3])
+def test_own_block_then_topk_of_the_rest(forced):
+    """With own blocks, row i holds the forced prefix, block i, and the top-k of the other
+    blocks by (score desc, index asc) from a brute-force lexsort, ascending; rows whose own
+    block is forced hold one block fewer and end with -1."""
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=320)
+    B, k = 16, 4
+    r = O.forward_all(x["q"], x["k"], x["v"], x["gates"], B, k, forced=forced, own=True)
+    Nb = 20
+    assert r["sel"].shape[-1] == O.num_selected(320, B, k, forced, True) == forced + 1 + k
+    for h in range(w.H):
+        for i in range(Nb):
+            sc = r["score"][h, i].astype(np.float64)
+            fixed = set(range(forced)) | {i}
+            cand = [j for j in range(Nb) if j not in fixed]
+            order = sorted(cand, key=lambda j: (-sc[j], j))
+            want = sorted(fixed | set(order[:k]))
+            got = r["sel"][h, i]
+            pad = len(got) - len(want)
+            assert pad == (1 if i < forced else 0)
+            np.testing.assert_array_equal(got[:len(want)], want)
+            assert (got[len(want):] == -1).all()
+
+
+def test_own_block_with_all_blocks_is_dense():
+    """Own block plus k = Nb - 1: every block is selected, so the selection branch is dense
+    attention (SDPA); every row contains its own block."""
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w)
+    r = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 63, own=True)
+    np.testing.assert_allclose(r["osel"], sdpa(x["q"], x["k"], x["v"], 1 / 8), atol=1e-12)
+    r4 = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 4, own=True)
+    for i in range(64):
+        assert (r4["sel"][:, i] == i).any(axis=-1).all()
