@@ -120,7 +120,7 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
     t_pool = time.perf_counter() - t0
     t0 = time.perf_counter()
     r = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32), rows,
-                       kc=kc, vc=vc, forced=w.forced)
+                       kc=kc, vc=vc, forced=w.forced, own=w.own)
     t_rows = time.perf_counter() - t0
     per_row = t_rows / len(rows)
     t_full = t_order + H * (t_pool + Nb * per_row)
@@ -131,7 +131,7 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
     ref = r
     if same < 1.0:
         ref = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32),
-                             rows, kc=kc, vc=vc, sel_in=gsel, forced=w.forced)
+                             rows, kc=kc, vc=vc, sel_in=gsel, forced=w.forced, own=w.own)
     for a, i in enumerate(rows):
         nn = min(T, (i + 1) * w.block) - i * w.block
         toks = torch.from_numpy(order[i * w.block:i * w.block + nn]).to(out_gpu.device)
@@ -158,11 +158,11 @@ def time_backward(w: W.Workload, x, reps: int):
     T, H, D = x["q"].shape
     gen = torch.Generator(device=x["q"].device).manual_seed(29)
     dout = torch.randn(T, H, D, device=x["q"].device, generator=gen).to(torch.bfloat16)
-    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced)
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced, w.own)
     tws = S.alloc_workspace(S.train_workspace_size(p), x["q"].device)
     bws = S.alloc_workspace(S.bwd_workspace_size(p), x["q"].device)
     st = S.sparse_attn_fwd_train(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
-                                 forced_blocks=w.forced, workspace=tws)
+                                 forced_blocks=w.forced, force_own=w.own, workspace=tws)
     S.sparse_attn_bwd(st, dout, workspace=bws)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -170,7 +170,7 @@ def time_backward(w: W.Workload, x, reps: int):
     for _ in range(reps):
         ev[0].record()
         st = S.sparse_attn_fwd_train(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
-                                     forced_blocks=w.forced, workspace=tws)
+                                     forced_blocks=w.forced, force_own=w.own, workspace=tws)
         ev[1].record()
         S.sparse_attn_bwd(st, dout, workspace=bws)
         ev[2].record()
@@ -219,26 +219,28 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] workload {w.name}: T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}")
+    log(f"[bench] workload {w.name}: T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} "
+        f"own={w.own}")
     x = W.make_inputs(w, device=dev)
     torch.cuda.synchronize()
     T, H, D = x["q"].shape
-    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced)
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced, w.own)
     Nb = S.num_blocks(p)
     layout = w.layout()
     ws = S.alloc_workspace(S.windows_workspace_size(p, layout) if layout else
                            S.workspace_size(p), dev)
-    out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, D, dtype=x["q"].dtype, device=dev)
     sel = torch.empty(H, Nb, w.k_eff, dtype=torch.int32, device=dev)
 
     def step():
         if layout:  # 2-D windows: reorder in, forward, reorder out
             S.sparse_attn_fwd_windows(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
                                       layout, out=out, sel_idx=sel, workspace=ws,
-                                      forced_blocks=w.forced)
+                                      forced_blocks=w.forced, force_own=w.own)
         else:
             S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
-                              sel_idx=sel, workspace=ws, forced_blocks=w.forced)
+                              sel_idx=sel, workspace=ws, forced_blocks=w.forced,
+                              force_own=w.own)
 
     for _ in range(args.warmup):
         step()
@@ -259,7 +261,7 @@ def main():
     # per-kernel durations: the same kernels launched stage by stage
     del ws
     torch.cuda.empty_cache()
-    folds = w.block <= 64 and w.k_eff - min(w.forced, Nb) <= 64
+    folds = w.block <= 64 and min(w.topk, Nb - min(w.forced, Nb)) <= 64
     xs, perm_ms = x, None
     if layout:
         # window order once; the reordering (3 tensors in, 1 out) is timed on its own
@@ -277,7 +279,7 @@ def main():
         perm_ms = p0.elapsed_time(p1)
         del tmp
     st = S.Stages(xs["q"], xs["k"], xs["v"], xs["gates"], w.block, w.topk, keep_o_sel=False,
-                  keep_score=not folds, forced_blocks=w.forced)
+                  keep_score=not folds, forced_blocks=w.forced, force_own=w.own)
     st.run_pool()
     st.run_lse()
     stage_ms = timed_stages(st, max(1, min(3, args.steps)))

@@ -76,7 +76,8 @@ typedef struct {
   int64_t gate_stride_t; /* 0: gates are [H][2]; otherwise per-token gates with
                             gate(t, h, b) = gates[t * gate_stride_t + h * 2 + b] */
   int32_t dtype;        /* s3r_dtype of q, k, v and out; 0 (zero-initialised) is bf16 */
-  int32_t pad;          /* unused */
+  int32_t force_own;    /* nonzero: every query block also keeps its own key block (after the
+                           forced prefix; top-k then runs over the remaining blocks) */
 } s3r_params;
 
 /* Human-readable name of a status code (static storage). */
@@ -85,8 +86,10 @@ const char* speed3r_status_string(s3r_status s);
 /* Nb = ceil(T / B), the number of key blocks (= query blocks). -1 if p is invalid. */
 int64_t speed3r_num_blocks(const s3r_params* p);
 
-/* Entries per selection row: n_sel = F' + min(k, Nb - F') with F' = min(forced_blocks, Nb).
- * Rows hold the forced blocks 0..F'-1 followed by the chosen ones, ascending. -1 if invalid. */
+/* Entries per selection row: n_sel = F' + o + min(k, Nb - F' - o) with F' = min(forced_blocks,
+ * Nb) and o = 1 when force_own is set and F' < Nb. Rows hold the forced blocks 0..F'-1 and the
+ * chosen ones (with the query block's own block when force_own), ascending; a row whose own
+ * block is already forced holds one block fewer and ends with -1. -1 if p is invalid. */
 int64_t speed3r_num_selected(const s3r_params* p);
 
 /* Row stride (in floats) of the score matrix [H][Nb][ld]: Nb rounded up to 32. -1 if invalid. */

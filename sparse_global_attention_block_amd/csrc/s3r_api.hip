@@ -19,6 +19,8 @@ struct Dims {
   int64_t T, Nb, n_ctiles, n_ktiles, ld;
   int64_t k_eff;   // entries per selection row: forced prefix + chosen blocks (n_sel)
   int64_t forced;  // F' = min(forced_blocks, Nb)
+  int64_t topk;    // k as given
+  int32_t own;     // each query block also keeps its own block (and F' < Nb)
   int32_t H, B;
   int32_t half;    // q, k, v (and out) are fp16; else bf16
   float scale;
@@ -56,10 +58,15 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->n_ktiles = (d->T + kTileKeys - 1) / kTileKeys;
   d->ld = d->n_ctiles * kTileKeys;
   d->forced = p->forced_blocks < d->Nb ? p->forced_blocks : d->Nb;
-  const int64_t rest = d->Nb - d->forced;
-  d->k_eff = d->forced + (p->topk < rest ? p->topk : rest);
+  d->topk = p->topk;
+  d->own = (p->force_own != 0 && d->forced < d->Nb) ? 1 : 0;
+  const int64_t rest = d->Nb - d->forced - d->own;
+  d->k_eff = d->forced + d->own + (p->topk < rest ? p->topk : rest);
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)kD);
-  d->fold_topk = d->B <= 64 && d->k_eff - d->forced <= kFusedTopkMaxK;
+  // the running top-k holds one entry per lane; a row whose own block is forced chooses from
+  // one more candidate
+  const int64_t most = (p->topk < d->Nb - d->forced) ? p->topk : d->Nb - d->forced;
+  d->fold_topk = d->B <= 64 && most <= kFusedTopkMaxK;
   // the separate top-k kernel holds a score row in registers; the folded one has no limit
   if (!d->fold_topk && d->Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   return S3R_OK;
@@ -217,6 +224,8 @@ s3r_status run_forward(const s3r_params* p, const Dims& d, const Layout& L, cons
     c.sel = sel;
     c.n_sel = (int32_t)d.k_eff;
     c.forced = (int32_t)d.forced;
+    c.topk = (int32_t)d.topk;
+    c.own = d.own;
     if ((st = hip_status(launch_cmp_fused_topk(c, stream))) != S3R_OK) return st;
   } else {
     c.score = score;
@@ -224,6 +233,7 @@ s3r_status run_forward(const s3r_params* p, const Dims& d, const Layout& L, cons
     TopkArgs t;
     t.score = score; t.ld = d.ld; t.Nb = d.Nb; t.n_rows = (int64_t)d.H * d.Nb;
     t.n_sel = (int32_t)d.k_eff; t.forced = (int32_t)d.forced; t.sel = sel;
+    t.topk = (int32_t)d.topk; t.own = d.own;
     if ((st = hip_status(launch_topk(t, stream))) != S3R_OK) return st;
   }
   AttnArgs a = attn_args(p, d, q, ws + L.raw);
@@ -396,6 +406,8 @@ s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void
   a.sel = sel_idx;
   a.n_sel = (int32_t)d.k_eff;
   a.forced = (int32_t)d.forced;
+  a.topk = (int32_t)d.topk;
+  a.own = d.own;
   return hip_status(launch_cmp_fused_topk(a, stream));
 }
 
@@ -410,6 +422,7 @@ s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_id
   TopkArgs a;
   a.score = score; a.ld = d.ld; a.Nb = d.Nb; a.n_rows = (int64_t)d.H * d.Nb;
   a.n_sel = (int32_t)d.k_eff; a.forced = (int32_t)d.forced; a.sel = sel_idx;
+  a.topk = (int32_t)d.topk; a.own = d.own;
   return hip_status(launch_topk(a, stream));
 }
 

@@ -109,7 +109,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     th_v[qb] = -1.0f;
     th_j[qb] = 0x7FFFFFFF;
   }
-  const int K = a.n_sel - a.forced;  // blocks chosen per query block (after the forced prefix)
+  // blocks chosen per query block: top-k among those neither forced nor (with own blocks) the
+  // query block's own
+  auto chosen = [&](int64_t qblk, bool& own) {
+    own = a.own && qblk >= a.forced;
+    const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
+    return (int)(a.topk < nc ? a.topk : nc);
+  };
   auto better = [](float v1, int j1, float v2, int j2) {
     return v1 > v2 || (v1 == v2 && j1 < j2);
   };
@@ -251,7 +257,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
             // lanes with bit 1 clear hold the 32 distinct keys of this tile; a block can only
             // enter the list if its score is >= the current k-th score (one compare per tile)
             const int j = (int)(tau * kTileKeys) + reduced_key(lane);
-            const bool mine = ((lane & 2) == 0) && K > 0 && j >= a.forced && j < a.Nb;
+            bool own;
+            const int K = chosen(qblk, own);
+            const bool mine = ((lane & 2) == 0) && K > 0 && j >= a.forced && j < a.Nb &&
+                              !(own && j == qblk);
             uint64_t cand = __ballot(mine && tot >= th_v[qb]);
             while (cand) {  // rare after the first tiles
               const int c = __builtin_ctzll(cand);
@@ -364,10 +373,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         const int64_t qblk = (q0 + 16 * qb * kNtPerQB) / a.B;
         if (qblk < a.Nb) {
           int32_t* row = a.sel + ((int64_t)h * a.Nb + qblk) * a.n_sel;
+          bool own;
+          const int K = chosen(qblk, own);
           for (int m = lane; m < a.forced; m += 64) row[m] = m;
-          int rank = 0;
-          for (int m = 0; m < K; ++m) rank += __builtin_amdgcn_readlane(tk_j[qb], m) < tk_j[qb];
+          for (int m = a.forced + (own ? 1 : 0) + K + lane; m < a.n_sel; m += 64) row[m] = -1;
+          int rank = (own && qblk < tk_j[qb]) ? 1 : 0, own_pos = 0;
+          for (int m = 0; m < K; ++m) {
+            const int o = __builtin_amdgcn_readlane(tk_j[qb], m);
+            rank += o < tk_j[qb];
+            own_pos += o < qblk;
+          }
           if (lane < K) row[a.forced + rank] = tk_j[qb];
+          if (own && lane == 0) row[a.forced + own_pos] = (int32_t)qblk;
         }
       }
     }

@@ -40,8 +40,10 @@ struct CmpArgs {
   float* score;            // [H][Nb][ld]
   int64_t ld;
   int32_t* sel;            // running top-k output [H][Nb][n_sel] (fused selection only)
-  int32_t n_sel;           // row length: forced prefix + chosen blocks
+  int32_t n_sel;           // row length: forced prefix (+ own block) + chosen blocks
   int32_t forced;          // F': blocks 0..F'-1 always selected, top-k over the rest
+  int32_t topk;            // k (chosen per row, clamped to the candidates)
+  int32_t own;             // each query block also keeps its own block
 };
 
 struct TopkArgs {
@@ -50,8 +52,10 @@ struct TopkArgs {
   int64_t Nb;
   int64_t n_rows;          // H * Nb
   int32_t n_sel;           // row length of sel
-  int32_t forced;          // F': blocks 0..F'-1 always selected, top-(n_sel - F') of the rest
-  int32_t* sel;            // [n_rows][n_sel]
+  int32_t forced;          // F': blocks 0..F'-1 always selected
+  int32_t topk;            // k chosen among the remaining blocks (clamped)
+  int32_t own;             // row i also keeps block i (when i >= F')
+  int32_t* sel;            // [n_rows][n_sel], rows padded with -1
 };
 
 struct AttnArgs {

@@ -1,4 +1,5 @@
-// Top-k block selection per (head, query block), after an optional forced prefix of blocks.
+// Top-k block selection per (head, query block), after an optional forced prefix of blocks and
+// the query block's own block.
 //
 // Speed3R technical summary (gist.science), "Methodologie" section 1: the selection branch
 // keeps, per query block, the k key blocks with the highest compression score. This kernel
@@ -49,10 +50,14 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Nb = (int)a.Nb;
   const int F = a.forced;       // blocks 0..F-1 are selected outright
-  const int k = a.n_sel - F;    // chosen among blocks F..Nb-1
+  const int qi = (int)(row % a.Nb);
+  const bool own = a.own && qi >= F;  // the row's own block, selected outright too
+  const int ncand = Nb - F - (own ? 1 : 0);
+  const int k = a.topk < ncand ? a.topk : ncand;  // chosen among the other blocks
   int32_t* row_out = a.sel + row * a.n_sel;
   for (int j = tid; j < F; j += 256) row_out[j] = j;
-  if (k >= Nb - F) {
+  for (int j = F + (own ? 1 : 0) + k + tid; j < a.n_sel; j += 256) row_out[j] = -1;
+  if (k >= ncand) {  // every block: F..Nb-1 in order (the own block among them)
     for (int j = F + tid; j < Nb; j += 256) row_out[j] = j;
     return;
   }
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    key[e] = (j >= F && j < Nb) ? order_key(raw[e]) : 0u;
+    key[e] = (j >= F && j < Nb && !(own && j == qi)) ? order_key(raw[e]) : 0u;
     tmax = key[e] > tmax ? key[e] : tmax;
   }
   tmax_s[tid] = tmax;
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    if (j >= F && j < Nb && key[e] >= theta) {
+    if (j >= F && j < Nb && !(own && j == qi) && key[e] >= theta) {
       const int pos = atomicAdd(&s_count, 1);
       if (pos < kCap) {
         cand_key[pos] = key[e];
@@ -124,9 +129,14 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     __syncthreads();
     if (tid < C && cand_rank[tid] < k) {
       const int mi = cand_idx[tid];
-      int pos = 0;
+      int pos = (own && qi < mi) ? 1 : 0;
       for (int c = 0; c < C; ++c) pos += (cand_rank[c] < k) && (cand_idx[c] < mi);
       out[pos] = mi;
+    }
+    if (own && tid == 0) {
+      int pos = 0;
+      for (int c = 0; c < C; ++c) pos += (cand_rank[c] < k) && (cand_idx[c] < qi);
+      out[pos] = qi;
     }
     return;
   }
@@ -146,7 +156,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = e * 256 + tid;
-      local += (j >= F && j < Nb) && key[e] >= cand;
+      local += (j >= F && j < Nb && !(own && j == qi)) && key[e] >= cand;
     }
     if (block_count(local) >= k) kth = cand;
   }
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    greater += (j >= F && j < Nb) && key[e] > kth;
+    greater += (j >= F && j < Nb && !(own && j == qi)) && key[e] > kth;
   }
   const int need = k - block_count(greater);  // tied entries to keep, >= 1
   // largest J with #{ties with index < J} < need: J is the index of the last tie kept
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = e * 256 + tid;
-      local += (j >= F && j < Nb) && key[e] == kth && j < cand;
+      local += (j >= F && j < Nb && !(own && j == qi)) && key[e] == kth && j < cand;
     }
     if (block_count(local) < need) J = cand;
   }
@@ -173,7 +183,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    const bool take = (j >= F && j < Nb) && (key[e] > kth || (key[e] == kth && j <= J));
+    const bool take = ((j >= F && j < Nb && !(own && j == qi)) &&
+                       (key[e] > kth || (key[e] == kth && j <= J))) ||
+                      (own && j == qi);
     const uint64_t m = __ballot(take);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     __syncthreads();

@@ -28,7 +28,8 @@ class Params(ctypes.Structure):
         ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
         ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
         ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
-        ("gate_stride_t", ctypes.c_int64), ("dtype", ctypes.c_int32), ("pad", ctypes.c_int32),
+        ("gate_stride_t", ctypes.c_int64), ("dtype", ctypes.c_int32),
+        ("force_own", ctypes.c_int32),
     ]
 
 
@@ -137,10 +138,11 @@ def _stream():
 
 def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
                 scale: float = 0.0, gates: Optional[torch.Tensor] = None,
-                forced_blocks: int = 0) -> Params:
+                forced_blocks: int = 0, force_own: bool = False) -> Params:
     """Params for [T, H, 64] bf16 or fp16 token tensors (one type for q, k, v; any token/head
     strides, last dim contiguous). ``forced_blocks`` key blocks 0..F-1 are selected for every
-    query block on top of the top-k of the rest."""
+    query block on top of the top-k of the rest; with ``force_own`` each query block also
+    keeps its own key block."""
     T, H, D = q.shape
     for x in (q, k, v):
         if x.dtype not in _DTYPES or x.dtype != q.dtype or tuple(x.shape) != (T, H, D) or \
@@ -151,7 +153,8 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, t
     if gates is not None and gates.dim() == 3:
         gst = gates.stride(0)
     return Params(T, H, D, block, topk, float(scale), forced_blocks, q.stride(0), q.stride(1),
-                  k.stride(0), k.stride(1), v.stride(0), v.stride(1), gst, _DTYPES[q.dtype], 0)
+                  k.stride(0), k.stride(1), v.stride(0), v.stride(1), gst, _DTYPES[q.dtype],
+                  int(force_own))
 
 
 def num_blocks(p: Params) -> int:
@@ -186,10 +189,10 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0
-                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                    workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0,
+                    force_own: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Full forward pass. Returns (out [T, H, 64] in the input type, sel_idx or None)."""
-    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if workspace is None:
@@ -265,10 +268,10 @@ class Trained:
 
 
 def sparse_attn_fwd_train(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
-                          forced_blocks: int = 0, workspace: Optional[torch.Tensor] = None
-                          ) -> Trained:
+                          forced_blocks: int = 0, workspace: Optional[torch.Tensor] = None,
+                          force_own: bool = False) -> Trained:
     """Forward pass that keeps the state speed3r_sparse_attn_bwd needs."""
-    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own)
     out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     sel = torch.empty(q.shape[1], num_blocks(p), num_selected(p), dtype=torch.int32,
                       device=q.device)
@@ -329,11 +332,12 @@ def windows_workspace_size(p: Params, layout) -> int:
 def sparse_attn_fwd_windows(q, k, v, gates, block: int, topk: int, layout, scale: float = 0.0,
                             out: Optional[torch.Tensor] = None,
                             sel_idx: Optional[torch.Tensor] = None,
-                            workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0
+                            workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0,
+                            force_own: bool = False
                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward pass with 2-D windows as blocks; out in the caller's token order, sel_idx over
     blocks of the window order."""
-    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own)
     w = make_windows(layout)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
@@ -352,15 +356,18 @@ class Stages:
     o_sel [T, H, 64] f32, out (input type)."""
 
     def __init__(self, q, k, v, gates, block: int, topk_: int, scale: float = 0.0,
-                 keep_o_sel: bool = True, keep_score: bool = True, forced_blocks: int = 0):
+                 keep_o_sel: bool = True, keep_score: bool = True, forced_blocks: int = 0,
+                 force_own: bool = False):
         self.q, self.k, self.v, self.gates = q, k, v, gates
-        self.p = make_params(q, k, v, block, topk_, scale, gates, forced_blocks)
+        self.p = make_params(q, k, v, block, topk_, scale, gates, forced_blocks, force_own)
         T, H, D = q.shape
         dev = q.device
         self.Nb = num_blocks(self.p)
         self.ld = score_row_stride(self.p)
         self.k_eff = num_selected(self.p)
         self.forced = min(forced_blocks, self.Nb)
+        self.own = bool(force_own) and self.forced < self.Nb
+        self.topk = topk_
         self.ws = alloc_workspace(tiles_workspace_size(self.p), dev)
         f32 = dict(dtype=torch.float32, device=dev)
         self.k_mean = torch.empty(H, self.Nb, D, **f32)
@@ -392,7 +399,7 @@ class Stages:
 
     @property
     def folds_topk(self) -> bool:
-        return self.p.block <= 64 and self.k_eff - self.forced <= 64
+        return self.p.block <= 64 and min(self.topk, self.Nb - self.forced) <= 64
 
     def run_sel(self, sel=None, o_cmp=None):
         sel_combine(self.p, self.q, self.ws, self.sel if sel is None else sel,

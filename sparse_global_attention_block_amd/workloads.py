@@ -58,6 +58,7 @@ class Workload:
     window: Optional[Tuple[int, int]] = None  # 2-D pooling window (rows, cols): window order
     spatial: float = 0.0  # weight of the smooth 2-D position term (grid workloads only)
     dtype: str = "bf16"   # element type of q, k, v: "bf16" or "fp16"
+    own: bool = False     # each query block also keeps its own key block
 
     @property
     def T(self) -> int:
@@ -75,9 +76,10 @@ class Workload:
 
     @property
     def k_eff(self) -> int:
-        """Entries per selection row: the forced blocks plus the chosen ones."""
+        """Entries per selection row: the forced blocks (and own block) plus the chosen ones."""
         f = min(self.forced, self.n_blocks)
-        return f + min(self.topk, self.n_blocks - f)
+        o = 1 if self.own and f < self.n_blocks else 0
+        return f + o + min(self.topk, self.n_blocks - f - o)
 
     def describe(self) -> Dict:
         return {
@@ -86,6 +88,7 @@ class Workload:
             "generator": self.gen, "seed": self.seed,
             "dtype": self.dtype,
             **({"forced_blocks": self.forced} if self.forced else {}),
+            **({"own_block": True} if self.own else {}),
             **({"grid": list(self.grid)} if self.grid else {}),
             **({"window": list(self.window), "spatial": self.spatial} if self.window else {}),
             **({"iid_scale": self.iid_scale} if self.gen == "iid" else
@@ -111,6 +114,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     # by every query block in addition to its top-16
     Workload("v1000_k16_ref", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
              special_mult=3.0, forced=22),
+    # ... and each query block also attending its own key block
+    Workload("v1000_k16_ref_own", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
+             special_mult=3.0, forced=22, own=True),
     # the same in fp16 (the model runs in bf16 or fp16)
     Workload("v1000_k16_fp16", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,
              special_mult=3.0, dtype="fp16"),

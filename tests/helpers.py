@@ -35,31 +35,54 @@ def row_gaps(score_row_f32: np.ndarray, k: int) -> float:
 
 
 def check_selection(gpu_sel: np.ndarray, ora_score: np.ndarray, ora_sel: np.ndarray, k: int,
-                    forced: int = 0):
-    """Index parity: every row starts with the forced blocks 0..forced-1; of the k chosen
-    after them, rows whose oracle gap (over blocks >= forced) exceeds GAP must match exactly;
-    on the other rows every GPU-chosen block must score within GAP of the oracle's k-th score.
-    Returns the fraction of rows held to the exact rule and the list of differing rows."""
+                    forced: int = 0, qblocks=None):
+    """Index parity. Every row starts with the forced blocks 0..forced-1; with `qblocks` (the
+    query block of each row: own blocks on) a row whose query block is past the prefix also
+    holds that block. The k (at most the candidates left) chosen among the other blocks follow,
+    sorted together with the own block, then -1 padding. Of the chosen, rows whose oracle gap
+    over the candidates exceeds GAP must match exactly; on the other rows every GPU-chosen
+    block must score within GAP of the oracle's k-th score. Returns the fraction of rows held
+    to the exact rule and the list of differing rows."""
     rows = gpu_sel.reshape(-1, gpu_sel.shape[-1])
     osel = ora_sel.reshape(-1, ora_sel.shape[-1])
     osc = ora_score.reshape(-1, ora_score.shape[-1])
-    assert rows.shape[1] == forced + k == osel.shape[1]
+    own = None if qblocks is None else np.asarray(qblocks).reshape(-1)
+    assert rows.shape == osel.shape
+    Nb = osc.shape[1]
     exact, differing = 0, []
     for r in range(rows.shape[0]):
-        np.testing.assert_array_equal(rows[r][:forced], np.arange(forced), err_msg=f"row {r}")
-        got, want, free = rows[r][forced:], osel[r][forced:], osc[r][forced:]
-        gap = row_gaps(free, k) if k > 0 else math.inf
+        row, orow = rows[r], osel[r]
+        np.testing.assert_array_equal(row[:forced], np.arange(forced), err_msg=f"row {r}")
+        n = int((row >= 0).sum())
+        assert (row[:n] >= 0).all() and (row[n:] == -1).all(), f"row {r}: bad padding {row}"
+        assert n == int((orow >= 0).sum()), f"row {r}: {n} entries, oracle {orow}"
+        got, want = row[forced:n], orow[forced:n]
+        cand = np.ones(Nb, bool)
+        cand[:forced] = False
+        if own is not None and own[r] >= forced:
+            i = int(own[r])
+            assert i in got, f"row {r}: own block {i} missing from {row}"
+            got, want, cand[i] = got[got != i], want[want != i], False
+        kr = min(k, int(cand.sum()))
+        assert len(got) == kr, f"row {r}: {len(got)} chosen blocks, expected {kr}"
+        free = osc[r][cand]
+        gap = row_gaps(free, kr) if kr > 0 else math.inf
         same = np.array_equal(got, want)
         if gap > GAP:
             exact += 1
-            assert same, f"row {r}: gap {gap:.3e} > {GAP} but GPU {rows[r]} != oracle {osel[r]}"
+            assert same, f"row {r}: gap {gap:.3e} > {GAP} but GPU {row} != oracle {orow}"
         elif not same:
-            kth = -np.sort(-free.astype(np.float64))[k - 1]
-            assert (got >= forced).all(), f"row {r}: a forced block was chosen twice"
+            kth = -np.sort(-free.astype(np.float64))[kr - 1]
+            assert cand[got].all(), f"row {r}: a forced or own block was chosen twice"
             assert (osc[r][got] >= kth - GAP).all(), f"row {r}: GPU picked a far block"
             assert np.array_equal(np.sort(got), got) and len(set(got)) == len(got)
             differing.append(r)
     return exact / max(1, rows.shape[0]), differing
+
+
+def own_rows(H: int, Nb: int, own: bool):
+    """Query block of each row of an [H, Nb, n_sel] selection when own blocks are on."""
+    return np.tile(np.arange(Nb), H) if own else None
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:

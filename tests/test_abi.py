@@ -38,10 +38,10 @@ def test_status_strings():
     assert S.status_string(99) == "S3R_ERR_UNKNOWN"
 
 
-def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0, dtype=0):
+def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0, dtype=0, own=0):
     st = st or (H * D, D)
     return S.Params(T, H, D, B, k, scale, forced, st[0], st[1], st[0], st[1], st[0], st[1], 0,
-                    dtype, 0)
+                    dtype, own)
 
 
 def test_size_queries():
@@ -104,6 +104,15 @@ def test_bad_params_rejected_everywhere(kw, code):
 def test_num_selected_counts_forced_prefix(T, B, k, F, n_sel):
     """Rows hold F' = min(F, Nb) forced blocks and min(k, Nb - F') chosen ones."""
     assert S.num_selected(params(T=T, B=B, k=k, forced=F)) == n_sel
+
+
+@pytest.mark.parametrize("T,B,k,F,n_sel", [
+    (1024, 16, 8, 0, 9), (1024, 16, 8, 3, 12), (1024, 16, 100, 0, 64), (1024, 16, 8, 64, 64),
+    (40, 16, 8, 1, 3), (1, 64, 16, 0, 1),
+])
+def test_num_selected_with_own_block(T, B, k, F, n_sel):
+    """With own blocks a row holds F' + 1 + min(k, Nb - F' - 1) entries (F' < Nb)."""
+    assert S.num_selected(params(T=T, B=B, k=k, forced=F, own=1)) == n_sel
 
 
 def test_null_and_misaligned_pointers():
@@ -225,3 +234,4 @@ def test_params_layout_matches_header():
     """The ctypes mirror of s3r_params has the C layout: 96 bytes, dtype at offset 88."""
     assert ctypes.sizeof(S.Params) == 96
     assert S.Params.dtype.offset == 88 and S.Params.gate_stride_t.offset == 80
+    assert S.Params.force_own.offset == 92

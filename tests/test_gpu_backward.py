@@ -13,7 +13,7 @@ import torch
 from oracle import oracle as O
 from sparse_global_attention_block_amd import speed3r as S
 from sparse_global_attention_block_amd import workloads as W
-from tests.helpers import check_selection, cuda_inputs, host
+from tests.helpers import check_selection, cuda_inputs, host, own_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,11 @@ CASES = {
                 {}),
     "b128_fp16": (dataclasses.replace(_tiny_s, name="b128_fp16", H=2, block=128, topk=3,
                                       dtype="fp16"), 1100, {}),
+    # own blocks after a prefix: rows of the prefix end in -1
+    "v3_ref_own": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_ref_own", forced=22,
+                                       own=True), 3 * 1374, {}),
+    "tiny_f3_own": (dataclasses.replace(W.WORKLOADS["tiny"], name="tiny_f3_own", forced=3,
+                                        own=True), None, {}),
 }
 
 
@@ -67,8 +72,8 @@ def check_dgates(name, gpu, ref, dout, ora_f):
 
 def run_case(name):
     w, T, opt = CASES[name]
-    print(f"[bwd {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} {opt}",
-          flush=True)
+    print(f"[bwd {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} own={w.own} "
+          f"{w.dtype} {opt}", flush=True)
     x = cuda_inputs(w, T=T)
     T = x["q"].shape[0]
     gates = x["gates"]
@@ -82,15 +87,18 @@ def run_case(name):
         big[:, :, 1] = dout
         dout = big[:, :, 1]
     st = S.sparse_attn_fwd_train(x["q"], x["k"], x["v"], gates, w.block, w.topk,
-                                 forced_blocks=w.forced)
+                                 forced_blocks=w.forced, force_own=w.own)
     dq, dk, dv, dg = S.sparse_attn_bwd(st, dout)
     torch.cuda.synchronize()
     hx = {n: host(t) for n, t in x.items()}
     hg = host(gates)
-    ora_f = O.forward_all(hx["q"], hx["k"], hx["v"], hg, w.block, w.topk, forced=w.forced)
+    ora_f = O.forward_all(hx["q"], hx["k"], hx["v"], hg, w.block, w.topk, forced=w.forced,
+                          own=w.own)
     gsel = host(st.sel).numpy()
-    F = min(w.forced, gsel.shape[1])
-    check_selection(gsel, ora_f["score"], ora_f["sel"], gsel.shape[-1] - F, forced=F)
+    Nb = gsel.shape[1]
+    F = min(w.forced, Nb)
+    check_selection(gsel, ora_f["score"], ora_f["sel"], w.topk, forced=F,
+                    qblocks=own_rows(w.H, Nb, w.own and F < Nb))
     ref = O.backward(hx["q"], hx["k"], hx["v"], hg, host(dout), w.block, gsel)
     ref["forward"] = ora_f
     ref["dout"] = host(dout)

@@ -24,15 +24,16 @@ def sample_rows(w: W.Workload, n_random: int, seed: int):
 
 
 @pytest.mark.parametrize("name", ["v32", "v100", "v1000_k16", "v1000_k32", "v1000_k16_ref",
-                                  "v1000_k16_fp16"])
+                                  "v1000_k16_ref_own", "v1000_k16_fp16"])
 def test_fullsize_sampled_rows(name):
     w = W.WORKLOADS[name]
-    print(f"[fullsize {name}] T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}", flush=True)
+    print(f"[fullsize {name}] T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} own={w.own}",
+          flush=True)
     x = cuda_inputs(w)
     Nb, k_eff = w.n_blocks, w.k_eff
     sel = torch.empty(w.H, Nb, k_eff, dtype=torch.int32, device="cuda")
     out, _ = S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, sel_idx=sel,
-                               forced_blocks=w.forced)
+                               forced_blocks=w.forced, force_own=w.own)
     torch.cuda.synchronize()
     rows = sample_rows(w, 3, w.seed)
     heads = [0, w.H - 1]
@@ -42,14 +43,15 @@ def test_fullsize_sampled_rows(name):
         kc, vc = O.pool(hk, w.block), O.pool(hv, w.block)
         zeros = np.zeros(len(rows), np.int32)
         ora = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, zeros, rows, kc=kc, vc=vc,
-                             forced=w.forced)
+                             forced=w.forced, own=w.own)
         gsel = sel[h, rows].cpu().numpy()
         F = min(w.forced, Nb)
-        frac, differing = check_selection(gsel, ora["score"], ora["sel"], k_eff - F, forced=F)
+        frac, differing = check_selection(gsel, ora["score"], ora["sel"], w.topk, forced=F,
+                                          qblocks=rows if w.own and F < Nb else None)
         ref = ora
         if differing:
             ref = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, zeros, rows, kc=kc, vc=vc,
-                                 sel_in=gsel, forced=w.forced)
+                                 sel_in=gsel, forced=w.forced, own=w.own)
         for a, i in enumerate(rows):
             n = min(w.T, (i + 1) * w.block) - i * w.block
             check_out(out[i * w.block:i * w.block + n, h], ref["out"][a, :n],

@@ -9,7 +9,7 @@ import torch
 from oracle import oracle as O
 from sparse_global_attention_block_amd import speed3r as S
 from sparse_global_attention_block_amd import workloads as W
-from tests.helpers import check_out, check_selection, cuda_inputs, host
+from tests.helpers import check_out, check_selection, cuda_inputs, host, own_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,19 @@ CASES = {
     "v3_fp16": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_fp16", dtype="fp16"), 3 * 1374),
     "b128_fp16": (dataclasses.replace(_tiny_s, name="b128_fp16", H=2, block=128, topk=3,
                                       dtype="fp16"), 1100),
+    # each query block also keeps its own key block: alone, after a prefix (rows of the prefix
+    # keep one entry less and end in -1), with B = 128, and with every block kept
+    "tiny_s_own": (dataclasses.replace(_tiny_s, name="tiny_s_own", own=True), None),
+    "v3_ref_own": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_ref_own", forced=22,
+                                       own=True), 3 * 1374),
+    "tiny_f3_own": (dataclasses.replace(W.WORKLOADS["tiny"], name="tiny_f3_own", forced=3,
+                                        own=True), None),
+    "b128_own": (dataclasses.replace(_tiny_s, name="b128_own", H=2, block=128, topk=3,
+                                     forced=1, own=True), 1100),
+    "tiny_all_own": (dataclasses.replace(W.WORKLOADS["tiny_all"], name="tiny_all_own",
+                                         forced=2, own=True), None),
+    "forced_all_own": (dataclasses.replace(_tiny_s, name="forced_all_own", H=2, block=32,
+                                           topk=5, forced=100, own=True), 1000),
 }
 
 _cache = {}
@@ -46,14 +59,15 @@ def run_case(name):
     if name in _cache:
         return _cache[name]
     w, T = CASES[name]
-    print(f"[case {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}", flush=True)
+    print(f"[case {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} "
+          f"own={w.own} {w.dtype}", flush=True)
     x = cuda_inputs(w, T=T)
     st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
-                  forced_blocks=w.forced).run_all()
+                  forced_blocks=w.forced, force_own=w.own).run_all()
     torch.cuda.synchronize()
     hx = {n: host(t) for n, t in x.items()}
     ora = O.forward_all(hx["q"], hx["k"], hx["v"], hx["gates"], w.block, w.topk,
-                        forced=w.forced)
+                        forced=w.forced, own=w.own)
     ora["k_mean"] = O.pool(hx["k"], w.block)
     ora["v_mean"] = O.pool(hx["v"], w.block)
     _cache[name] = (w, x, hx, st, ora)
@@ -104,16 +118,22 @@ def test_cmp_output_and_scores(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_topk_bit_exact_on_gpu_scores(name):
     """Integer stage: on identical f32 score rows the GPU's choice must equal the oracle's
-    (forced prefix, then top-k of the remaining blocks) on every row."""
+    (forced prefix, the own block, top-k of the remaining blocks, -1 padding) on every row."""
     w, x, hx, st, ora = run_case(name)
     sc = host(st.score).numpy()[:, :, :st.Nb]
     got = host(st.sel).numpy()
     F = st.forced
     for h in range(sc.shape[0]):
         for i in range(sc.shape[1]):
-            want = np.arange(F, dtype=np.int32)
-            if F < st.Nb:
-                want = np.concatenate([want, F + O.topk(sc[h, i, F:], w.topk)])
+            keep = list(range(F))
+            cand = np.arange(F, st.Nb)
+            if st.own and i >= F:
+                keep.append(i)
+                cand = cand[cand != i]
+            if len(cand):
+                keep += list(cand[O.topk(sc[h, i, cand], w.topk)])
+            want = np.full(st.k_eff, -1, np.int32)
+            want[:len(keep)] = np.sort(keep)
             np.testing.assert_array_equal(got[h, i], want, err_msg=f"row h={h} i={i}")
 
 
@@ -158,10 +178,10 @@ def test_topk_ties_and_fallback():
 @pytest.mark.parametrize("name", list(CASES))
 def test_selection_indices(name):
     w, x, hx, st, ora = run_case(name)
-    frac, diff = check_selection(host(st.sel).numpy(), ora["score"], ora["sel"],
-                                 st.k_eff - st.forced, forced=st.forced)
+    frac, diff = check_selection(host(st.sel).numpy(), ora["score"], ora["sel"], w.topk,
+                                 forced=st.forced, qblocks=own_rows(w.H, st.Nb, st.own))
     print(f"[{name}] rows held to exact index parity: {frac:.1%}, near-tie rows differing: {len(diff)}")
-    if name in ("tiny_s", "v3_ragged", "tiny_s_ref", "v3_ref"):
+    if name in ("tiny_s", "v3_ragged", "tiny_s_ref", "v3_ref", "tiny_s_own", "v3_ref_own"):
         assert frac > 0.5
 
 
@@ -188,7 +208,7 @@ def test_end_to_end(name):
     k_eff = st.k_eff
     sel = torch.empty(w.H, Nb, k_eff, dtype=torch.int32, device="cuda")
     out, _ = S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, sel_idx=sel,
-                               forced_blocks=w.forced)
+                               forced_blocks=w.forced, force_own=w.own)
     torch.cuda.synchronize()
     gsel = host(sel).numpy()
     ref = ora["out"]
@@ -196,7 +216,7 @@ def test_end_to_end(name):
         rows_h = np.repeat(np.arange(w.H), Nb)
         rows_i = np.tile(np.arange(Nb), w.H)
         r = O.forward_rows(hx["q"], hx["k"], hx["v"], hx["gates"], w.block, w.topk, rows_h,
-                           rows_i, sel_in=gsel.reshape(-1, k_eff), forced=w.forced)
+                           rows_i, sel_in=gsel.reshape(-1, k_eff), forced=w.forced, own=w.own)
         T = x["q"].shape[0]
         ref = np.ascontiguousarray(r["out"].reshape(w.H, Nb * w.block, 64)[:, :T]
                                    .transpose(1, 0, 2))

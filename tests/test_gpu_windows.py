@@ -9,7 +9,7 @@ import torch
 from oracle import oracle as O
 from sparse_global_attention_block_amd import speed3r as S
 from sparse_global_attention_block_amd import workloads as W
-from tests.helpers import check_out, check_selection, cuda_inputs, host
+from tests.helpers import check_out, check_selection, cuda_inputs, host, own_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,8 @@ CASES = {
     "win8_b64": (dataclasses.replace(_w8, views=3), {}),
     # the same with the first view's 25 windows forced
     "win8_forced": (dataclasses.replace(_w8, views=3, forced=25), {}),
+    # ... and each window block also keeping itself
+    "win8_forced_own": (dataclasses.replace(_w8, views=3, forced=25, own=True), {}),
     # 4x4 windows grouped four to a block of 64 (4x16 strips), per-token gates, no specials
     "win4_b64_strips": (dataclasses.replace(_w4, views=2, special=0, tokens_per_view=36 * 36,
                                             block=64, topk=4, H=2), {"token_gates": True}),
@@ -50,40 +52,41 @@ def test_window_permute_byte_exact(layout):
 def run_case(name):
     w, opt = CASES[name]
     layout = w.layout()
-    print(f"[case {name}] layout {layout} T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced}",
-          flush=True)
+    print(f"[case {name}] layout {layout} T={w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} "
+          f"own={w.own}", flush=True)
     x = cuda_inputs(w)
     gates = x["gates"]
     if opt.get("token_gates"):
         gates = torch.rand(w.T, w.H, 2, device="cuda",
                            generator=torch.Generator(device="cuda").manual_seed(3))
-    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, gates, w.forced)
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, gates, w.forced, w.own)
     sel = torch.empty(w.H, S.num_blocks(p), S.num_selected(p), dtype=torch.int32, device="cuda")
     out, _ = S.sparse_attn_fwd_windows(x["q"], x["k"], x["v"], gates, w.block, w.topk, layout,
-                                       sel_idx=sel, forced_blocks=w.forced)
+                                       sel_idx=sel, forced_blocks=w.forced, force_own=w.own)
     torch.cuda.synchronize()
     hx = {n: host(t) for n, t in x.items()}
     hg = host(gates)
     ora = O.forward_windows(hx["q"], hx["k"], hx["v"], hg, w.block, w.topk, layout,
-                            forced=w.forced)
+                            forced=w.forced, own=w.own)
     return w, layout, x, hx, hg, out, host(sel).numpy(), ora
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_windowed_forward_against_oracle(name):
     w, layout, x, hx, hg, out, gsel, ora = run_case(name)
-    F = min(w.forced, gsel.shape[1])
-    frac, diff = check_selection(gsel, ora["score"], ora["sel"], gsel.shape[-1] - F, forced=F)
+    H, Nb = gsel.shape[:2]
+    F = min(w.forced, Nb)
+    frac, diff = check_selection(gsel, ora["score"], ora["sel"], w.topk, forced=F,
+                                 qblocks=own_rows(H, Nb, w.own and F < Nb))
     print(f"[{name}] exact-index rows {frac:.1%}, near-tie rows differing {len(diff)}")
     ref = ora["out"]
     if not np.array_equal(gsel, ora["sel"]):
         # rows where a near-tie flipped the set: the oracle on the GPU's own indices
         order = ora["order"]
         gp = hg[order] if hg.dim() == 3 else hg
-        H, Nb = gsel.shape[:2]
         r = O.forward_rows(hx["q"][order], hx["k"][order], hx["v"][order], gp, w.block, w.topk,
                            np.repeat(np.arange(H), Nb), np.tile(np.arange(Nb), H),
-                           sel_in=gsel.reshape(H * Nb, -1), forced=w.forced)
+                           sel_in=gsel.reshape(H * Nb, -1), forced=w.forced, own=w.own)
         T = x["q"].shape[0]
         perm_out = r["out"].reshape(H, Nb * w.block, 64)[:, :T].transpose(1, 0, 2)
         ref = np.empty_like(perm_out)
