@@ -10,45 +10,92 @@
 // Both kernels share one tile step: S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (lane l holds
 // query l%16, keys 4*(l/16)+r), base-2 online softmax with a per-query offset shared by the
 // four lanes that hold a query, and O^T += V^T . P^T in fp16 with P taken straight from the
-// S^T registers. The offset only moves when a logit exceeds it by more than 2^8 (checked with one
-// max per element), which happens on the first tile and rarely afterwards.
+// S^T registers. The offset only moves when a logit exceeds it by more than 8 (base 2), i.e. a
+// weight exceeds 2^8, which happens on the first tile and rarely afterwards.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
 namespace s3r {
 
-constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the offset must move
+// The offset of a query only moves once one of its weights exceeds 2^8 (8 in base 2 of
+// headroom above the offset); the weights of a tile are never more than 2^8 in fp16.
+constexpr uint32_t kWeightLimitF32 = 0x43800000u;  // f32 bits of 2^8
 
 template <int NT, bool kHalf = false>
 struct Flash {
   float m[NT];          // per-query offset (base 2), identical in the 4 lanes of a query
-  floatx4 l[NT];        // sum over keys of the bf16-rounded weights (all 4 entries equal)
+  float nm[NT];         // -m, or 0 while m = -inf (weights then come out 0 or get rescaled)
+  floatx4 l[NT];        // sum over keys of the fp16-rounded weights (all 4 entries equal)
   floatx4 o[4][NT];     // O^T accumulators: dims 16*mt + 4g + r, query 16*nt + l%16
+  bool fresh;           // some query has no offset yet (before the first tile)
 
   __device__ void init() {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       m[nt] = -INFINITY;
+      nm[nt] = 0.f;
       l[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) o[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    fresh = true;
   }
 
-  // One tile of 32 keys. rec[0..3] = K records (bf16), rec[4..7] = V^T records (fp16), this
-  // lane's 16 bytes of each. Keys outside [lo, hi) of the tile are masked. The softmax denominator is a
-  // ones-row MFMA over the same bf16 weights that multiply V, so numerator and denominator
-  // see identical rounding.
-  __device__ void step(const bf16x8 (&rec)[8], const bf16x8 (&qb)[NT][2], int lo, int hi,
-                       float mult, int g) {
-    floatx4 acc[2][NT];
+  // S^T = K . Q^T of one tile of 32 keys (unscaled logits); k = the tile's four K records
+  // (this lane's 16 bytes of each).
+  __device__ static void logits(const bf16x8* k, const bf16x8 (&qb)[NT][2], floatx4 (&acc)[2][NT]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        floatx4 x = mfma_in<kHalf>(rec[2 * s2], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
-        acc[s2][nt] = mfma_in<kHalf>(rec[2 * s2 + 1], qb[nt][1], x);
+        floatx4 x = mfma_in<kHalf>(k[2 * s2], qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        acc[s2][nt] = mfma_in<kHalf>(k[2 * s2 + 1], qb[nt][1], x);
       }
+  }
+
+  // fp16 weights exp2(logit * mult - m) of column tile nt, packed as its P.V operand; big is
+  // set if one of them exceeds the headroom (weights are >= 0, so their f32 bit patterns order
+  // like the numbers: an integer max, which needs no NaN handling)
+  __device__ halfx8 weights(const floatx4 (&acc)[2][NT], int nt, float mult, bool& big) const {
+    float p[2][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[s2][r] = fast_exp2(fmaf(acc[s2][nt][r], mult, nm[nt]));
+    uint32_t b = __float_as_uint(p[0][0]);
+#pragma unroll
+    for (int e = 1; e < 8; ++e) b = max(b, __float_as_uint(p[e >> 2][e & 3]));
+    big = b > kWeightLimitF32;
+    return pack8h(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]);
+  }
+
+  // Moves the offset of the queries of column tile nt to their running maximum (rare: the
+  // first tile, and when a logit exceeds the offset by more than the headroom) and rescales
+  // their sums.
+  __device__ void rescale(const floatx4 (&acc)[2][NT], int nt, float mult) {
+    float M = acc[0][nt][0];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) M = fmaxf(M, acc[s2][nt][r]);
+    M *= mult;
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    if (M > m[nt]) {
+      const float f = (m[nt] == -INFINITY) ? 0.f : fast_exp2(m[nt] - M);
+      l[nt] *= f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) o[mt][nt] *= f;
+      m[nt] = M;
+      nm[nt] = -M;
+    }
+  }
+
+  // Online-softmax update with one tile: acc = its logits (masked here to keys [lo, hi) of the
+  // tile), v = its four V^T records (fp16). The softmax denominator is a ones-row MFMA over the
+  // same fp16 weights that multiply V, so numerator and denominator see identical rounding.
+  __device__ void update(floatx4 (&acc)[2][NT], const bf16x8* v, int lo, int hi, float mult,
+                         int g) {
     if (lo > 0 || hi < kTileKeys) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
@@ -61,50 +108,34 @@ struct Flash {
           }
         }
     }
-    bool need = false;
-    float mx[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float v = acc[0][nt][0];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v = fmaxf(v, acc[s2][nt][r]);
-      mx[nt] = v * mult;
-      need |= mx[nt] > m[nt] + kRescaleSlack;
-    }
-    if (__builtin_expect(__any(need), 0)) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float M = mx[nt];
-        M = fmaxf(M, __shfl_xor(M, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        if (M > m[nt]) {
-          const float f = (m[nt] == -INFINITY) ? 0.f : fast_exp2(m[nt] - M);
-          l[nt] *= f;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) o[mt][nt] *= f;
-          m[nt] = M;
-        }
-      }
-    }
     const halfx8 ones = pack8h(1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      // a query whose every key so far is masked keeps m = -inf: use 0 so that p = 0
-      const float mm = (m[nt] == -INFINITY) ? 0.f : m[nt];
-      float p[2][4];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[s2][r] = fast_exp2(fmaf(acc[s2][nt][r], mult, -mm));
-      const halfx8 pb = pack8h(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2],
-                               p[1][3]);
+      bool big;
+      halfx8 pb = weights(acc, nt, mult, big);
+      if (__builtin_expect(__any(big) || fresh, 0)) {
+        rescale(acc, nt, mult);
+        pb = weights(acc, nt, mult, big);
+      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        o[mt][nt] = mfma16h(__builtin_bit_cast(halfx8, rec[4 + mt]), pb, o[mt][nt]);
+        o[mt][nt] = mfma16h(__builtin_bit_cast(halfx8, v[mt]), pb, o[mt][nt]);
       l[nt] = mfma16h(ones, pb, l[nt]);
     }
+    if (__builtin_expect(fresh, 0)) {
+      bool unset = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) unset |= m[nt] == -INFINITY;
+      fresh = __any(unset);
+    }
+  }
+
+  // One tile: rec[0..3] = K records (bf16), rec[4..7] = V^T records (fp16).
+  __device__ void step(const bf16x8 (&rec)[8], const bf16x8 (&qb)[NT][2], int lo, int hi,
+                       float mult, int g) {
+    floatx4 acc[2][NT];
+    logits(rec, qb, acc);
+    update(acc, rec + 4, lo, hi, mult, g);
   }
 
   // 1 / softmax denominator per query, 0 for an empty softmax
@@ -136,20 +167,40 @@ __device__ __forceinline__ void load_tile(const unsigned char* base, int lane, b
 
 // ---------------------------------------------------------------------------------------
 // Selection branch. One wave per (head, query block) (two waves for B = 128, 64 queries
-// each). The wave walks the tiles of its selected blocks in list order, loading each tile's
-// 8 operand records straight from the packed raw tiles in global memory (one coalesced 1 KB
-// read per record) while it computes on the previous tile.
+// each). The wave walks the tiles of its selected blocks in list order. The tiles are
+// gathered from all over the key sequence, so each costs a full memory latency: the wave
+// keeps two tiles in flight, copied from global memory straight into two LDS slots of its own
+// (no registers held while in flight), and computes on a third, read from its slot into
+// registers just before the slot is refilled.
 // ---------------------------------------------------------------------------------------
+// Walks a selection row block by block and tile by tile. The row is held 64 entries at a time
+// in one register (lane l: entry base + l) and read with readlane, so that walking it issues
+// no memory access (a vector load inside the tile loop would make the compiler wait for every
+// tile copy in flight); only rows longer than 64 entries reload it, once per 64 entries.
 struct SelIter {
   int idx;          // position in the selection row
+  int base;         // first entry held in chunk
+  int32_t chunk;    // lane l: row[base + l] (-1 past the end)
   int64_t prev;     // last block taken
   int64_t tile, tile_end;
   int64_t blk_lo, blk_hi;  // token range of the current block
 };
 
-__device__ __forceinline__ bool sel_next_block(const AttnArgs& a, const int32_t* row, SelIter& it) {
+__device__ __forceinline__ int32_t sel_chunk(const AttnArgs& a, const int32_t* row, int base,
+                                             int lane) {
+  return (base + lane < a.k_eff) ? row[base + lane] : -1;
+}
+
+__device__ __forceinline__ bool sel_next_block(const AttnArgs& a, const int32_t* row, int lane,
+                                               SelIter& it) {
   while (it.idx < a.k_eff) {
-    const int64_t j = row[it.idx++];
+    if (it.idx >= it.base + 64) {
+      it.base += 64;
+      it.chunk = sel_chunk(a, row, it.base, lane);
+      wait_vmem<0>();  // here, so that the common path below carries no pending load
+    }
+    const int64_t j = __builtin_amdgcn_readlane(it.chunk, it.idx - it.base);
+    ++it.idx;
     if (j < 0 || j >= a.Nb || j == it.prev) continue;
     it.prev = j;
     it.blk_lo = j * a.B;
@@ -161,17 +212,23 @@ __device__ __forceinline__ bool sel_next_block(const AttnArgs& a, const int32_t*
   return false;
 }
 
-__device__ __forceinline__ bool sel_advance(const AttnArgs& a, const int32_t* row, SelIter& it) {
+__device__ __forceinline__ bool sel_advance(const AttnArgs& a, const int32_t* row, int lane,
+                                            SelIter& it) {
   if (it.tile + 1 < it.tile_end) {
     ++it.tile;
     return true;
   }
-  return sel_next_block(a, row, it);
+  return sel_next_block(a, row, lane, it);
 }
+
+constexpr int kSelSlots = 2;  // tiles in flight per wave (the vmcnt waits below assume 2)
 
 template <int NT, bool kHalf>
 __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ uint4 ring[4][kSelSlots][kRawTileBytes / 16];  // 16 KB per wave
+  // wave-uniform as far as the compiler can see, so that the selection row is read with scalar
+  // loads (a vector load would make the compiler wait for every copy in flight)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
   const int parts = (a.B > 64) ? a.B / 64 : 1;
   const int64_t n_items = (int64_t)a.H * a.Nb * parts;
@@ -190,28 +247,73 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   const int32_t* row = a.sel + ((int64_t)h * a.Nb + i) * a.k_eff;
   const unsigned char* tiles = a.tiles + (int64_t)h * a.n_tiles * kRawTileBytes;
 
+  // O_cmp of this wave's queries for the gated epilogue, copied into the wave's (then idle)
+  // LDS slots while the last tile is computed: copy x = nt*4 + mt, lane li + 16g fetches query
+  // 16nt + li, dims 16mt + 4g..+3, so the epilogue's read of (nt, mt) is one contiguous,
+  // conflict-free 1 KB record. Rows past the end read the last row (not used).
+  uint4* const cmp_lds = ring[wave][0];
+  auto fetch_ocmp = [&](int64_t first) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      int64_t t = first + 16 * nt + li;
+      t = t < a.T ? t : a.T - 1;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        __builtin_amdgcn_global_load_lds(a.o_cmp + (t * a.H + h) * kD + 16 * mt + 4 * g,
+                                         cmp_lds + 64 * (nt * 4 + mt), 16, 0, 0);
+    }
+  };
+  static_assert(NT * 4 * 1024 <= kSelSlots * kRawTileBytes, "O_cmp fits the wave's slots");
+
   Flash<NT, kHalf> f;
   f.init();
-  SelIter it{0, -1, 0, 0, 0, 0};
-  bool valid = sel_next_block(a, row, it);
-  bf16x8 cur[8];
-  if (valid) load_tile(tiles + it.tile * kRawTileBytes, lane, cur);
-  while (valid) {
-    const int64_t t0 = it.tile * kTileKeys;
-    const int lo = (int)((it.blk_lo > t0) ? it.blk_lo - t0 : 0);
-    const int hi = (int)((it.blk_hi < t0 + kTileKeys) ? it.blk_hi - t0 : kTileKeys);
-    SelIter nx = it;
-    const bool nvalid = sel_advance(a, row, nx);
-    bf16x8 nxt[8];
-    if (nvalid) load_tile(tiles + nx.tile * kRawTileBytes, lane, nxt);
-    f.step(cur, qb, lo, hi, a.logit_mult, g);
-    if (nvalid) {
+  // cons: the tile being computed; prod: the next tile to request (kSelSlots ahead)
+  SelIter cons{0, 0, sel_chunk(a, row, 0, lane), -1, 0, 0, 0, 0};
+  bool cvalid = sel_next_block(a, row, lane, cons);
+  SelIter prod = cons;
+  bool pvalid = cvalid;
+  int issued = 0;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) cur[x] = nxt[x];
+  for (int s = 0; s < kSelSlots; ++s) {
+    if (pvalid) {
+      tile_to_lds(tiles + prod.tile * kRawTileBytes, ring[wave][s], lane);
+      ++issued;
+      pvalid = sel_advance(a, row, lane, prod);
     }
-    it = nx;
-    valid = nvalid;
   }
+  if (!cvalid) fetch_ocmp(q0);
+  for (int t = 0; cvalid; ++t) {
+    const int slot = t % kSelSlots;
+    // tile t has landed once at most the copies issued after it are pending
+    if (issued > t + 1) wait_vmem<8>();
+    else wait_vmem<0>();
+    bf16x8 cur[8];
+    const bf16x8* L = reinterpret_cast<const bf16x8*>(ring[wave][slot]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) cur[x] = L[x * 64 + lane];
+    SelIter nx = cons;
+    const bool nvalid = sel_advance(a, row, lane, nx);
+    if (pvalid) {
+      wait_lds();  // the slot is read before the next tile overwrites it
+      tile_to_lds(tiles + prod.tile * kRawTileBytes, ring[wave][slot], lane);
+      ++issued;
+      pvalid = sel_advance(a, row, lane, prod);
+    } else if (!nvalid) {
+      wait_lds();  // last tile: both slots are free once it is read
+      // (the opaque copy of q0 keeps the compiler from hoisting the copy's 16 addresses out
+      // of the loop, where they would hold registers for the whole loop)
+      int64_t qq = q0;
+      asm volatile("" : "+s"(qq));
+      fetch_ocmp(qq);
+    }
+    const int64_t t0 = cons.tile * kTileKeys;
+    const int lo = (int)((cons.blk_lo > t0) ? cons.blk_lo - t0 : 0);
+    const int hi = (int)((cons.blk_hi < t0 + kTileKeys) ? cons.blk_hi - t0 : kTileKeys);
+    f.step(cur, qb, lo, hi, a.logit_mult, g);
+    cons = nx;
+    cvalid = nvalid;
+  }
+  wait_vmem<0>();  // O_cmp has landed
 
   float inv[NT];
   f.finish(inv);
@@ -227,7 +329,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int64_t base = (t * a.H + h) * kD + 16 * mt + 4 * g;
-      const float4 oc = *reinterpret_cast<const float4*>(a.o_cmp + base);
+      const float4 oc = __builtin_bit_cast(float4, cmp_lds[64 * (nt * 4 + mt) + lane]);
       const float s0 = f.o[mt][nt][0] * inv[nt], s1 = f.o[mt][nt][1] * inv[nt];
       const float s2 = f.o[mt][nt][2] * inv[nt], s3 = f.o[mt][nt][3] * inv[nt];
       if (a.o_sel) *reinterpret_cast<float4*>(a.o_sel + base) = make_float4(s0, s1, s2, s3);

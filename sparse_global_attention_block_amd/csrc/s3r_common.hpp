@@ -189,8 +189,6 @@ __device__ __forceinline__ int reduced_key(int lane) {
   return 16 * ((i >> 3) & 1) + 4 * g + 2 * ((i >> 2) & 1) + (i & 1);
 }
 
-// Work-group id remapped so that consecutive logical ids share an XCD: the dispatcher hands
-// work-groups to the 8 XCDs round-robin, so logical id x*per + s runs on XCD x.
 // Work-group barrier that orders LDS only: waits for this wave's LDS operations, not for its
 // global loads, so a prefetch for a later step stays in flight across it (__syncthreads
 // waits for every outstanding memory operation).
@@ -200,6 +198,32 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Waits on one counter of this wave (s_waitcnt, gfx9 field layout: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8; a field at its maximum does not wait). The empty asm keeps
+// the compiler from moving memory accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {  // at most N vector-memory operations pending
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds() {  // every LDS (and scalar-memory) operation done
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
+}
+
+// One packed tile (8 records of 1 KB) copied from global memory straight into LDS, without
+// passing through registers: record x of lane l (16 bytes) lands at dst[64 x + l]. dst must
+// be the same for every lane of the wave. Completion counts on vmcnt, 8 operations per tile;
+// the data may be read only after wait_vmem() has covered them.
+__device__ __forceinline__ void tile_to_lds(const unsigned char* src, uint4* dst, int lane) {
+#pragma unroll
+  for (int x = 0; x < kRawTileBytes / kRecBytes; ++x)
+    __builtin_amdgcn_global_load_lds(src + x * kRecBytes + 16 * lane, dst + 64 * x, 16, 0, 0);
+}
+
+// Work-group id remapped so that consecutive logical ids share an XCD: the dispatcher hands
+// work-groups to the 8 XCDs round-robin, so logical id x*per + s runs on XCD x.
 __device__ __forceinline__ int64_t xcd_logical_id(int64_t b, int64_t total) {
   const int64_t per = (total + 7) / 8;
   return (b % 8) * per + b / 8;
