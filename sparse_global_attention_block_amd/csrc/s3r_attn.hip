@@ -259,8 +259,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
       t = t < a.T ? t : a.T - 1;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        __builtin_amdgcn_global_load_lds(a.o_cmp + (t * a.H + h) * kD + 16 * mt + 4 * g,
-                                         cmp_lds + 64 * (nt * 4 + mt), 16, 0, 0);
+        copy16_to_lds(a.o_cmp + (t * a.H + h) * kD + 16 * mt + 4 * g, cmp_lds + 64 * (nt * 4 + mt));
     }
   };
   static_assert(NT * 4 * 1024 <= kSelSlots * kRawTileBytes, "O_cmp fits the wave's slots");

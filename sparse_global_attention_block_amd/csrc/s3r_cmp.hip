@@ -19,12 +19,11 @@
 // (-running offset in pass 1, -L_t*log2(e) in pass 2) is the MFMA's C input, leaving one exp2
 // per logit on the VALU.
 //
-// Optional software pipeline (kPipe): while the VALU works on the probabilities of tile t,
-// the logits of tile t+1 are already computed on the matrix cores (two accumulator sets), and
-// tile t+2 is on its way from memory. Measured on MI355X it loses to the unpipelined loop for
-// both passes: the second accumulator set pushes pass 2 to ~254 VGPRs and forces its offset
-// out of the MFMA C operand onto the VALU, while two resident waves per SIMD already overlap
-// one wave's VALU work with the other's MFMAs. Both passes therefore launch unpipelined.
+// Tiles reach LDS by direct global->LDS copies (each wave copies its share of the records),
+// kAhead tiles ahead of the one being computed, so no registers are held for tiles in flight.
+// A software pipeline inside one wave (logits of tile t+1 on the matrix cores while the VALU
+// works on tile t) was measured slower on MI355X: its second accumulator set costs occupancy,
+// and the resident waves of a SIMD already overlap one wave's VALU work with another's MFMAs.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
@@ -32,29 +31,27 @@ namespace s3r {
 
 constexpr int kLseWaves = 4;
 constexpr int kFusedWaves = 4;
+constexpr int kLseAhead = 1;    // tiles in flight, pass 1
+constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 
 // kQB: query blocks per wave (64 / B for B <= 64, else 1; B = 128 blocks span two waves and
 // their scores are completed with a second atomic add onto a zeroed matrix).
-// kPipe: overlap the logits of tile t+1 with the probabilities of tile t inside one wave
-// (two accumulator sets, 3-slot ring); without it the kernel needs fewer registers and relies
-// on more resident waves per SIMD for the same overlap.
 // kTopk (pass 2, B <= 64, k <= 64): instead of writing the score matrix, each wave keeps the
 // running top-k of its query block(s) in registers, one entry per lane, and writes the chosen
 // indices at the end. The entries are ordered by (score desc, block index asc), a total order,
 // so the final set does not depend on the order in which blocks arrive, and the decision is
 // made on exactly the f32 column sums the score matrix would have held.
-template <bool kFused, int kQB, int kWaves, bool kPipe, bool kTopk = false, bool kHalf = false>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void cmp_kernel(CmpArgs a) {
-  constexpr int kRing = kPipe ? 3 : 2;
-  constexpr int kThreads = 64 * kWaves;
+template <bool kFused, int kQB, int kWaves, bool kTopk = false, bool kHalf = false>
+// (second bound: resident waves per SIMD the register allocation must allow)
+__global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArgs a) {
+  constexpr int kAhead = kFused ? kFusedAhead : kLseAhead;  // tiles in flight
+  constexpr int kRing = kAhead + 1;
   constexpr int kQueries = 64 * kWaves;
-  constexpr int kTileU4 = (kFused ? 12 : 8) * kRecBytes / 16;  // bytes of a tile this pass reads
-  constexpr int kLoads = kTileU4 / kThreads;
-  static_assert(kLoads * kThreads == kTileU4 && kLoads <= 3, "whole staging registers");
-  constexpr int kTileStrideU4 = kPooledTileBytes / 16;
+  constexpr int kRecs = kFused ? 12 : 8;  // records of a tile this pass reads
+  constexpr int kRecsPerWave = kRecs / kWaves;
+  static_assert(kRecsPerWave * kWaves == kRecs, "each wave copies whole records");
   constexpr int kNtPerQB = 4 / kQB;
-  constexpr bool kOffsetOnValu = kFused && kPipe;
-  __shared__ uint4 lds[kRing][kTileU4];
+  __shared__ uint4 lds[kRing][kRecs * 64];
 
   const int64_t n_qtiles = (a.T + kQueries - 1) / kQueries;
   const int64_t total = (int64_t)a.H * n_qtiles;
@@ -62,7 +59,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   if (logical >= total) return;
   const int h = (int)(logical / n_qtiles);
   const int64_t qt = logical % n_qtiles;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
   const int64_t q0 = qt * kQueries + wave * 64;
   const int64_t n = a.n_tiles;
@@ -85,8 +82,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 
   // Per-lane softmax state. Pass 1: running offset m (base 2) and partial sum l of this lane's
   // keys; pass 2: the fixed offset L_t*log2(e) (+inf for a query past the end: P = 0).
+  // Pass 1 holds -offset as the first MFMA's C operand; pass 2 subtracts it on the VALU, which
+  // saves the 16 registers of that operand (pass 2 is register-bound).
   float off[4], lsum[4];
-  floatx4 cneg[4];
+  floatx4 cneg[kFused ? 1 : 4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t t = q0 + 16 * nt + li;
@@ -94,9 +93,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       off[nt] = (t < a.T) ? a.lse_in[(int64_t)h * a.T + t] * kLog2e : INFINITY;
     } else {
       off[nt] = 0.f;
+      cneg[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     lsum[nt] = 0.f;
-    cneg[nt] = floatx4{-off[nt], -off[nt], -off[nt], -off[nt]};
   }
   // running top-k: lane e holds entry e (score, block index) of each query block's list;
   // th_v / th_j mirror entry K-1 (the current k-th best) in scalar registers
@@ -128,19 +127,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int nt = 0; nt < 4; ++nt) o[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint4* tiles = reinterpret_cast<const uint4*>(a.tiles) + (int64_t)h * n * kTileStrideU4;
-  // Staging registers of one tile (named, not an array, so that they stay in VGPRs).
-  uint4 s0 = make_uint4(0, 0, 0, 0), s1 = s0, s2 = s0;
-  auto fetch = [&](int64_t t) {
-    const uint4* src = tiles + t * kTileStrideU4;
-    s0 = src[tid];
-    if constexpr (kLoads > 1) s1 = src[kThreads + tid];
-    if constexpr (kLoads > 2) s2 = src[2 * kThreads + tid];
-  };
-  auto stash = [&](int slot) {
-    lds[slot][tid] = s0;
-    if constexpr (kLoads > 1) lds[slot][kThreads + tid] = s1;
-    if constexpr (kLoads > 2) lds[slot][2 * kThreads + tid] = s2;
+  const unsigned char* tiles = a.tiles + (int64_t)h * n * kPooledTileBytes;
+  // this wave's share of tile t into ring slot `slot` (kRecsPerWave vector-memory operations)
+  auto copy = [&](int64_t t, int slot) {
+#pragma unroll
+    for (int r = 0; r < kRecsPerWave; ++r) {
+      const int rec = wave * kRecsPerWave + r;
+      copy16_to_lds(tiles + t * kPooledTileBytes + rec * kRecBytes + 16 * lane,
+                    &lds[slot][rec * 64]);
+    }
   };
 
   // S^T of one tile: keys (16 per half s2) x queries (16 per column tile nt), offset applied.
@@ -156,7 +151,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         // the pipelined pass 2 subtracts its fixed offset on the VALU (its second accumulator
         // set leaves no room to hold the offset as a C operand across tiles)
         floatx4 x = mfma_in<kHalf>(h0, qb[nt][0],
-                                   kOffsetOnValu ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[nt]);
+                                   kFused ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[kFused ? 0 : nt]);
         x = mfma_in<kHalf>(h1, qb[nt][1], x);
         x = mfma_in<kHalf>(l0, qb[nt][0], x);
         acc[s2][nt] = mfma_in<kHalf>(l1, qb[nt][1], x);
@@ -212,7 +207,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
                 for (int r = 0; r < 4; ++r) s += fast_exp2(acc[s2][nt][r] - mx);
               lsum[nt] = prev[nt] * fast_exp2(-mx) + s;
               off[nt] += mx;
-              cneg[nt] = floatx4{-off[nt], -off[nt], -off[nt], -off[nt]};
+              cneg[kFused ? 0 : nt] = floatx4{-off[nt], -off[nt], -off[nt], -off[nt]};
             }
           }
         }
@@ -226,7 +221,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            p[s2][nt][r] = fast_exp2(kOffsetOnValu ? acc[s2][nt][r] - off[nt] : acc[s2][nt][r]);
+            p[s2][nt][r] = fast_exp2(acc[s2][nt][r] - off[nt]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
@@ -297,55 +292,30 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     }
   };
 
-  // One pipeline step (t < n - 1): fetch tile t+2, logits of tile t+1, probabilities of
-  // tile t. Branch-free, so the matrix-core work of t+1 and the VALU work of t share one
-  // basic block and interleave. The last tile is peeled off (it alone needs key masking).
-  auto body = [&](int64_t tau, floatx4 (&cur)[2][4], floatx4 (&nxt)[2][4]) {
-    fetch((tau + 2 < n) ? tau + 2 : n - 1);
-    // keep the prefetch at the top of the step: its latency hides behind the whole step
-    __builtin_amdgcn_sched_barrier(0);
-    qk(lds[(int)((tau + 1) % kRing)], nxt);
-    process(tau, lds[(int)(tau % kRing)], cur, false);
-    stash((int)((tau + 2) % kRing));
-    __syncthreads();
-  };
-
-  if constexpr (kPipe) {
-    fetch(0);
-    stash(0);
-    fetch(n > 1 ? 1 : 0);
-    stash(1);
-    __syncthreads();
-    floatx4 accA[2][4], accB[2][4];
-    qk(lds[0], accA);
-    int64_t tau = 0;
-    for (; tau + 2 < n; tau += 2) {
-      body(tau, accA, accB);
-      body(tau + 1, accB, accA);
-    }
-    if (tau + 1 < n) {  // two tiles left: tau, tau + 1
-      body(tau, accA, accB);
-      process(tau + 1, lds[(int)((tau + 1) % kRing)], accB, true);
-    } else {            // one tile left
-      process(tau, lds[(int)(tau % kRing)], accA, true);
-    }
-  } else {
-    // one tile per step: fetch t+1, logits and probabilities of t, 2-slot ring
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    floatx4 acc[2][4];
-    for (int64_t tau = 0; tau + 1 < n; ++tau) {
-      fetch(tau + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      qk(lds[(int)(tau & 1)], acc);
-      process(tau, lds[(int)(tau & 1)], acc, false);
-      stash((int)((tau + 1) & 1));
-      __syncthreads();
-    }
-    qk(lds[(int)((n - 1) & 1)], acc);
-    process(n - 1, lds[(int)((n - 1) & 1)], acc, true);
+  // Ring of kRing slots, kAhead tiles in flight. Every step requests one tile (the last one
+  // again once the sequence is exhausted) so that "tile t+1 has landed" is always "at most
+  // (kAhead - 1) * kRecsPerWave copies of this wave pending"; the barrier then publishes
+  // every wave's share. Slot (t + kAhead) % kRing was last read in step t - 1, before the
+  // barrier that ended it.
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) copy(s < n ? s : n - 1, s);
+  wait_vmem<(kAhead - 1) * kRecsPerWave>();
+  lds_barrier();
+  floatx4 acc[2][4];
+  for (int64_t tau = 0; tau + 1 < n; ++tau) {
+    copy(tau + kAhead < n ? tau + kAhead : n - 1, (int)((tau + kAhead) % kRing));
+    const uint4* L = lds[(int)(tau % kRing)];
+    qk(L, acc);
+    process(tau, L, acc, false);
+    wait_vmem<(kAhead - 1) * kRecsPerWave>();
+    lds_barrier();
   }
+  {
+    const uint4* L = lds[(int)((n - 1) % kRing)];
+    qk(L, acc);
+    process(n - 1, L, acc, true);
+  }
+  wait_vmem<0>();  // no copy outlives the work-group
 
   if constexpr (!kFused) {
     // combine the four lane groups of each query: offsets and partial sums
@@ -414,19 +384,19 @@ static hipError_t launch_cmp_t(const CmpArgs& a, hipStream_t s, bool fused, bool
     const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
     if (topk) {
       switch (a.B) {
-        case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, true, kHalf>), g3, b3, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, true, kHalf>), g3, b3, 0, s, a); break;
-        default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, true, kHalf>), g3, b3, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, kHalf>), g3, b3, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, kHalf>), g3, b3, 0, s, a); break;
+        default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, kHalf>), g3, b3, 0, s, a); break;
       }
     } else {
       switch (a.B) {
-        case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, false, kHalf>), g3, b3, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, false, kHalf>), g3, b3, 0, s, a); break;
-        default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, false, kHalf>), g3, b3, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, false, kHalf>), g3, b3, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, false, kHalf>), g3, b3, 0, s, a); break;
+        default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, false, kHalf>), g3, b3, 0, s, a); break;
       }
     }
   } else {
-    hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false, false, kHalf>), cmp_grid(a, kLseWaves),
+    hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false, kHalf>), cmp_grid(a, kLseWaves),
                        dim3(64 * kLseWaves), 0, s, a);
   }
   return hipGetLastError();

@@ -212,6 +212,14 @@ __device__ __forceinline__ void wait_lds() {  // every LDS (and scalar-memory) o
   asm volatile("" ::: "memory");
 }
 
+// Direct global->LDS copy of 16 bytes per lane: lane l's 16 bytes at src land at dst + 16 l
+// (dst the same for every lane of the wave). Counts on vmcnt like a load. (Kept out of line of
+// kernel templates: there the host pass of hipcc rejects the builtin and silently drops the
+// kernel's launch stub.)
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 // One packed tile (8 records of 1 KB) copied from global memory straight into LDS, without
 // passing through registers: record x of lane l (16 bytes) lands at dst[64 x + l]. dst must
 // be the same for every lane of the wave. Completion counts on vmcnt, 8 operations per tile;
@@ -219,7 +227,7 @@ __device__ __forceinline__ void wait_lds() {  // every LDS (and scalar-memory) o
 __device__ __forceinline__ void tile_to_lds(const unsigned char* src, uint4* dst, int lane) {
 #pragma unroll
   for (int x = 0; x < kRawTileBytes / kRecBytes; ++x)
-    __builtin_amdgcn_global_load_lds(src + x * kRecBytes + 16 * lane, dst + 64 * x, 16, 0, 0);
+    copy16_to_lds(src + x * kRecBytes + 16 * lane, dst + 64 * x);
 }
 
 // Work-group id remapped so that consecutive logical ids share an XCD: the dispatcher hands
