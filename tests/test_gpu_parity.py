@@ -50,6 +50,8 @@ CASES = {
                                          forced=2, own=True), None),
     "forced_all_own": (dataclasses.replace(_tiny_s, name="forced_all_own", H=2, block=32,
                                            topk=5, forced=100, own=True), 1000),
+    "v3_own_fp16": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_own_fp16", own=True,
+                                        dtype="fp16"), 3 * 1374),
 }
 
 _cache = {}

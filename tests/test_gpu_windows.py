@@ -24,6 +24,8 @@ CASES = {
     "win8_forced": (dataclasses.replace(_w8, views=3, forced=25), {}),
     # ... and each window block also keeping itself
     "win8_forced_own": (dataclasses.replace(_w8, views=3, forced=25, own=True), {}),
+    # fp16 inputs and output
+    "win8_fp16": (dataclasses.replace(_w8, views=3, dtype="fp16"), {}),
     # 4x4 windows grouped four to a block of 64 (4x16 strips), per-token gates, no specials
     "win4_b64_strips": (dataclasses.replace(_w4, views=2, special=0, tokens_per_view=36 * 36,
                                             block=64, topk=4, H=2), {"token_gates": True}),
