@@ -8,22 +8,22 @@
 //   pass 1 (cmp_lse):   L_t = log sum_j exp(c_tj)
 //   pass 2 (cmp_fused): P_tj = exp(c_tj - L_t), O_cmp_t = sum_j P_tj Vc_j,
 //                       Score[i][j] = sum_{t in block i} P_tj
-// with c_tj = scale * q_t . Kc_j. Both passes are MFMA-bound (16x16x32, f32 accumulate).
+// with c_tj = scale * q_t . Kc_j, on 16x16x32 MFMAs with f32 accumulation.
 //
 // Work decomposition: a work-group of 4 waves owns 256 consecutive queries of one head; each
 // wave holds 64 queries (4 column tiles of 16) as resident B operands and streams the pooled
-// tiles (32 coarse tokens each) through a 3-slot LDS ring. The accumulator tile is S^T (keys x
+// tiles (32 coarse tokens each) through a 2-slot LDS ring. The accumulator tile is S^T (keys x
 // queries): lane l holds query l%16 and keys 4*(l/16)+r, so P feeds the P.V MFMA directly as
 // its B operand (in fp16, against fp16 pooled values). The pooled keys arrive pre-multiplied
-// by scale*log2(e) as bf16 hi + lo, so logits come out in base-2 units; the query's offset
-// (-running offset in pass 1, -L_t*log2(e) in pass 2) is the MFMA's C input, leaving one exp2
-// per logit on the VALU.
+// by scale*log2(e) as bf16 hi + lo, so logits come out in base-2 units. The query's offset is
+// the first MFMA's C input in pass 1 (the running offset) and one VALU subtraction per logit in
+// pass 2 (-L_t*log2(e)): pass 2 is register-bound, and the 16 registers of that operand decide
+// between two and three resident waves per SIMD.
 //
 // Tiles reach LDS by direct global->LDS copies (each wave copies its share of the records),
 // kAhead tiles ahead of the one being computed, so no registers are held for tiles in flight.
 // A software pipeline inside one wave (logits of tile t+1 on the matrix cores while the VALU
-// works on tile t) was measured slower on MI355X: its second accumulator set costs occupancy,
-// and the resident waves of a SIMD already overlap one wave's VALU work with another's MFMAs.
+// works on tile t) was measured slower on MI355X: its second accumulator set costs occupancy.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
@@ -148,8 +148,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 1) * 64 + lane]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        // the pipelined pass 2 subtracts its fixed offset on the VALU (its second accumulator
-        // set leaves no room to hold the offset as a C operand across tiles)
+        // pass 2 subtracts its fixed offset on the VALU instead (registers)
         floatx4 x = mfma_in<kHalf>(h0, qb[nt][0],
                                    kFused ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[kFused ? 0 : nt]);
         x = mfma_in<kHalf>(h1, qb[nt][1], x);
