@@ -235,3 +235,34 @@ def test_params_layout_matches_header():
     assert ctypes.sizeof(S.Params) == 96
     assert S.Params.dtype.offset == 88 and S.Params.gate_stride_t.offset == 80
     assert S.Params.force_own.offset == 92
+
+
+def test_training_entry_points_validate_before_launching():
+    """The training forward and the backward reject bad parameters, null or misaligned
+    pointers, bad dout strides and short workspaces on the host (no launch, no GPU needed)."""
+    L = S.lib()
+    p = params()
+    tw, bw = S.lib().speed3r_train_workspace_size(ctypes.byref(p)), \
+        S.lib().speed3r_bwd_workspace_size(ctypes.byref(p))
+    assert tw > S.workspace_size(p) > 0 and bw > 0
+    ws = ctypes.c_void_p(1 << 20)
+    fwd = lambda pp, q=FAKE, w=ws, n=tw: L.speed3r_sparse_attn_fwd_train(  # noqa: E731
+        ctypes.byref(pp), q, FAKE, FAKE, FAKE, FAKE, None, w, ctypes.c_size_t(n), None)
+    assert fwd(params(D=32)) == S.S3R_ERR_UNSUPPORTED
+    assert fwd(params(k=0)) == S.S3R_ERR_INVALID_ARG
+    assert fwd(p, q=None) == S.S3R_ERR_INVALID_ARG
+    assert fwd(p, n=tw - 1) == S.S3R_ERR_WORKSPACE
+    assert fwd(p, w=None) == S.S3R_ERR_WORKSPACE
+
+    def bwd(pp, dout=FAKE, st=(4 * 64, 64), train=tw, w=ws, n=bw, dq=FAKE):
+        return L.speed3r_sparse_attn_bwd(ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, dout,
+                                         ctypes.c_int64(st[0]), ctypes.c_int64(st[1]), ws,
+                                         ctypes.c_size_t(train), dq, FAKE, FAKE, FAKE, w,
+                                         ctypes.c_size_t(n), None)
+    assert bwd(params(B=48)) == S.S3R_ERR_UNSUPPORTED
+    assert bwd(p, dout=None) == S.S3R_ERR_INVALID_ARG
+    assert bwd(p, dq=None) == S.S3R_ERR_INVALID_ARG
+    assert bwd(p, dout=ctypes.c_void_p((1 << 20) + 2)) == S.S3R_ERR_INVALID_ARG
+    assert bwd(p, st=(4 * 64 + 4, 64)) == S.S3R_ERR_INVALID_ARG  # stride not a multiple of 8
+    assert bwd(p, train=tw - 1) == S.S3R_ERR_WORKSPACE
+    assert bwd(p, n=bw - 1) == S.S3R_ERR_WORKSPACE
