@@ -11,7 +11,9 @@ using namespace s3r;
 
 namespace {
 
-constexpr int64_t kMaxBlocks = 96 * 256;  // top-k holds a row of up to 96 keys per thread
+// Longest score row the separate top-k path takes: the score matrix is H * Nb^2 floats
+// (38.7 GB at H = 16, Nb = 24576), and the exact tie search of the top-k kernel indexes up to 2^16.
+constexpr int64_t kMaxBlocks = 96 * 256;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -6,17 +6,18 @@
 // makes that choice exactly and deterministically: order by (score descending, block index
 // ascending), output the k indices in ascending order.
 //
-// One work-group (4 waves) per score row; the row (up to 96 entries per thread) is held in
-// registers as order-preserving 32-bit keys, so the row is read from HBM once.
-//  1. Each thread's maximum key; theta = the k-th largest of those 256 maxima (bitwise search
-//     in one wave). The k largest thread maxima are k distinct entries >= theta, so every entry
-//     of the true top-k is >= theta.
-//  2. Entries >= theta (usually a few dozen) are compacted into LDS. Each candidate's rank is
-//     its number of better candidates; rank < k selects it, and its output slot is the number
-//     of selected candidates with a smaller index.
+// One work-group (4 waves) per score row. The row is streamed once with 16-byte loads and no
+// part of it is held in registers (so many rows are in flight per CU); in step 2 only the few
+// threads whose maximum reaches theta read their entries again.
+//  1. Each thread's maximum key over its entries (order-preserving 32-bit keys); theta = the
+//     k-th largest of those 256 maxima (bitwise search in one wave). The k largest thread
+//     maxima are k distinct entries >= theta, so every entry of the true top-k is >= theta.
+//  2. Entries >= theta (usually a few dozen) are compacted into LDS. Each
+//     candidate's rank is its number of better candidates; rank < k selects it, and its
+//     output slot is the number of selected candidates with a smaller index.
 //  3. If more than kCap candidates survive (heavy ties), an exact fallback finds the k-th key
-//     and the cut inside the tied keys by bitwise search over all entries, then writes the
-//     selected indices in ascending order with block-wide prefix counts.
+//     and the cut inside the tied keys by bitwise search over all entries (re-reading the
+//     row), then writes the selected indices in ascending order with block-wide prefix counts.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
@@ -36,7 +37,6 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-template <int E>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t tmax_s[256];
   __shared__ uint32_t cand_key[kCap];
@@ -63,22 +63,26 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   }
   int32_t* out = row_out + F;
   const float* src = a.score + row * a.ld;
+  auto candidate = [&](int j) { return j >= F && j < Nb && !(own && j == qi); };
+  auto key_of = [&](float f, int j) { return candidate(j) ? order_key(f) : 0u; };
+  // Thread tid owns entries 1024c + 4tid .. +3 of chunk c. The row stride is a multiple of 32
+  // floats, so a 16-byte load starting below Nb stays inside the row; chunks past the end
+  // re-read the row's first entries (their keys are masked).
+  const int nchunks = (Nb + 1023) / 1024;
+  auto load4 = [&](int c, int& j0) {
+    j0 = c * 1024 + 4 * tid;
+    return *reinterpret_cast<const float4*>(src + (j0 < Nb ? j0 : 0));
+  };
 
-  // All E loads are issued before any is used: the index is clamped instead of branched on,
-  // so no load waits behind a bounds check.
-  float raw[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = e * 256 + tid;
-    raw[e] = src[j < Nb ? j : Nb - 1];
-  }
-  uint32_t key[E];
+  // 1. thread maxima, theta
   uint32_t tmax = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = e * 256 + tid;
-    key[e] = (j >= F && j < Nb && !(own && j == qi)) ? order_key(raw[e]) : 0u;
-    tmax = key[e] > tmax ? key[e] : tmax;
+#pragma unroll 4
+  for (int c = 0; c < nchunks; ++c) {
+    int j0;
+    const float4 v = load4(c, j0);
+    const uint32_t m01 = max(key_of(v.x, j0), key_of(v.y, j0 + 1));
+    const uint32_t m23 = max(key_of(v.z, j0 + 2), key_of(v.w, j0 + 3));
+    tmax = max(tmax, max(m01, m23));
   }
   tmax_s[tid] = tmax;
   if (tid == 0) s_count = 0;
@@ -101,14 +105,23 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __syncthreads();
   const uint32_t theta = s_theta;
 
+  // 2. candidates >= theta: only a thread whose maximum reaches theta can hold one, so only
+  //    those threads (typically k or a few more of the 256) read their entries again
+  if (tmax >= theta)
+#pragma unroll 4
+  for (int c = 0; c < nchunks; ++c) {
+    int j0;
+    const float4 v = load4(c, j0);
+    const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = e * 256 + tid;
-    if (j >= F && j < Nb && !(own && j == qi) && key[e] >= theta) {
-      const int pos = atomicAdd(&s_count, 1);
-      if (pos < kCap) {
-        cand_key[pos] = key[e];
-        cand_idx[pos] = j;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t key = order_key(f[i]);
+      if (candidate(j0 + i) && key >= theta) {
+        const int pos = atomicAdd(&s_count, 1);
+        if (pos < kCap) {
+          cand_key[pos] = key;
+          cand_idx[pos] = j0 + i;
+        }
       }
     }
   }
@@ -141,7 +154,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     return;
   }
 
-  // ---- exact fallback: k-th key by bitwise search over all entries ------------------------
+  // ---- 3. exact fallback: k-th key by bitwise search over all entries ---------------------
+  // (one entry per thread per step of 256: j = 256e + tid, the row re-read each time)
   auto block_count = [&](int local) -> int {
     const int w = wave_sum(local);
     __syncthreads();
@@ -149,43 +163,37 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     __syncthreads();
     return part[0] + part[1] + part[2] + part[3];
   };
+  const int E = (Nb + 255) / 256;
+  auto key_e = [&](int e) {  // 0 for entries that are not candidates
+    const int j = e * 256 + tid;
+    return j < Nb ? key_of(src[j], j) : 0u;
+  };
   uint32_t kth = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = kth | (1u << b);
     int local = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = e * 256 + tid;
-      local += (j >= F && j < Nb && !(own && j == qi)) && key[e] >= cand;
-    }
+    for (int e = 0; e < E; ++e) local += key_e(e) >= cand;
     if (block_count(local) >= k) kth = cand;
   }
   int greater = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = e * 256 + tid;
-    greater += (j >= F && j < Nb && !(own && j == qi)) && key[e] > kth;
-  }
+  for (int e = 0; e < E; ++e) greater += key_e(e) > kth;
   const int need = k - block_count(greater);  // tied entries to keep, >= 1
   // largest J with #{ties with index < J} < need: J is the index of the last tie kept
   int J = 0;
   for (int b = 15; b >= 0; --b) {
     const int cand = J | (1 << b);
     int local = 0;
-#pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = e * 256 + tid;
-      local += (j >= F && j < Nb && !(own && j == qi)) && key[e] == kth && j < cand;
+      local += candidate(j) && key_e(e) == kth && j < cand;
     }
     if (block_count(local) < need) J = cand;
   }
   int base = 0;
-#pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = e * 256 + tid;
-    const bool take = ((j >= F && j < Nb && !(own && j == qi)) &&
-                       (key[e] > kth || (key[e] == kth && j <= J))) ||
-                      (own && j == qi);
+    const uint32_t key = key_e(e);
+    const bool take = (candidate(j) && (key > kth || (key == kth && j <= J))) || (own && j == qi);
     const uint64_t m = __ballot(take);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     __syncthreads();
@@ -199,16 +207,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  const dim3 g3((unsigned)a.n_rows), b3(256);
-  const int64_t per = (a.Nb + 255) / 256;
-  if (per <= 1) hipLaunchKernelGGL((topk_kernel<1>), g3, b3, 0, s, a);
-  else if (per <= 2) hipLaunchKernelGGL((topk_kernel<2>), g3, b3, 0, s, a);
-  else if (per <= 4) hipLaunchKernelGGL((topk_kernel<4>), g3, b3, 0, s, a);
-  else if (per <= 8) hipLaunchKernelGGL((topk_kernel<8>), g3, b3, 0, s, a);
-  else if (per <= 16) hipLaunchKernelGGL((topk_kernel<16>), g3, b3, 0, s, a);
-  else if (per <= 32) hipLaunchKernelGGL((topk_kernel<32>), g3, b3, 0, s, a);
-  else if (per <= 64) hipLaunchKernelGGL((topk_kernel<64>), g3, b3, 0, s, a);
-  else hipLaunchKernelGGL((topk_kernel<96>), g3, b3, 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.n_rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
