@@ -304,6 +304,32 @@ def main():
             ach = wk["flops"] / (ms_k * 1e-3)
             kernels[name] = {"ms": ms_k, "bound": "mfma", "achieved": ach / 1e12,
                              "unit": "TFLOP/s", "frac": ach / PEAK_BF16}
+    if folds and not layout:
+        # the separate top-k kernel (the path for B = 128 or more than 64 chosen blocks) on this
+        # workload's score matrix: reported beside the step, not part of it
+        del st
+        torch.cuda.empty_cache()
+        st = S.Stages(xs["q"], xs["k"], xs["v"], xs["gates"], w.block, w.topk, keep_o_sel=False,
+                      keep_score=True, forced_blocks=w.forced, force_own=w.own)
+        st.run_pool()
+        st.run_lse()
+        st.run_fused()
+        st.run_topk()
+        reps = max(1, min(3, args.steps))
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            st.run_topk()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_k = t0.elapsed_time(t1) / reps
+        ach = work["topk"]["bytes"] / (ms_k * 1e-3)
+        kernels["topk_separate"] = {"ms": ms_k, "bound": "hbm", "achieved": ach / 1e9,
+                                    "unit": "GB/s", "frac": ach / PEAK_HBM,
+                                    "note": "separate top-k kernel on the score matrix; not in "
+                                            "the step, where top-k runs inside pass 2"}
+        log(f"[bench] separate top-k on the score matrix {ms_k:.3f} ms")
     dom = max(("cmp_fused", "cmp_lse", "sel"), key=lambda n: stage_ms[n])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
