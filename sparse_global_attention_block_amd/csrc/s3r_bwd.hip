@@ -20,6 +20,8 @@
 //   sel_dq        selection dq, query-centric over the selected blocks
 //   sel_dkv       selection dk, dv plus the spread-back pooled gradients, key-centric over the
 //                 query blocks that selected the key block (from a selection bitmap)
+#include <type_traits>
+
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
@@ -280,7 +282,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   fetch(0);
   stash(0);
   __syncthreads();
-  for (int64_t tau = 0; tau < n; ++tau) {
+  // kLast: only the last tile can hold keys past the last pooled token (masked per element)
+  auto step = [&](int64_t tau, auto last_tile) {
+    constexpr bool kLast = decltype(last_tile)::value;
     fetch(tau + 1 < n ? tau + 1 : tau);
     const uint4* L = lds[(int)(tau & 1)];
     // one 16-key half at a time: its dS values wait in d0 until the second half completes the
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           // keys past the last pooled token carry no probability
-          const bool live = tau * kTileKeys + 16 * s2_ + 4 * g + r < a.Nb;
+          const bool live = !kLast || tau * kTileKeys + 16 * s2_ + 4 * g + r < a.Nb;
           d[r] = live ? fast_exp2(x[r]) * fmaf(g0[nt], y[r], -dl[nt]) : 0.f;
         }
         if (s2_ == 0) {
@@ -325,7 +329,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
     stash((int)((tau + 1) & 1));
     __syncthreads();
-  }
+  };
+  for (int64_t tau = 0; tau + 1 < n; ++tau) step(tau, std::false_type{});
+  step(n - 1, std::true_type{});
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t t = q0 + 16 * nt + li;
