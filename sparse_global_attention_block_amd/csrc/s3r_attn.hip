@@ -159,12 +159,6 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int h, int64_t q0, int
   }
 }
 
-__device__ __forceinline__ void load_tile(const unsigned char* base, int lane, bf16x8 (&rec)[8]) {
-  const bf16x8* p = reinterpret_cast<const bf16x8*>(base);
-#pragma unroll
-  for (int x = 0; x < 8; ++x) rec[x] = p[x * 64 + lane];
-}
-
 // ---------------------------------------------------------------------------------------
 // Selection branch. One wave per (head, query block) (two waves for B = 128, 64 queries
 // each). The wave walks the tiles of its selected blocks in list order. The tiles are
@@ -226,8 +220,8 @@ constexpr int kSelSlots = 2;  // tiles in flight per wave (the vmcnt waits below
 template <int NT, bool kHalf>
 __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   __shared__ uint4 ring[4][kSelSlots][kRawTileBytes / 16];  // 16 KB per wave
-  // wave-uniform as far as the compiler can see, so that the selection row is read with scalar
-  // loads (a vector load would make the compiler wait for every copy in flight)
+  // wave-uniform as far as the compiler can see: the LDS copy destinations (M0), the item and
+  // the row walk then live in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
   const int parts = (a.B > 64) ? a.B / 64 : 1;
