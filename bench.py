@@ -55,10 +55,11 @@ def algorithmic_work(w: W.Workload, T: int, Nb: int):
     }
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the compressed-attention pass-2 kernel, from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy calibration). None
-    when no summary exists for this workload or the kernel source changed since it was taken."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` (its demangled name, e.g. the compressed-attention
+    pass-2 kernel), from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already
+    scaled by the copy calibration). None when no summary exists for this workload, the kernel
+    is not in it, or the kernel source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -68,10 +69,8 @@ def measured_traffic(workload: str):
         h.update(open(os.path.join(ROOT, "sparse_global_attention_block_amd", "csrc", f), "rb").read())
     if rec.get("cmp_fused_source_sha256") != h.hexdigest():
         return None
-    for name, v in rec["kernels"].items():
-        if name.startswith("s3r::cmp_kernel<true"):
-            return v["read_bytes"] + v["write_bytes"]
-    return None
+    v = rec["kernels"].get(kernel)
+    return None if v is None else v["read_bytes"] + v["write_bytes"]
 
 
 def timed_stages(st: "S.Stages", reps: int):
@@ -330,10 +329,14 @@ def main():
                                     "note": "separate top-k kernel on the score matrix; not in "
                                             "the step, where top-k runs inside pass 2"}
         log(f"[bench] separate top-k on the score matrix {ms_k:.3f} ms")
+    # the pass-2 kernel instance the step launched: <fused, query blocks per wave, waves,
+    # running top-k, fp16>
+    pass2_kernel = (f"s3r::cmp_kernel<true, {64 // w.block if w.block <= 64 else 1}, 4, "
+                    f"{'true' if folds else 'false'}, {'true' if w.dtype == 'fp16' else 'false'}>")
     dom = max(("cmp_fused", "cmp_lse", "sel"), key=lambda n: stage_ms[n])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
-            "traffic": measured_traffic(w.name) if dom == "cmp_fused" else None}
+            "traffic": measured_traffic(w.name, pass2_kernel) if dom == "cmp_fused" else None}
     del st, xs
     torch.cuda.empty_cache()
 
