@@ -832,14 +832,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   };
 
   if (active) {
+    // The bitmap row is read 64 words at a time, one per lane (most words are zero: a key
+    // block is chosen by a few dozen of the Nb query blocks); the set bits are then visited in
+    // ascending order, so every wave sees the same ranks and the split is deterministic.
     const uint32_t* bm = a.bitmap + ((int64_t)h * a.Nb + u) * a.bm_words;
     int64_t rank = 0;
-    for (int64_t w = 0; w < a.bm_words; ++w) {
-      uint32_t bits = bm[w];
-      while (bits) {
-        const int b = __builtin_ctz(bits);
-        bits &= bits - 1;
-        if (rank++ % nsplit == split) process(w * 32 + b);
+    for (int64_t w0 = 0; w0 < a.bm_words; w0 += 64) {
+      const uint32_t word = (w0 + lane < a.bm_words) ? bm[w0 + lane] : 0u;
+      uint64_t nz = __ballot(word != 0u);
+      while (nz) {
+        const int l = __builtin_ctzll(nz);
+        nz &= nz - 1;
+        uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)word, l);
+        while (bits) {
+          const int b = __builtin_ctz(bits);
+          bits &= bits - 1;
+          if (rank++ % nsplit == split) process((w0 + l) * 32 + b);
+        }
       }
     }
   }
