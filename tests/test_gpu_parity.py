@@ -52,6 +52,12 @@ CASES = {
                                            topk=5, forced=100, own=True), 1000),
     "v3_own_fp16": (dataclasses.replace(W.WORKLOADS["v8"], name="v3_own_fp16", own=True,
                                         dtype="fp16"), 3 * 1374),
+    # two query blocks per wave in the running top-k (B = 32), with a prefix and own blocks
+    "b32_forced_own": (dataclasses.replace(_tiny_s, name="b32_fo", H=2, block=32, topk=5,
+                                           forced=3, own=True), 1000),
+    # a sequence shorter than one tile of pooled keys: one query block, every block kept
+    "one_block_own": (dataclasses.replace(_tiny_s, name="one_block_own", H=1, block=64, topk=4,
+                                          own=True), 50),
 }
 
 _cache = {}
