@@ -58,6 +58,9 @@ CASES = {
     # a sequence shorter than one tile of pooled keys: one query block, every block kept
     "one_block_own": (dataclasses.replace(_tiny_s, name="one_block_own", H=1, block=64, topk=4,
                                           own=True), 50),
+    # a single token, and a second block of a single token
+    "t1": (dataclasses.replace(_tiny_s, name="t1", H=2, block=16, topk=8), 1),
+    "t17": (dataclasses.replace(_tiny_s, name="t17", H=2, block=16, topk=1), 17),
 }
 
 _cache = {}
