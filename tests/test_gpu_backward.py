@@ -44,6 +44,11 @@ CASES = {
                                        own=True), 3 * 1374, {}),
     "tiny_f3_own": (dataclasses.replace(W.WORKLOADS["tiny"], name="tiny_f3_own", forced=3,
                                         own=True), None, {}),
+    # a second block of a single token, and a single token
+    "t17": (dataclasses.replace(_tiny_s, name="t17", H=2, block=16, topk=1), 17, {}),
+    # one token: both softmaxes have a single key, so dq and dk vanish in exact arithmetic
+    "t1": (dataclasses.replace(_tiny_s, name="t1", H=2, block=16, topk=8), 1,
+           {"vanishing_dqdk": True}),
 }
 
 
@@ -108,8 +113,19 @@ def run_case(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_backward_against_oracle(name):
     (dq, dk, dv, dg), ref, _, _ = run_case(name)
-    compare(name, "dq", dq, ref["dq"])
-    compare(name, "dk", dk, ref["dk"])
+    if CASES[name][2].get("vanishing_dqdk"):
+        # a relative bound means nothing against an exact zero: the GPU's dq, dk are the
+        # rounding of cancelling terms (dP with bf16 operands against the f32 D), held to
+        # 1 % of the gradient scale that dv shows
+        assert np.abs(ref["dq"]).max() < 1e-9 and np.abs(ref["dk"]).max() < 1e-9
+        scale = np.abs(ref["dv"]).max()
+        for what, t in (("dq", dq), ("dk", dk)):
+            a = np.abs(host(t).double().numpy()).max()
+            print(f"[{name}] {what}: max |gpu| {a:.2e} vs dv scale {scale:.2e}", flush=True)
+            assert a <= 1e-2 * scale, what
+    else:
+        compare(name, "dq", dq, ref["dq"])
+        compare(name, "dk", dk, ref["dk"])
     compare(name, "dv", dv, ref["dv"])
     check_dgates(name, dg, ref["dgates"], ref["dout"], ref["forward"])
 
