@@ -130,6 +130,31 @@ def cmp_row(q, kc: np.ndarray, vc: np.ndarray, B: int, h: int, i: int,
     return lse[:n], oc[:n], sc
 
 
+def lse_group_bound(q, k, B: int, group: int = 8, scale: Optional[float] = None) -> np.ndarray:
+    """Lower bound of the compression branch's log-sum-exp used by the single-pass variant
+    (an implementation choice, not part of the pages' method): the pooled keys Kc_0..Kc_{Nb-1}
+    are cut into floor(Nb / group) full groups (a short last group is left out), each group is
+    replaced by its mean G_g, and the bound is
+
+        lse_bound[h, t] = log sum_g group * exp(scale * q_t . G_g)        ([H, T] float64).
+
+    exp is convex and the logit is linear in the key, so by Jensen's inequality
+    group * exp(mean of the group's logits) <= sum of exp over the group's keys: the bound is
+    at most the log-sum-exp over all pooled keys, with equality when every group's keys are
+    equal and no block is left out."""
+    a = _f32(q).astype(np.float64)
+    T, H, D = a.shape
+    kc = pool(k, B)
+    G = kc.shape[1] // group
+    if G < 1:
+        raise ValueError("fewer pooled keys than one group")
+    means = kc[:, :G * group].reshape(H, G, group, D).mean(axis=2)       # [H, G, D]
+    s = default_scale(D) if scale is None else scale
+    logits = s * np.matmul(a.transpose(1, 0, 2), means.transpose(0, 2, 1))  # [H, T, G]
+    m = logits.max(axis=-1, keepdims=True)
+    return m[..., 0] + np.log(np.exp(logits - m).sum(axis=-1)) + math.log(group)
+
+
 def topk(score_row, k: int) -> np.ndarray:
     """Top-k block indices of one float32 score row (value desc, index asc), ascending."""
     s = np.ascontiguousarray(np.asarray(score_row, dtype=np.float32))

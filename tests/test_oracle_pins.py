@@ -536,3 +536,60 @@ def test_own_block_with_all_blocks_is_dense():
     r4 = O.forward_all(x["q"], x["k"], x["v"], x["gates"], 16, 4, own=True)
     for i in range(64):
         assert (r4["sel"][:, i] == i).any(axis=-1).all()
+
+
+# ------------------------------------------------------------- log-sum-exp bound (single pass)
+def _group_constant_keys(T, H, B, group, seed):
+    """Keys constant over every run of `group` consecutive blocks (one random vector each)."""
+    n_groups = -(-T // (B * group))
+    base = bf16_tensor((n_groups, H, 64), seed)
+    return base[torch.arange(T) // (B * group)].contiguous()
+
+
+def test_group_bound_equals_lse_when_groups_are_constant():
+    """Every group of 8 blocks holds one key and Nb is a multiple of 8: Jensen is an equality,
+    so the bound is the exact log-sum-exp (catches a wrong log(group) term, a mean over the
+    wrong axis, or a missing scale)."""
+    T, H, B = 64 * 8 * 3, 2, 64
+    q = bf16_tensor((T, H, 64), 1)
+    k = _group_constant_keys(T, H, B, 8, 2)
+    v = bf16_tensor((T, H, 64), 3)
+    lse = O.forward_all(q, k, v, torch.ones(H, 2), B, 4)["lse"]
+    np.testing.assert_allclose(O.lse_group_bound(q, k, B), lse, rtol=0, atol=1e-12)
+
+
+def test_group_bound_leaves_out_the_short_last_group():
+    """All keys equal (logit c for every pooled key): the log-sum-exp is c + log Nb, the bound
+    c + log(8 floor(Nb / 8)) (catches counting the partial group, or its keys, in the bound)."""
+    T, H, B = 64 * 21 + 17, 1, 64   # Nb = 22: two full groups and 6 blocks left out
+    q = bf16_tensor((T, H, 64), 4)
+    kv = bf16_tensor((1, H, 64), 5)
+    k = kv.expand(T, H, 64).contiguous()
+    c = (q.double() * kv.double()).sum(-1)[:, 0].numpy() / 8.0
+    np.testing.assert_allclose(O.lse_group_bound(q, k, B)[0], c + math.log(16), rtol=0,
+                               atol=1e-12)
+    lse = O.forward_all(q, k, k, torch.ones(H, 2), B, 4)["lse"][0]
+    np.testing.assert_allclose(lse, c + math.log(22), rtol=0, atol=1e-12)
+
+
+def test_group_bound_is_below_the_lse():
+    """Jensen: on random keys the bound lies below the exact log-sum-exp for every query, and
+    the gap closes as the keys within each group become alike (catches a sign slip, or a max
+    in place of the mean, which would lift the bound above the log-sum-exp)."""
+    w = W.WORKLOADS["tiny_s"]
+    x = W.make_inputs(w, T=1536)  # 96 blocks: 12 full groups, none left out
+    lse = O.forward_all(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk)["lse"]
+    bnd = O.lse_group_bound(x["q"], x["k"], w.block)
+    assert (bnd <= lse + 1e-12).all()
+    assert (lse - bnd).max() > 1e-3
+    # keys pulled toward their group's constant key: the gap shrinks with the spread
+    T, H, B = 1536, x["q"].shape[1], w.block
+    kc = _group_constant_keys(T, H, B, 8, 6).float()
+    noise = bf16_tensor((T, H, 64), 7).float()
+    for eps, most in ((1.0, None), (0.01, 0.01)):
+        k = (kc + eps * noise).to(torch.bfloat16)
+        gap = (O.forward_all(x["q"], k, x["v"], x["gates"], B, w.topk)["lse"] -
+               O.lse_group_bound(x["q"], k, B))
+        assert gap.min() >= -1e-12
+        if most is not None:
+            assert gap.max() < most
