@@ -2,10 +2,11 @@
 """Benchmark of the sparse global attention forward pass on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic tokens: block pooling
-(+ packing of the raw keys/values), compressed LSE, compressed output + block scores, top-k
-selection, selection attention + gated combine. Inputs are generated on the GPU and resident
-in HBM before timing starts. The dense attention comparator is timed separately at the same
-shape. Prints one JSON line.
+(+ packing of the raw keys/values), the compression branch (by default the single pass from
+the group-mean bound of the log-sum-exp, with its exact reruns; --cmp-mode two_pass for the
+two exact passes), block scores and top-k selection, selection attention + gated combine.
+Inputs are generated on the GPU and resident in HBM before timing starts. The dense attention
+comparator is timed separately at the same shape. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v1000_k16]
 """
@@ -38,6 +39,7 @@ def algorithmic_work(w: W.Workload, T: int, Nb: int):
     """Per-launch algorithmic flops / bytes of each kernel (per-unit figures times units)."""
     H, D, B, k = w.H, w.D, w.block, w.k_eff
     th = T * H
+    Nb_g = Nb // 8
     sel_keys = sum(min(T, (j + 1) * B) - j * B for j in range(min(k, Nb)))  # ~ k*B
     return {
         # reads k and v once (2 x 128 B per token-head), writes 12 KB per 32 pooled tokens
@@ -48,6 +50,11 @@ def algorithmic_work(w: W.Workload, T: int, Nb: int):
         "cmp_lse": {"flops": 2 * D * th * Nb, "bound": "mfma"},
         # logits + P.Vc: 4*D flops per (token, head, block)
         "cmp_fused": {"flops": 4 * D * th * Nb, "bound": "mfma"},
+        # bound pass: logits over the group keys (means of 8 pooled keys), 2*D per pair
+        "cmp_bound": {"flops": 2 * D * th * Nb_g, "bound": "mfma"},
+        # single pass: logits + P.Vc once over all coarse tokens, 4*D flops per pair (its
+        # rescoring of the listed blocks and the exact reruns are not counted)
+        "cmp_single": {"flops": 4 * D * th * Nb, "bound": "mfma"},
         # reads the score matrix once (4 B per (head, query block, key block))
         "topk": {"bytes": 4 * H * Nb * Nb, "bound": "hbm"},
         # q.k and p.v over the k*B selected tokens: 4*D flops per (token, head, key)
@@ -73,10 +80,13 @@ def measured_traffic(workload: str, kernel: str):
     return None if v is None else v["read_bytes"] + v["write_bytes"]
 
 
-def timed_stages(st: "S.Stages", reps: int):
+def timed_stages(st: "S.Stages", reps: int, single: bool):
     """Runs the hot path stage by stage with HIP events between stages (on the stream the
     library launches on) and returns the mean duration of each stage in ms."""
-    if st.folds_topk:  # the path speed3r_sparse_attn_fwd takes: top-k inside pass 2
+    if single:  # the single compression pass (its exact reruns inside cmp_single)
+        names = ["pool", "cmp_bound", "cmp_single", "sel"]
+        fns = [st.run_pool, st.run_lse_bound, st.run_single_topk, st.run_sel]
+    elif st.folds_topk:  # the two passes with top-k inside pass 2
         names = ["pool", "cmp_lse", "cmp_fused", "sel"]
         fns = [st.run_pool, st.run_lse, st.run_fused_topk, st.run_sel]
     else:
@@ -195,6 +205,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cmp-mode", default="auto", choices=["auto", "two_pass", "single"],
+                    help="compression branch: automatic (the single pass where it applies), "
+                         "the two exact passes, or the single pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (the reference kernel "
                          "for scaling HBM byte counters) and exit")
@@ -223,7 +236,10 @@ def main():
     x = W.make_inputs(w, device=dev)
     torch.cuda.synchronize()
     T, H, D = x["q"].shape
-    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced, w.own)
+    mode = {"auto": S.CMP_AUTO, "two_pass": S.CMP_TWO_PASS, "single": S.CMP_SINGLE}[args.cmp_mode]
+    p = S.make_params(x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced, w.own,
+                      mode)
+    single = S.runs_single(p)
     Nb = S.num_blocks(p)
     layout = w.layout()
     ws = S.alloc_workspace(S.windows_workspace_size(p, layout) if layout else
@@ -235,11 +251,11 @@ def main():
         if layout:  # 2-D windows: reorder in, forward, reorder out
             S.sparse_attn_fwd_windows(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
                                       layout, out=out, sel_idx=sel, workspace=ws,
-                                      forced_blocks=w.forced, force_own=w.own)
+                                      forced_blocks=w.forced, force_own=w.own, cmp_mode=mode)
         else:
             S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
                               sel_idx=sel, workspace=ws, forced_blocks=w.forced,
-                              force_own=w.own)
+                              force_own=w.own, cmp_mode=mode)
 
     for _ in range(args.warmup):
         step()
@@ -255,7 +271,28 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] sparse forward {ms:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f})")
+    log(f"[bench] sparse forward {ms:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f}), "
+        f"compression {'single pass' if single else 'two passes'}")
+    two_pass = None
+    if single and not layout:
+        # the same step with the two exact passes, for comparison (not the reported value)
+        del ws
+        torch.cuda.empty_cache()
+        ws = S.alloc_workspace(S.workspace_size(S.make_params(
+            x["q"], x["k"], x["v"], w.block, w.topk, 0.0, x["gates"], w.forced, w.own,
+            S.CMP_TWO_PASS)), dev)
+        reps = max(1, min(3, args.steps))
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, out=out,
+                              workspace=ws, forced_blocks=w.forced, force_own=w.own,
+                              cmp_mode=S.CMP_TWO_PASS)
+        t1.record()
+        torch.cuda.synchronize()
+        two_pass = {"ms_per_step": t0.elapsed_time(t1) / reps,
+                    "value": T / (t0.elapsed_time(t1) / reps * 1e-3)}
+        log(f"[bench] the same step with the two exact passes: {two_pass['ms_per_step']:.3f} ms")
 
     # per-kernel durations: the same kernels launched stage by stage
     del ws
@@ -281,7 +318,8 @@ def main():
                   keep_score=not folds, forced_blocks=w.forced, force_own=w.own)
     st.run_pool()
     st.run_lse()
-    stage_ms = timed_stages(st, max(1, min(3, args.steps)))
+    stage_ms = timed_stages(st, max(1, min(3, args.steps)), single)
+    redone = int((st.redo != 0).sum().item()) if single else None
     if perm_ms is not None:
         stage_ms["window_permute"] = perm_ms
     log(f"[bench] stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
@@ -329,14 +367,16 @@ def main():
                                     "note": "separate top-k kernel on the score matrix; not in "
                                             "the step, where top-k runs inside pass 2"}
         log(f"[bench] separate top-k on the score matrix {ms_k:.3f} ms")
-    # the pass-2 kernel instance the step launched: <fused, query blocks per wave, waves,
-    # running top-k, fp16>
+    # the compression kernel instance the step launched: <fused, query blocks per wave, waves,
+    # running top-k, fp16, single pass, tiles in flight (0: default)>
     pass2_kernel = (f"s3r::cmp_kernel<true, {64 // w.block if w.block <= 64 else 1}, 4, "
-                    f"{'true' if folds else 'false'}, {'true' if w.dtype == 'fp16' else 'false'}>")
-    dom = max(("cmp_fused", "cmp_lse", "sel"), key=lambda n: stage_ms[n])
+                    f"{'true' if folds else 'false'}, {'true' if w.dtype == 'fp16' else 'false'}, "
+                    f"{'true' if single else 'false'}, 0>")
+    cands = ("cmp_single", "cmp_bound", "sel") if single else ("cmp_fused", "cmp_lse", "sel")
+    dom = max(cands, key=lambda n: stage_ms[n])
     roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved"],
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
-            "traffic": measured_traffic(w.name, pass2_kernel) if dom == "cmp_fused" else None}
+            "traffic": measured_traffic(w.name, pass2_kernel) if dom == cands[0] else None}
     del st, xs
     torch.cuda.empty_cache()
 
@@ -375,10 +415,13 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded structured q/k/v, generated on the GPU)",
-        "config": {**w.describe(), "parallelism": "none (1 GPU)"},
+        "config": {**w.describe(), "parallelism": "none (1 GPU)",
+                   "compression": "single pass" if single else "two passes"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "single_pass_waves_redone": redone,
+        "two_pass": two_pass,
         "backward": backward,
         "dense": dense,
         "x_vs_dense": (dense["ms"] / ms) if dense else None,

@@ -59,6 +59,19 @@ typedef enum {
 /* Element type of q, k, v and out. The model runs in bf16 or fp16 (README "Notice" 3). */
 typedef enum { S3R_BF16 = 0, S3R_FP16 = 1 } s3r_dtype;
 
+/* How the compression branch's softmax is normalised (params.cmp_mode); every mode gives the
+ * same results up to rounding, and the same selection except between blocks whose scores
+ * agree to rounding.
+ *   S3R_CMP_TWO_PASS  pass 1 computes each query's log-sum-exp, pass 2 the probabilities,
+ *                     O_cmp and the scores (speed3r_cmp_lse, then speed3r_cmp_fused[_topk]).
+ *   S3R_CMP_SINGLE    one pass from a cheap lower bound of the log-sum-exp
+ *                     (speed3r_cmp_lse_bound, then speed3r_cmp_single_topk), with the two
+ *                     exact passes rerun where its check fails. Needs the folded selection
+ *                     (B <= 64, n_sel - F' <= 64) and Nb >= 8; S3R_ERR_UNSUPPORTED otherwise.
+ *   S3R_CMP_AUTO      (0) the single pass where it applies and k <= 21 (or every candidate
+ *                     block fits its list of 64), the two passes otherwise. */
+typedef enum { S3R_CMP_AUTO = 0, S3R_CMP_TWO_PASS = 1, S3R_CMP_SINGLE = 2 } s3r_cmp_mode;
+
 typedef struct {
   int64_t T;            /* number of tokens (all views concatenated), >= 1 */
   int32_t H;            /* number of heads, >= 1 */
@@ -78,6 +91,7 @@ typedef struct {
   int32_t dtype;        /* s3r_dtype of q, k, v and out; 0 (zero-initialised) is bf16 */
   int32_t force_own;    /* nonzero: every query block also keeps its own key block (after the
                            forced prefix; top-k then runs over the remaining blocks) */
+  int32_t cmp_mode;     /* s3r_cmp_mode; 0 (zero-initialised) is automatic */
 } s3r_params;
 
 /* Human-readable name of a status code (static storage). */
@@ -96,14 +110,15 @@ int64_t speed3r_num_selected(const s3r_params* p);
 int64_t speed3r_score_row_stride(const s3r_params* p);
 
 /* Bytes of workspace the per-stage entry points need (packed tiles of the pooled keys and
- * values and of the raw keys and values). 0 if p is invalid. */
+ * values, of the group keys of the bound pass, and of the raw keys and values). 0 if p is
+ * invalid. */
 size_t speed3r_tiles_workspace_size(const s3r_params* p);
 
 /* Bytes of workspace speed3r_sparse_attn_fwd needs: the tiles plus LSE [H][T] f32, O_cmp
- * [T][H][64] f32, the selected indices and, only when the selection cannot be folded into
- * the compression pass (B = 128 or more than 64 chosen blocks), the score matrix [H][Nb][ld]
- * f32. About 11.5
- * GB at T = 1,374,000, H = 16, B = 64, k = 16. 0 if p is invalid. */
+ * [T][H][64] f32, the selected indices, the redo flags when the forward pass runs the single
+ * compression pass and, only when the selection cannot be folded into the compression pass
+ * (B = 128 or more than 64 chosen blocks), the score matrix [H][Nb][ld] f32. About 11.5 GB
+ * at T = 1,374,000, H = 16, B = 64, k = 16. 0 if p is invalid. */
 size_t speed3r_workspace_size(const s3r_params* p);
 
 /* Bytes of workspace speed3r_dense_attn_fwd needs (packed raw keys and values). */
@@ -112,7 +127,8 @@ size_t speed3r_dense_workspace_size(const s3r_params* p);
 /* The whole sparse forward pass (the method of the summary's "Methodologie" sections 1-2):
  * pool -> compressed LSE -> compressed output + block scores -> top-k -> selection attention
  * with the gate-combine epilogue. When B <= 64 and k_eff <= 64 the scores never leave the chip
- * (speed3r_cmp_fused_topk); otherwise they go through the score matrix and speed3r_topk.
+ * (speed3r_cmp_fused_topk, or the single pass speed3r_cmp_single_topk per params.cmp_mode);
+ * otherwise they go through the score matrix and speed3r_topk.
  *   gates    f32, [H][2] or per token (see gate_stride_t); column 0 multiplies the
  *            compression branch, column 1 the selection branch.
  *   out      [T][H][64] of the input type, contiguous.
@@ -132,7 +148,8 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
 
 /* Compression branch, pooling (summary "Methodologie" 1, average pooling of blocks): fills the
  * workspace tiles from k and v. k_mean / v_mean (optional, f32 [H][Nb][64]) receive the block
- * means themselves: sum in f32 then an IEEE division by the block's token count. */
+ * means themselves: sum in f32 then an IEEE division by the block's token count. Also writes
+ * the group keys that speed3r_cmp_lse_bound reads. */
 s3r_status speed3r_pool(const s3r_params* p, const void* k, const void* v, void* workspace,
                         size_t workspace_bytes, float* k_mean, float* v_mean,
                         hipStream_t stream);
@@ -162,6 +179,52 @@ s3r_status speed3r_cmp_fused(const s3r_params* p, const void* q, const void* wor
 s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void* workspace,
                                   size_t workspace_bytes, const float* lse, float* o_cmp,
                                   int32_t* sel_idx, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Single compression pass (an implementation choice of this library, not the page's: the
+ * page's method needs each query's log-sum-exp before any probability is final, hence the
+ * two passes above; this computes the same O_cmp and selection with one pass over the
+ * pooled keys plus one over 1/8 of them).
+ * ------------------------------------------------------------------------------------- */
+
+/* Number of int32 flags speed3r_cmp_single_topk writes to `redo`: 4 per 256 queries per head,
+ * H * ceil(T / 256) * 4. -1 if p is invalid. */
+int64_t speed3r_redo_flag_count(const s3r_params* p);
+
+/* Lower bound of the compression branch's log-sum-exp: with group keys G_g = the mean of
+ * pooled keys 8g..8g+7 (g < floor(Nb / 8); the pooling stores them scaled like the pooled
+ * keys, as hi + lo pairs of the input type), lse_bound[h][t] = log sum_g 8 exp(scale * q_t .
+ * G_g) (f32 [H][T], natural log). Convexity of exp (Jensen) makes each group's term at most
+ * the sum of exp over its 8 keys, so lse_bound <= the log-sum-exp of speed3r_cmp_lse (up to
+ * rounding). S3R_ERR_UNSUPPORTED if Nb < 8. */
+s3r_status speed3r_cmp_lse_bound(const s3r_params* p, const void* q, const void* workspace,
+                                 size_t workspace_bytes, float* lse_bound, hipStream_t stream);
+
+/* The compression branch in one pass from a lower bound lse_bound of each query's log-sum-exp
+ * (any bound works; a loose one only makes the checks below fail more often). Writes what
+ * speed3r_cmp_lse and speed3r_cmp_fused_topk write: lse [H][T] (natural log), o_cmp
+ * [T][H][64] f32 and sel_idx [H][Nb][n_sel]. lse may be the same buffer as lse_bound.
+ *   With weights u_tj = exp(c_tj - lse_bound_t) >= P_tj (c_tj = scale * q_t . Kc_j), one
+ *   sweep over the pooled keys accumulates Z_t = sum_j u_tj, O_cmp_t * Z_t and, per key
+ *   block, the upper bound U_ij = sum_{t in block i} u_tj of the score Score_ij. Each query
+ *   block keeps the 64 candidate blocks of largest bound (all of them if fewer); at the end
+ *   lse_t = lse_bound_t + log Z_t, O_cmp_t = (O_cmp_t * Z_t) / Z_t, and the listed blocks are
+ *   rescored exactly with that lse (the same logits, on the same matrix instructions) and
+ *   ranked by (score desc, index asc).
+ *   Checks, per wave of 64 queries: 1 <= Z_t <= 2^15 for each of its queries (the offset was
+ *   below lse_t, so every U bounds its Score, and no weight, each at most Z_t, overflowed the
+ *   fp16 operands of P.V); and, per query block, the smallest bound in the list times
+ *   (1 + 2^-12) is below the k-th exact score, so that no unlisted block can belong to the
+ *   top k. redo (int32 [H * ceil(T/256)][4], speed3r_redo_flag_count entries, 16-byte
+ *   aligned; one per wave) receives bit 1 where the first check failed and bit 0 where the
+ *   second did. Then, in the same call, speed3r_cmp_lse reruns on the 256 queries around
+ *   each wave with bit 1, and speed3r_cmp_fused_topk on those around any flagged wave, so
+ *   every output ends as the two exact passes would give it. Requires B <= 64,
+ *   n_sel - F' <= 64 and Nb >= 8 (S3R_ERR_UNSUPPORTED otherwise). */
+s3r_status speed3r_cmp_single_topk(const s3r_params* p, const void* q, const void* workspace,
+                                   size_t workspace_bytes, const float* lse_bound, float* lse,
+                                   float* o_cmp, int32_t* sel_idx, int32_t* redo,
+                                   hipStream_t stream);
 
 /* Top-k selection (summary "Methodologie" 1, selection guided by the compression scores):
  * sel_idx[(h*Nb + i)*n_sel + a]: the forced blocks 0..F'-1, then the n_sel - F' largest

@@ -27,11 +27,16 @@ struct Dims {
   int32_t half;    // q, k, v (and out) are fp16; else bf16
   float scale;
   bool fold_topk;  // selection folded into the compression pass (no score matrix)
+  int64_t Nb_g;     // keys of the bound pass: full groups of kGroupBlocks pooled keys
+  int64_t n_gtiles; // tiles of those keys, ceil(Nb_g / 32)
+  int64_t n_redo;   // redo flags of the single pass: 4 per 256 queries per head
+  bool single_ok;   // the single pass applies: folded selection and at least one group
+  bool single;      // the forward pass runs the single pass (cmp_mode)
 };
 
 // Workspace regions, in this order, each 256-byte aligned.
 struct Layout {
-  size_t pooled, raw, lse, o_cmp, score, sel, tiles_end, end;
+  size_t pooled, groups, raw, lse, o_cmp, score, sel, redo, tiles_end, end;
 };
 
 bool valid_stride(int64_t s) { return s >= 0 && (s % 8) == 0; }
@@ -42,6 +47,9 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   if (p->T < 1 || p->H < 1 || p->topk < 1 || p->forced_blocks < 0) return S3R_ERR_INVALID_ARG;
   if (p->block < 1 || p->D < 1) return S3R_ERR_INVALID_ARG;
   if (p->dtype != S3R_BF16 && p->dtype != S3R_FP16) return S3R_ERR_INVALID_ARG;
+  if (p->cmp_mode != S3R_CMP_AUTO && p->cmp_mode != S3R_CMP_TWO_PASS &&
+      p->cmp_mode != S3R_CMP_SINGLE)
+    return S3R_ERR_INVALID_ARG;
   if (!(p->scale >= 0.f) || isinf(p->scale)) return S3R_ERR_INVALID_ARG;
   if (!valid_stride(p->q_stride_t) || !valid_stride(p->q_stride_h) ||
       !valid_stride(p->k_stride_t) || !valid_stride(p->k_stride_h) ||
@@ -69,6 +77,15 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   // one more candidate
   const int64_t most = (p->topk < d->Nb - d->forced) ? p->topk : d->Nb - d->forced;
   d->fold_topk = d->B <= 64 && most <= kFusedTopkMaxK;
+  d->Nb_g = d->Nb / kGroupBlocks;
+  d->n_gtiles = (d->Nb_g + kTileKeys - 1) / kTileKeys;
+  d->n_redo = (int64_t)d->H * ((d->T + 255) / 256) * 4;
+  d->single_ok = d->fold_topk && d->Nb_g >= 1;
+  // automatic: the single pass where its list of 64 bound-ranked candidates holds every
+  // candidate or at least 3k of them (otherwise its check fails too often to pay)
+  d->single = d->single_ok && (p->cmp_mode == S3R_CMP_SINGLE ||
+                               (p->cmp_mode == S3R_CMP_AUTO &&
+                                (3 * most <= kFusedTopkMaxK || d->Nb - d->forced <= 64)));
   // the separate top-k kernel holds a score row in registers; the folded one has no limit
   if (!d->fold_topk && d->Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   return S3R_OK;
@@ -79,6 +96,8 @@ Layout layout(const Dims& d) {
   size_t off = 0;
   L.pooled = off;
   off += align256((size_t)d.H * d.n_ctiles * kPooledTileBytes);
+  L.groups = off;
+  off += align256((size_t)d.H * d.n_gtiles * kPooledTileBytes);
   L.raw = off;
   off += align256((size_t)d.H * d.n_ktiles * kRawTileBytes);
   L.tiles_end = off;
@@ -90,6 +109,8 @@ Layout layout(const Dims& d) {
   if (!d.fold_topk) off += align256((size_t)d.H * d.Nb * d.ld * sizeof(float));
   L.sel = off;
   off += align256((size_t)d.H * d.Nb * d.k_eff * sizeof(int32_t));
+  L.redo = off;
+  if (d.single) off += align256((size_t)d.n_redo * sizeof(int32_t));
   L.end = off;
   return L;
 }
@@ -112,6 +133,8 @@ PoolArgs pool_args(const s3r_params* p, const Dims& d, const void* k, const void
   a.key_mult = d.scale * kLog2e;
   a.k_mean = k_mean; a.v_mean = v_mean;
   a.tiles = (unsigned char*)ws + L.pooled;
+  a.group_tiles = d.n_gtiles > 0 ? (unsigned char*)ws + L.groups : nullptr;
+  a.n_gtiles = d.n_gtiles;
   return a;
 }
 
@@ -155,6 +178,38 @@ s3r_status run_cmp_fused(const Dims& d, CmpArgs a, hipStream_t stream) {
     if (st != S3R_OK) return st;
   }
   return hip_status(launch_cmp_fused(a, stream));
+}
+
+// The bound pass: the LSE pass over the group keys (mean of 8 pooled keys each), plus ln 8.
+// By Jensen's inequality sum_{j in G} exp(c_j) >= 8 exp(mean_G c), and c is linear in the
+// key, so log sum_G 8 exp(q . mean_G Kc) is at most the log-sum-exp over all pooled keys.
+s3r_status run_lse_bound(const Dims& d, CmpArgs a, const unsigned char* ws, const Layout& L,
+                         float* lse_bound, hipStream_t stream) {
+  a.tiles = ws + L.groups;
+  a.n_tiles = d.n_gtiles;
+  a.Nb = d.Nb_g;
+  a.lse = lse_bound;
+  a.lse_bias = logf((float)kGroupBlocks);
+  return hip_status(launch_cmp_lse(a, stream));
+}
+
+// The single pass from the bound, then the two exact passes on the work-groups it flagged.
+// `a` carries the selection fields; lse_bound may equal lse.
+s3r_status run_single(CmpArgs a, const float* lse_bound, float* lse, int32_t* redo,
+                      hipStream_t stream) {
+  s3r_status st;
+  a.lse_in = lse_bound;
+  a.lse = lse;
+  a.redo_out = redo;
+  if ((st = hip_status(launch_cmp_single_topk(a, stream))) != S3R_OK) return st;
+  a.redo_out = nullptr;
+  a.redo_in = redo;
+  a.redo_mask = 2;  // the log-sum-exp again where the Z check failed
+  a.lse_bias = 0.f;
+  if ((st = hip_status(launch_cmp_rerun(a, stream, false))) != S3R_OK) return st;
+  a.redo_mask = 3;  // probabilities, O_cmp and the selection where either check failed
+  a.lse_in = lse;
+  return hip_status(launch_cmp_rerun(a, stream, true));
 }
 
 // Regions the training forward pass adds after the forward workspace: what the backward
@@ -218,11 +273,19 @@ s3r_status run_forward(const s3r_params* p, const Dims& d, const Layout& L, cons
   if ((st = hip_status(launch_pack(pack_args(p, d, k, v, ws + L.raw), stream))) != S3R_OK)
     return st;
   CmpArgs c = cmp_args(p, d, q, ws, L);
-  c.lse = lse;
-  if ((st = hip_status(launch_cmp_lse(c, stream))) != S3R_OK) return st;
-  c.lse_in = lse;
   c.o_cmp = o_cmp;
-  if (d.fold_topk) {
+  if (d.single) {
+    c.sel = sel;
+    c.n_sel = (int32_t)d.k_eff;
+    c.forced = (int32_t)d.forced;
+    c.topk = (int32_t)d.topk;
+    c.own = d.own;
+    if ((st = run_lse_bound(d, c, ws, L, lse, stream)) != S3R_OK) return st;
+    if ((st = run_single(c, lse, lse, (int32_t*)(ws + L.redo), stream)) != S3R_OK) return st;
+  } else if (d.fold_topk) {
+    c.lse = lse;
+    if ((st = hip_status(launch_cmp_lse(c, stream))) != S3R_OK) return st;
+    c.lse_in = lse;
     c.sel = sel;
     c.n_sel = (int32_t)d.k_eff;
     c.forced = (int32_t)d.forced;
@@ -230,6 +293,9 @@ s3r_status run_forward(const s3r_params* p, const Dims& d, const Layout& L, cons
     c.own = d.own;
     if ((st = hip_status(launch_cmp_fused_topk(c, stream))) != S3R_OK) return st;
   } else {
+    c.lse = lse;
+    if ((st = hip_status(launch_cmp_lse(c, stream))) != S3R_OK) return st;
+    c.lse_in = lse;
     c.score = score;
     if ((st = run_cmp_fused(d, c, stream)) != S3R_OK) return st;
     TopkArgs t;
@@ -413,6 +479,48 @@ s3r_status speed3r_cmp_fused_topk(const s3r_params* p, const void* q, const void
   return hip_status(launch_cmp_fused_topk(a, stream));
 }
 
+int64_t speed3r_redo_flag_count(const s3r_params* p) {
+  Dims d;
+  return check_params(p, &d) == S3R_OK ? d.n_redo : -1;
+}
+
+s3r_status speed3r_cmp_lse_bound(const s3r_params* p, const void* q, const void* workspace,
+                                 size_t workspace_bytes, float* lse_bound, hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  if (!tok_ok(q) || !lse_bound || !aligned(lse_bound, 4)) return S3R_ERR_INVALID_ARG;
+  if (d.Nb_g < 1) return S3R_ERR_UNSUPPORTED;
+  const Layout L = layout(d);
+  if ((st = check_ws(workspace, workspace_bytes, L.tiles_end)) != S3R_OK) return st;
+  return run_lse_bound(d, cmp_args(p, d, q, workspace, L), (const unsigned char*)workspace, L,
+                       lse_bound, stream);
+}
+
+s3r_status speed3r_cmp_single_topk(const s3r_params* p, const void* q, const void* workspace,
+                                   size_t workspace_bytes, const float* lse_bound, float* lse,
+                                   float* o_cmp, int32_t* sel_idx, int32_t* redo,
+                                   hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  if (!tok_ok(q) || !lse_bound || !aligned(lse_bound, 4) || !lse || !aligned(lse, 4) ||
+      !o_cmp || !aligned(o_cmp, 16) || !sel_idx || !aligned(sel_idx, 4) || !redo ||
+      !aligned(redo, 16))
+    return S3R_ERR_INVALID_ARG;
+  if (!d.single_ok) return S3R_ERR_UNSUPPORTED;
+  const Layout L = layout(d);
+  if ((st = check_ws(workspace, workspace_bytes, L.tiles_end)) != S3R_OK) return st;
+  CmpArgs a = cmp_args(p, d, q, workspace, L);
+  a.o_cmp = o_cmp;
+  a.sel = sel_idx;
+  a.n_sel = (int32_t)d.k_eff;
+  a.forced = (int32_t)d.forced;
+  a.topk = (int32_t)d.topk;
+  a.own = d.own;
+  return run_single(a, lse_bound, lse, redo, stream);
+}
+
 s3r_status speed3r_topk(const s3r_params* p, const float* score, int32_t* sel_idx,
                         hipStream_t stream) {
   Dims d;
@@ -452,6 +560,7 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
   Dims d;
   s3r_status st = check_params(p, &d);
   if (st != S3R_OK) return st;
+  if (p->cmp_mode == S3R_CMP_SINGLE && !d.single_ok) return S3R_ERR_UNSUPPORTED;
   if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !out ||
       !aligned(out, 8) || (sel_idx && !aligned(sel_idx, 4)))
     return S3R_ERR_INVALID_ARG;
@@ -473,6 +582,7 @@ s3r_status speed3r_sparse_attn_fwd_train(const s3r_params* p, const void* q, con
   Dims d;
   s3r_status st = check_params(p, &d);
   if (st != S3R_OK) return st;
+  if (p->cmp_mode == S3R_CMP_SINGLE && !d.single_ok) return S3R_ERR_UNSUPPORTED;
   if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !out ||
       !aligned(out, 8) || (sel_idx && !aligned(sel_idx, 4)))
     return S3R_ERR_INVALID_ARG;
@@ -641,6 +751,7 @@ s3r_status speed3r_sparse_attn_fwd_windows(const s3r_params* p, const s3r_window
   Dims d;
   s3r_status st = check_params(p, &d);
   if (st != S3R_OK) return st;
+  if (p->cmp_mode == S3R_CMP_SINGLE && !d.single_ok) return S3R_ERR_UNSUPPORTED;
   WindowLayout L;
   int64_t T;
   if (!window_layout(w, &L, &T) || T != p->T) return S3R_ERR_INVALID_ARG;

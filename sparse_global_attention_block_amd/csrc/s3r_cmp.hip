@@ -41,10 +41,15 @@ constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 // indices at the end. The entries are ordered by (score desc, block index asc), a total order,
 // so the final set does not depend on the order in which blocks arrive, and the decision is
 // made on exactly the f32 column sums the score matrix would have held.
-template <bool kFused, int kQB, int kWaves, bool kTopk = false, bool kHalf = false>
+// kBound (with kTopk): the single pass over the pooled tokens described below.
+// kDeep: tiles in flight for the exact reruns after the single pass, where a few lone
+// work-groups sweep all tiles and the latency of each copy, not the chip's throughput, decides.
+template <bool kFused, int kQB, int kWaves, bool kTopk = false, bool kHalf = false,
+          bool kBound = false, int kDeep = 0>
 // (second bound: resident waves per SIMD the register allocation must allow)
 __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArgs a) {
-  constexpr int kAhead = kFused ? kFusedAhead : kLseAhead;  // tiles in flight
+  static_assert(!kBound || (kFused && kTopk), "the single pass keeps the running top-k");
+  constexpr int kAhead = kDeep ? kDeep : (kFused ? kFusedAhead : kLseAhead);  // tiles in flight
   constexpr int kRing = kAhead + 1;
   constexpr int kQueries = 64 * kWaves;
   constexpr int kRecs = kFused ? 12 : 8;  // records of a tile this pass reads
@@ -57,6 +62,10 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   const int64_t total = (int64_t)a.H * n_qtiles;
   const int64_t logical = xcd_logical_id(blockIdx.x, total);
   if (logical >= total) return;
+  if (a.redo_in) {  // exact rerun of the work-groups the single pass flagged
+    const int4 f = *reinterpret_cast<const int4*>(a.redo_in + 4 * logical);
+    if (((f.x | f.y | f.z | f.w) & a.redo_mask) == 0) return;
+  }
   const int h = (int)(logical / n_qtiles);
   const int64_t qt = logical % n_qtiles;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -89,7 +98,11 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t t = q0 + 16 * nt + li;
-    if constexpr (kFused) {
+    if constexpr (kBound) {
+      // a lower bound of L_t (base 2), lowered by kBoundMargin so that rounding cannot lift
+      // it above L_t
+      off[nt] = (t < a.T) ? a.lse_in[(int64_t)h * a.T + t] * kLog2e - kBoundMargin : INFINITY;
+    } else if constexpr (kFused) {
       off[nt] = (t < a.T) ? a.lse_in[(int64_t)h * a.T + t] * kLog2e : INFINITY;
     } else {
       off[nt] = 0.f;
@@ -117,6 +130,17 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   };
   auto better = [](float v1, int j1, float v2, int j2) {
     return v1 > v2 || (v1 == v2 && j1 < j2);
+  };
+  // length of the running list: k for the exact pass; the single pass ranks upper bounds and
+  // keeps every candidate up to one per lane
+  auto list_len = [&](int64_t qblk, bool& own) {
+    if constexpr (kBound) {
+      own = a.own && qblk >= a.forced;
+      const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
+      return (int)(nc < 64 ? nc : 64);
+    } else {
+      return chosen(qblk, own);
+    }
   };
 
   floatx4 o[4][4];
@@ -221,6 +245,36 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             p[s2][nt][r] = fast_exp2(acc[s2][nt][r] - off[nt]);
+      if constexpr (kBound) {
+        // this lane's part of Z_t
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          float z = p[0][nt][0];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int r = (s2 == 0 ? 1 : 0); r < 4; ++r) z += p[s2][nt][r];
+          lsum[nt] += z;
+        }
+      }
+      // column sums over the queries of each query block
+      float tots[kQB];
+      auto column_sums = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          float v[2][4];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float s = p[s2][qb * kNtPerQB][r];
+#pragma unroll
+              for (int nt = qb * kNtPerQB + 1; nt < (qb + 1) * kNtPerQB; ++nt) s += p[s2][nt][r];
+              v[s2][r] = s;
+            }
+          tots[qb] = row_reduce_scatter8(v, lane);
+        }
+      };
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
@@ -231,20 +285,10 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
           o[mt][nt] = mfma16h(vt, pb, o[mt][nt]);
         }
       }
-      // column sums over the queries of each query block
+      column_sums();
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
-        float v[2][4];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float s = p[s2][qb * kNtPerQB][r];
-#pragma unroll
-            for (int nt = qb * kNtPerQB + 1; nt < (qb + 1) * kNtPerQB; ++nt) s += p[s2][nt][r];
-            v[s2][r] = s;
-          }
-        const float tot = row_reduce_scatter8(v, lane);
+        const float tot = tots[qb];
         const int64_t qblk = (q0 + 16 * qb * kNtPerQB) / a.B;
         if constexpr (kTopk) {
           if (qblk < a.Nb) {
@@ -252,7 +296,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
             // enter the list if its score is >= the current k-th score (one compare per tile)
             const int j = (int)(tau * kTileKeys) + reduced_key(lane);
             bool own;
-            const int K = chosen(qblk, own);
+            const int K = list_len(qblk, own);
             const bool mine = ((lane & 2) == 0) && K > 0 && j >= a.forced && j < a.Nb &&
                               !(own && j == qblk);
             uint64_t cand = __ballot(mine && tot >= th_v[qb]);
@@ -289,6 +333,85 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         }
       }
     }
+  };
+
+  // (single pass) Exact scores of the listed blocks of query block qi, from the exact L_t:
+  // the blocks' pooled keys are gathered 16 at a time into this wave's LDS records R and meet
+  // the resident queries in the same MFMA sequence as in the pass, so every logit is the
+  // pass's own. The k best by (score desc, index asc) are kept if the largest upper bound of
+  // a block outside the list stays below the k-th score; otherwise `fail` is set.
+  auto rescore = [&](int qi, const float (&L2)[4], uint4* R, bool& fail) {
+    // (a list short of entries, from non-finite bounds, has also failed the Z check)
+    const int64_t qblk = (q0 + 16 * qi * kNtPerQB) / a.B;
+    if (qblk >= a.Nb) return;
+    bool own;
+    const int Kc = list_len(qblk, own);
+    const int K = chosen(qblk, own);
+    if (Kc <= 0) return;
+    const int j = tk_j[qi];
+    float S = -1.0f;
+    fail |= lane < Kc && !(j >= 0 && j < a.Nb);
+    for (int gq = 0; gq < (Kc + 15) / 16; ++gq) {
+      const int e = 16 * gq + li;
+      int je = __shfl(j, e);
+      je = (e < Kc && je >= 0 && je < a.Nb) ? je : 0;
+      const int kk = je & 31, s = kk >> 4;
+      const unsigned char* src =
+          tiles + (int64_t)(je >> 5) * kPooledTileBytes + 16 * ((kk & 15) + 16 * g);
+      wait_lds();  // the previous group's operands have been read
+      copy16_to_lds(src + (2 * s) * kRecBytes, R);            // hi, dims 0..31
+      copy16_to_lds(src + (2 * s + 1) * kRecBytes, R + 64);   // hi, dims 32..63
+      copy16_to_lds(src + (4 + 2 * s) * kRecBytes, R + 128);  // lo, dims 0..31
+      copy16_to_lds(src + (5 + 2 * s) * kRecBytes, R + 192);  // lo, dims 32..63
+      wait_vmem<0>();
+      const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(&R[lane]);
+      const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(&R[64 + lane]);
+      const bf16x8 l0 = *reinterpret_cast<const bf16x8*>(&R[128 + lane]);
+      const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(&R[192 + lane]);
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nt = qi * kNtPerQB; nt < (qi + 1) * kNtPerQB; ++nt) {
+        floatx4 x = mfma_in<kHalf>(h0, qb[nt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        x = mfma_in<kHalf>(h1, qb[nt][1], x);
+        x = mfma_in<kHalf>(l0, qb[nt][0], x);
+        x = mfma_in<kHalf>(l1, qb[nt][1], x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += fast_exp2(x[r] - L2[nt]);
+      }
+      // sum over the 16 queries of each column tile: lane group g then holds the scores of
+      // listed entries 16 gq + 4 g + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int sh = 1; sh < 16; sh *= 2) v[r] += __shfl_xor(v[r], sh);
+      const int from = 16 * (li >> 2);
+      const float t0 = __shfl(v[0], from), t1 = __shfl(v[1], from);
+      const float t2 = __shfl(v[2], from), t3 = __shfl(v[3], from);
+      const int rr = lane & 3;
+      const float pick = rr == 0 ? t0 : (rr == 1 ? t1 : (rr == 2 ? t2 : t3));
+      if (g == gq) S = pick;
+    }
+    // exact rank of each entry among the Kc listed ones
+    int rank = 0;
+    for (int m = 0; m < Kc; ++m) {
+      const float sm =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), m));
+      const int jm = __builtin_amdgcn_readlane(j, m);
+      rank += better(sm, jm, S, j) ? 1 : 0;
+    }
+    if (lane >= Kc) rank = lane;
+    const uint64_t at = __ballot(rank == K - 1);
+    const int kth = at ? __builtin_ctzll(at) : 0;
+    const float sk =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), kth));
+    // Every block outside the list has a bound <= the list's last entry th_v (it fell below
+    // the threshold of its tile, was pushed out from the last place, or tied with it), and
+    // the threshold only rises. With at most 64 candidates every one is listed. The sums of
+    // the bounds and of the exact scores round in different orders: 2^-12 margin.
+    const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
+    const float rmax = nc <= Kc ? -1.0f : th_v[qi];
+    fail |= !(at != 0 && (rmax < 0.f || rmax * (1.0f + 0x1p-12f) < sk));
+    tk_j[qi] = __builtin_amdgcn_ds_permute(4 * rank, j);  // entry of exact rank e to lane e
   };
 
   // Ring of kRing slots, kAhead tiles in flight. Every step requests one tile (the last one
@@ -332,9 +455,37 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         m = M;
       }
       const int64_t t = q0 + 16 * nt + li;
-      if (g == 0 && t < a.T) a.lse[(int64_t)h * a.T + t] = (m + __log2f(l)) * kLn2;
+      if (g == 0 && t < a.T) a.lse[(int64_t)h * a.T + t] = (m + __log2f(l)) * kLn2 + a.lse_bias;
     }
   } else {
+    float zinv[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (kBound) {
+      // Z_t and the exact L_t = offset + log2 Z_t. Z_t >= 1 proves offset <= L_t, i.e. every
+      // weight was at least its probability, so each block's accumulated sum bounds its score
+      // from above; Z_t <= 2^15 proves that no weight (each is at most Z_t) overflowed fp16 in
+      // P.V. A wave that holds a query outside [1, 2^15] fails (flag bit 1: both exact passes
+      // rerun); one whose selection is not proven fails with bit 0 (only the second reruns:
+      // its L_t are exact).
+      bool zfail = false, fail = false;
+      float L2[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float z = lsum[nt] + __shfl_xor(lsum[nt], 16);
+        z += __shfl_xor(z, 32);
+        const int64_t t = q0 + 16 * nt + li;
+        zfail |= t < a.T && !(z >= 1.0f && z <= 0x1p15f);
+        L2[nt] = (t < a.T && z > 0.f) ? off[nt] + __log2f(z) : INFINITY;
+        zinv[nt] = z > 0.f ? 1.0f / z : 0.f;
+        if (g == 0 && t < a.T) a.lse[(int64_t)h * a.T + t] = L2[nt] * kLn2;
+      }
+      lds_barrier();  // every wave is done with the ring: each takes a quarter of it
+      static_assert(kRing * kRecs * 64 / kWaves >= 4 * 64, "four records per wave");
+      uint4* R = &lds[0][0] + wave * (kRing * kRecs * 64 / kWaves);
+#pragma unroll
+      for (int qi = 0; qi < kQB; ++qi) rescore(qi, L2, R, fail);
+      const int flag = (__any(zfail) ? 2 : 0) | (__any(fail) ? 1 : 0);
+      if (lane == 0) a.redo_out[4 * logical + wave] = flag;
+    }
     if constexpr (kTopk) {
       // the chosen blocks of each query block, in ascending index order
 #pragma unroll
@@ -364,7 +515,8 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           *reinterpret_cast<float4*>(a.o_cmp + (t * a.H + h) * kD + 16 * mt + 4 * g) =
-              make_float4(o[mt][nt][0], o[mt][nt][1], o[mt][nt][2], o[mt][nt][3]);
+              make_float4(o[mt][nt][0] * zinv[nt], o[mt][nt][1] * zinv[nt],
+                          o[mt][nt][2] * zinv[nt], o[mt][nt][3] * zinv[nt]);
         }
       }
     }
@@ -401,6 +553,36 @@ static hipError_t launch_cmp_t(const CmpArgs& a, hipStream_t s, bool fused, bool
   return hipGetLastError();
 }
 
+template <bool kHalf>
+static hipError_t launch_single_t(const CmpArgs& a, hipStream_t s) {
+  const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
+  switch (a.B) {
+    case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, kHalf, true>), g3, b3, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, kHalf, true>), g3, b3, 0, s, a); break;
+    default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, kHalf, true>), g3, b3, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+constexpr int kRerunAhead = 3;
+
+template <bool kHalf>
+static hipError_t launch_rerun_t(const CmpArgs& a, hipStream_t s, bool fused) {
+  const dim3 b4(64 * 4);
+  if (fused) {
+    const dim3 g3 = cmp_grid(a, kFusedWaves);
+    switch (a.B) {
+      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, kHalf, false, kRerunAhead>), g3, b4, 0, s, a); break;
+      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, kHalf, false, kRerunAhead>), g3, b4, 0, s, a); break;
+      default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, kHalf, false, kRerunAhead>), g3, b4, 0, s, a); break;
+    }
+  } else {
+    hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false, kHalf, false, kRerunAhead>),
+                       cmp_grid(a, kLseWaves), b4, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 static hipError_t launch_cmp(const CmpArgs& a, hipStream_t s, bool fused, bool topk) {
   return a.half ? launch_cmp_t<true>(a, s, fused, topk) : launch_cmp_t<false>(a, s, fused, topk);
 }
@@ -409,6 +591,12 @@ hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s) { return launch_cmp(a
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, true, false); }
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s) {
   return launch_cmp(a, s, true, true);
+}
+hipError_t launch_cmp_single_topk(const CmpArgs& a, hipStream_t s) {
+  return a.half ? launch_single_t<true>(a, s) : launch_single_t<false>(a, s);
+}
+hipError_t launch_cmp_rerun(const CmpArgs& a, hipStream_t s, bool fused) {
+  return a.half ? launch_rerun_t<true>(a, s, fused) : launch_rerun_t<false>(a, s, fused);
 }
 
 }  // namespace s3r

@@ -16,6 +16,8 @@ struct PoolArgs {
   float key_mult;          // scale * log2(e), folded into the packed pooled keys
   float* k_mean; float* v_mean;  // optional f32 [H][Nb][64]
   unsigned char* tiles;    // [H][n_tiles][12 KB]
+  unsigned char* group_tiles;  // optional [H][n_gtiles][12 KB] (K records only): key g is the
+  int64_t n_gtiles;            // mean of pooled keys 8g..8g+7, for g < 32 * n_gtiles
 };
 
 struct PackArgs {
@@ -44,7 +46,17 @@ struct CmpArgs {
   int32_t forced;          // F': blocks 0..F'-1 always selected, top-k over the rest
   int32_t topk;            // k (chosen per row, clamped to the candidates)
   int32_t own;             // each query block also keeps its own block
+  float lse_bias;          // added to every log-sum-exp the LSE pass writes (natural log)
+  const int32_t* redo_in;  // if set: only work-groups with a flag & redo_mask of their 4 run
+  int32_t redo_mask;
+  int32_t* redo_out;       // single pass: [work-group][4 waves], bit 0 = selection not proven,
+                           // bit 1 = Z check failed (the log-sum-exp must be recomputed)
 };
+
+// The single compression pass starts from lse_in - kBoundMargin (base 2): a lower bound of
+// the log-sum-exp must stay one after rounding.
+constexpr float kBoundMargin = 0x1p-10f;
+constexpr int kGroupBlocks = 8;  // pooled keys averaged into one key of the bound pass
 
 struct TopkArgs {
   const float* score;
@@ -183,6 +195,9 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s);
+hipError_t launch_cmp_single_topk(const CmpArgs& a, hipStream_t s);
+// the exact passes on the work-groups redo_in flags (fused: pass 2 with the running top-k)
+hipError_t launch_cmp_rerun(const CmpArgs& a, hipStream_t s, bool fused);
 constexpr int kFusedTopkMaxK = 64;  // the running top-k keeps one entry per lane
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sel(const AttnArgs& a, hipStream_t s);

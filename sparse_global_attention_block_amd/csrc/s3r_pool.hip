@@ -14,7 +14,8 @@ namespace s3r {
 // then divides by the block's token count (IEEE division). Writes the f32 means (optional)
 // and one pooled tile: the mean keys scaled by key_mult = scale*log2(e) as a hi + lo pair in the
 // input type (hi = round(x), lo = round(x - hi); bf16 or fp16), and the mean values as fp16
-// V^T records.
+// V^T records. Optionally also the group keys (means of 8 consecutive scaled pooled keys) of
+// the bound pass, in the K records of group tiles.
 template <bool kHalf>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[kPooledTileBytes];
@@ -82,6 +83,38 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     int rec, lane, slot;
     vt_position(m, d8 * 8 + e, rec, lane, slot);
     vt[(rec * 64 + lane) * 8 + slot] = f16_bits(vs[e]);
+  }
+  if (a.group_tiles) {
+    // group key 4*tile + wave: the mean of the scaled pooled keys 8*(4*tile + wave)..+7, held
+    // by lanes 8*m' + d8 of this wave (m' = 0..7), written as a hi + lo pair like them
+    const int64_t gk = tile * 4 + (tid >> 6);
+    float gx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = ks[e] * a.key_mult;
+      x += __shfl_xor(x, 8);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      gx[e] = x * 0.125f;
+    }
+    if ((tid & 63) < 8 && gk < kTileKeys * a.n_gtiles) {
+      u16 ghi[8], glo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ghi[e] = float_to_in<kHalf>(gx[e]);
+        glo[e] = float_to_in<kHalf>(gx[e] - in_to_float<kHalf>(ghi[e]));
+      }
+      unsigned char* gt =
+          a.group_tiles + ((int64_t)h * a.n_gtiles + gk / kTileKeys) * kPooledTileBytes;
+      const int goff = k_chunk_offset((int)(gk % kTileKeys), d8);
+      uint4 gh, gl;
+      gh.x = ghi[0] | ((uint32_t)ghi[1] << 16); gh.y = ghi[2] | ((uint32_t)ghi[3] << 16);
+      gh.z = ghi[4] | ((uint32_t)ghi[5] << 16); gh.w = ghi[6] | ((uint32_t)ghi[7] << 16);
+      gl.x = glo[0] | ((uint32_t)glo[1] << 16); gl.y = glo[2] | ((uint32_t)glo[3] << 16);
+      gl.z = glo[4] | ((uint32_t)glo[5] << 16); gl.w = glo[6] | ((uint32_t)glo[7] << 16);
+      *reinterpret_cast<uint4*>(gt + goff) = gh;
+      *reinterpret_cast<uint4*>(gt + 4 * kRecBytes + goff) = gl;
+    }
   }
   __syncthreads();
   uint4* dst = reinterpret_cast<uint4*>(a.tiles + ((int64_t)h * a.n_tiles + tile) * kPooledTileBytes);

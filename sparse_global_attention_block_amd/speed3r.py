@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspeed3r.so")
 
 S3R_OK, S3R_ERR_INVALID_ARG, S3R_ERR_UNSUPPORTED, S3R_ERR_WORKSPACE, S3R_ERR_HIP = range(5)
+CMP_AUTO, CMP_TWO_PASS, CMP_SINGLE = range(3)  # s3r_cmp_mode
 
 
 class Params(ctypes.Structure):
@@ -29,7 +30,7 @@ class Params(ctypes.Structure):
         ("k_stride_t", ctypes.c_int64), ("k_stride_h", ctypes.c_int64),
         ("v_stride_t", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
         ("gate_stride_t", ctypes.c_int64), ("dtype", ctypes.c_int32),
-        ("force_own", ctypes.c_int32),
+        ("force_own", ctypes.c_int32), ("cmp_mode", ctypes.c_int32),
     ]
 
 
@@ -71,6 +72,13 @@ EXPORTS = {
     "speed3r_cmp_fused_topk": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "speed3r_redo_flag_count": (ctypes.c_int64, [ctypes.POINTER(Params)]),
+    "speed3r_cmp_lse_bound": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
+    "speed3r_cmp_single_topk": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_size_t] +
+                                [ctypes.c_void_p] * 6),
     "speed3r_topk": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]),
     "speed3r_sel_combine": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.c_void_p,
@@ -138,11 +146,12 @@ def _stream():
 
 def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
                 scale: float = 0.0, gates: Optional[torch.Tensor] = None,
-                forced_blocks: int = 0, force_own: bool = False) -> Params:
+                forced_blocks: int = 0, force_own: bool = False,
+                cmp_mode: int = CMP_AUTO) -> Params:
     """Params for [T, H, 64] bf16 or fp16 token tensors (one type for q, k, v; any token/head
     strides, last dim contiguous). ``forced_blocks`` key blocks 0..F-1 are selected for every
     query block on top of the top-k of the rest; with ``force_own`` each query block also
-    keeps its own key block."""
+    keeps its own key block. ``cmp_mode``: CMP_AUTO, CMP_TWO_PASS or CMP_SINGLE."""
     T, H, D = q.shape
     for x in (q, k, v):
         if x.dtype not in _DTYPES or x.dtype != q.dtype or tuple(x.shape) != (T, H, D) or \
@@ -154,7 +163,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, t
         gst = gates.stride(0)
     return Params(T, H, D, block, topk, float(scale), forced_blocks, q.stride(0), q.stride(1),
                   k.stride(0), k.stride(1), v.stride(0), v.stride(1), gst, _DTYPES[q.dtype],
-                  int(force_own))
+                  int(force_own), int(cmp_mode))
 
 
 def num_blocks(p: Params) -> int:
@@ -182,6 +191,21 @@ def dense_workspace_size(p: Params) -> int:
     return int(lib().speed3r_dense_workspace_size(ctypes.byref(p)))
 
 
+def runs_single(p: Params) -> bool:
+    """Whether the forward pass with these params runs the single compression pass: CMP_SINGLE,
+    or CMP_AUTO where the single pass applies (B <= 64, at most 64 chosen blocks, Nb >= 8) and
+    k <= 21 or at most 64 candidate blocks (the rule the library applies, include/speed3r.h)."""
+    Nb = num_blocks(p)
+    if Nb < 0:
+        raise ValueError("invalid params")
+    forced = min(p.forced_blocks, Nb)
+    most = min(p.topk, Nb - forced)
+    ok = p.block <= 64 and most <= 64 and Nb >= 8
+    if p.cmp_mode == CMP_SINGLE:
+        return ok
+    return ok and p.cmp_mode == CMP_AUTO and (3 * most <= 64 or Nb - forced <= 64)
+
+
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator hands out 512-byte aligned blocks, more than the 256 required
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -190,9 +214,10 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, sel_idx: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0,
-                    force_own: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                    force_own: bool = False, cmp_mode: int = CMP_AUTO
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Full forward pass. Returns (out [T, H, 64] in the input type, sel_idx or None)."""
-    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if workspace is None:
@@ -225,6 +250,22 @@ def cmp_fused_topk(p: Params, q, workspace, lse, o_cmp, sel_idx):
     _check("speed3r_cmp_fused_topk", lib().speed3r_cmp_fused_topk(
         ctypes.byref(p), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(lse), _ptr(o_cmp),
         _ptr(sel_idx), _stream()))
+
+
+def redo_flag_count(p: Params) -> int:
+    return int(lib().speed3r_redo_flag_count(ctypes.byref(p)))
+
+
+def cmp_lse_bound(p: Params, q, workspace, lse_bound):
+    _check("speed3r_cmp_lse_bound", lib().speed3r_cmp_lse_bound(
+        ctypes.byref(p), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(lse_bound),
+        _stream()))
+
+
+def cmp_single_topk(p: Params, q, workspace, lse_bound, lse, o_cmp, sel_idx, redo):
+    _check("speed3r_cmp_single_topk", lib().speed3r_cmp_single_topk(
+        ctypes.byref(p), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(lse_bound),
+        _ptr(lse), _ptr(o_cmp), _ptr(sel_idx), _ptr(redo), _stream()))
 
 
 def topk(p: Params, score, sel_idx):
@@ -269,9 +310,9 @@ class Trained:
 
 def sparse_attn_fwd_train(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                           forced_blocks: int = 0, workspace: Optional[torch.Tensor] = None,
-                          force_own: bool = False) -> Trained:
+                          force_own: bool = False, cmp_mode: int = CMP_AUTO) -> Trained:
     """Forward pass that keeps the state speed3r_sparse_attn_bwd needs."""
-    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
     out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     sel = torch.empty(q.shape[1], num_blocks(p), num_selected(p), dtype=torch.int32,
                       device=q.device)
@@ -333,11 +374,11 @@ def sparse_attn_fwd_windows(q, k, v, gates, block: int, topk: int, layout, scale
                             out: Optional[torch.Tensor] = None,
                             sel_idx: Optional[torch.Tensor] = None,
                             workspace: Optional[torch.Tensor] = None, forced_blocks: int = 0,
-                            force_own: bool = False
+                            force_own: bool = False, cmp_mode: int = CMP_AUTO
                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward pass with 2-D windows as blocks; out in the caller's token order, sel_idx over
     blocks of the window order."""
-    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own)
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
     w = make_windows(layout)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
@@ -353,7 +394,8 @@ class Stages:
     """Runs the forward pass one stage at a time and keeps every intermediate result:
     k_mean, v_mean [H, Nb, 64] f32, lse [H, T] f32, o_cmp [T, H, 64] f32,
     score [H, Nb, ld] f32, sel [H, Nb, k_eff] int32 (k_eff = forced prefix + chosen blocks),
-    o_sel [T, H, 64] f32, out (input type)."""
+    o_sel [T, H, 64] f32, out (input type); for the single compression pass also
+    lse_bound [H, T] f32 and redo (int32 flags, 4 per 256 queries per head)."""
 
     def __init__(self, q, k, v, gates, block: int, topk_: int, scale: float = 0.0,
                  keep_o_sel: bool = True, keep_score: bool = True, forced_blocks: int = 0,
@@ -378,6 +420,8 @@ class Stages:
         self.sel = torch.empty(H, self.Nb, self.k_eff, dtype=torch.int32, device=dev)
         self.o_sel = torch.empty(T, H, D, **f32) if keep_o_sel else None
         self.out = torch.empty(T, H, D, dtype=q.dtype, device=dev)
+        self.lse_bound = torch.empty(H, T, **f32)
+        self.redo = torch.empty(redo_flag_count(self.p), dtype=torch.int32, device=dev)
 
     def run_pool(self):
         pool(self.p, self.k, self.v, self.ws, self.k_mean, self.v_mean)
@@ -400,6 +444,22 @@ class Stages:
     @property
     def folds_topk(self) -> bool:
         return self.p.block <= 64 and min(self.topk, self.Nb - self.forced) <= 64
+
+    @property
+    def single_ok(self) -> bool:
+        """The single compression pass applies: folded selection and Nb >= 8."""
+        return self.folds_topk and self.Nb >= 8
+
+    def run_lse_bound(self, out=None):
+        cmp_lse_bound(self.p, self.q, self.ws, self.lse_bound if out is None else out)
+
+    def run_single_topk(self, lse_bound=None, sel=None, lse=None, o_cmp=None):
+        """The single compression pass (with its exact reruns) from lse_bound: writes lse,
+        o_cmp, the selection and the redo flags."""
+        cmp_single_topk(self.p, self.q, self.ws,
+                        self.lse_bound if lse_bound is None else lse_bound,
+                        self.lse if lse is None else lse, self.o_cmp if o_cmp is None else o_cmp,
+                        self.sel if sel is None else sel, self.redo)
 
     def run_sel(self, sel=None, o_cmp=None):
         sel_combine(self.p, self.q, self.ws, self.sel if sel is None else sel,

@@ -38,10 +38,11 @@ def test_status_strings():
     assert S.status_string(99) == "S3R_ERR_UNKNOWN"
 
 
-def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0, dtype=0, own=0):
+def params(T=1024, H=4, D=64, B=16, k=8, scale=0.0, st=None, forced=0, dtype=0, own=0,
+           mode=0):
     st = st or (H * D, D)
     return S.Params(T, H, D, B, k, scale, forced, st[0], st[1], st[0], st[1], st[0], st[1], 0,
-                    dtype, own)
+                    dtype, own, mode)
 
 
 def test_size_queries():
@@ -76,6 +77,8 @@ def test_size_queries():
     (dict(T=24577 * 16, B=16, k=65), S.S3R_ERR_UNSUPPORTED),  # > 24576 blocks, not folded
     (dict(forced=-1), S.S3R_ERR_INVALID_ARG),
     (dict(dtype=2), S.S3R_ERR_INVALID_ARG),
+    (dict(mode=3), S.S3R_ERR_INVALID_ARG),
+    (dict(mode=-1), S.S3R_ERR_INVALID_ARG),
 ])
 def test_bad_params_rejected_everywhere(kw, code):
     p = params(**kw)
@@ -89,12 +92,16 @@ def test_bad_params_rejected_everywhere(kw, code):
         L.speed3r_cmp_lse(ctypes.byref(p), FAKE, ws, big, FAKE, None),
         L.speed3r_cmp_fused(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, None),
         L.speed3r_cmp_fused_topk(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, None),
+        L.speed3r_cmp_lse_bound(ctypes.byref(p), FAKE, ws, big, FAKE, None),
+        L.speed3r_cmp_single_topk(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None),
         L.speed3r_topk(ctypes.byref(p), FAKE, FAKE, None),
         L.speed3r_sel_combine(ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, FAKE, None, None),
         L.speed3r_dense_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws, big, None),
     ]
     assert calls == [code] * len(calls)
     assert S.workspace_size(p) == 0 and S.num_blocks(p) == -1 and S.num_selected(p) == -1
+    assert S.redo_flag_count(p) == -1
 
 
 @pytest.mark.parametrize("T,B,k,F,n_sel", [
@@ -231,10 +238,45 @@ def test_window_forward_checks():
 
 
 def test_params_layout_matches_header():
-    """The ctypes mirror of s3r_params has the C layout: 96 bytes, dtype at offset 88."""
-    assert ctypes.sizeof(S.Params) == 96
+    """The ctypes mirror of s3r_params has the C layout: 104 bytes (int64 alignment), dtype
+    at offset 88, cmp_mode at 96."""
+    assert ctypes.sizeof(S.Params) == 104
     assert S.Params.dtype.offset == 88 and S.Params.gate_stride_t.offset == 80
-    assert S.Params.force_own.offset == 92
+    assert S.Params.force_own.offset == 92 and S.Params.cmp_mode.offset == 96
+
+
+def test_single_pass_limits():
+    """The single compression pass needs the folded selection (B <= 64, k_eff - F' <= 64) and
+    at least one group of 8 blocks; the forward pass refuses CMP_SINGLE elsewhere and the
+    automatic mode then takes the two passes."""
+    L = S.lib()
+    ws, big = ctypes.c_void_p(1 << 20), ctypes.c_size_t(1 << 40)
+    single = lambda p, redo=FAKE: L.speed3r_cmp_single_topk(  # noqa: E731
+        ctypes.byref(p), FAKE, ws, big, FAKE, FAKE, FAKE, FAKE, redo, None)
+    fwd = lambda p: L.speed3r_sparse_attn_fwd(  # noqa: E731
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, big, None)
+    for kw in (dict(B=128, T=4096), dict(k=65, T=100 * 64, B=64), dict(T=7 * 16, B=16)):
+        assert single(params(**kw)) == S.S3R_ERR_UNSUPPORTED
+        assert fwd(params(mode=S.CMP_SINGLE, **kw)) == S.S3R_ERR_UNSUPPORTED
+        # automatic and two-pass modes take the two passes: no redo flags in the workspace
+        assert S.workspace_size(params(**kw)) == S.workspace_size(
+            params(mode=S.CMP_TWO_PASS, **kw))
+    assert L.speed3r_cmp_lse_bound(ctypes.byref(params(T=7 * 16, B=16)), FAKE, ws, big, FAKE,
+                                   None) == S.S3R_ERR_UNSUPPORTED
+    p = params(T=8 * 16, B=16)  # one group: both apply
+    assert S.redo_flag_count(p) == 4 * 1 * 4
+    assert single(p, redo=None) == S.S3R_ERR_INVALID_ARG
+    assert single(p, redo=ctypes.c_void_p((1 << 20) + 4)) == S.S3R_ERR_INVALID_ARG
+    big_p = params(T=1_374_000, H=16, B=64, k=16)
+    assert S.redo_flag_count(big_p) == 16 * 5368 * 4
+    # the forward workspace holds the redo flags only when the single pass runs
+    two = S.workspace_size(params(T=1_374_000, H=16, B=64, k=16, mode=S.CMP_TWO_PASS))
+    assert S.workspace_size(big_p) == two + S.redo_flag_count(big_p) * 4
+    # automatic mode: the single pass for k <= 21 or when every candidate fits the list of 64
+    assert S.workspace_size(params(T=1_374_000, H=16, B=64, k=22)) == S.workspace_size(
+        params(T=1_374_000, H=16, B=64, k=22, mode=S.CMP_TWO_PASS))
+    assert S.workspace_size(params(T=60 * 64, B=64, k=30)) > S.workspace_size(
+        params(T=60 * 64, B=64, k=30, mode=S.CMP_TWO_PASS))
 
 
 def test_training_entry_points_validate_before_launching():
@@ -266,3 +308,20 @@ def test_training_entry_points_validate_before_launching():
     assert bwd(p, st=(4 * 64 + 4, 64)) == S.S3R_ERR_INVALID_ARG  # stride not a multiple of 8
     assert bwd(p, train=tw - 1) == S.S3R_ERR_WORKSPACE
     assert bwd(p, n=bw - 1) == S.S3R_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("T,B,k,F,own", [
+    (1_374_000, 64, 16, 0, 0), (1_374_000, 64, 22, 0, 0), (1_374_000, 64, 21, 22, 1),
+    (60 * 64, 64, 30, 0, 0), (7 * 16, 16, 4, 0, 0), (8 * 16, 16, 4, 0, 0), (4096, 128, 4, 0, 0),
+    (100 * 64, 64, 65, 0, 0), (100 * 64, 64, 30, 40, 0), (1000, 32, 5, 3, 1),
+])
+def test_runs_single_matches_the_library(T, B, k, F, own):
+    """The binding's rule for the automatic mode agrees with the library's choice (seen through
+    the workspace, which holds the redo flags only when the single pass runs)."""
+    for mode in (S.CMP_AUTO, S.CMP_TWO_PASS, S.CMP_SINGLE):
+        p = params(T=T, H=4, B=B, k=k, forced=F, own=own, mode=mode)
+        two = S.workspace_size(params(T=T, H=4, B=B, k=k, forced=F, own=own, mode=S.CMP_TWO_PASS))
+        got = S.workspace_size(p)
+        if mode == S.CMP_SINGLE and got == 0:
+            continue
+        assert S.runs_single(p) == (got > two), (mode, got, two)

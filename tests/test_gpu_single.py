@@ -1,0 +1,187 @@
+"""GPU parity of the single compression pass (speed3r_cmp_lse_bound + speed3r_cmp_single_topk)
+against the float64 oracle, and of its exact reruns.
+
+The single pass must give what the two exact passes give: the log-sum-exp and O_cmp to the
+same tolerances, and a selection that passes the same index-parity rule. Its failure paths
+are driven from the host through the bound it is handed: a bound above the true log-sum-exp
+fails every wave's Z check (so the exact passes rerun everywhere), a bound far below it makes
+Z_t leave [1, 2^15] (the same), and one moderately below it leaves every check to pass on
+large weights."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_global_attention_block_amd import speed3r as S
+from sparse_global_attention_block_amd import workloads as W
+from tests.helpers import check_out, check_selection, cuda_inputs, host, own_rows
+
+pytestmark = pytest.mark.gpu
+
+_tiny_s = W.WORKLOADS["tiny_s"]
+_v8 = W.WORKLOADS["v8"]
+CASES = {
+    # B = 16: four query blocks per wave; Nb = 64, every candidate fits the list of 64
+    "tiny_s": (_tiny_s, None),
+    # B = 64, Nb = 65 with a 26-token last block: one candidate more than the list holds
+    "v3_ragged": (_v8, 3 * 1374),
+    # B = 32: two query blocks per wave, Nb = 94
+    "b32_ragged": (dataclasses.replace(_tiny_s, name="b32", H=2, block=32, topk=5), 3000),
+    # B = 16 over 188 blocks
+    "b16_many": (dataclasses.replace(_tiny_s, name="b16", H=1, block=16, topk=6), 3000),
+    # 300 blocks of 64 in 14 views: the list of 64 holds a fifth of the candidates
+    "v14": (dataclasses.replace(_v8, name="v14", H=2), 14 * 1374),
+    "v14_fp16": (dataclasses.replace(_v8, name="v14_fp16", H=2, dtype="fp16"), 14 * 1374),
+    # a forced prefix and own blocks
+    "v14_ref_own": (dataclasses.replace(_v8, name="v14_ref_own", H=2, forced=22, own=True),
+                    14 * 1374),
+    "b32_forced_own": (dataclasses.replace(_tiny_s, name="b32_fo", H=2, block=32, topk=5,
+                                           forced=3, own=True), 3000),
+    # exactly one group of 8 blocks
+    "one_group": (dataclasses.replace(_tiny_s, name="one_group", H=2, block=64, topk=3), 8 * 64),
+}
+
+_cache = {}
+
+
+def run_case(name):
+    if name in _cache:
+        return _cache[name]
+    w, T = CASES[name]
+    print(f"[single {name}] T={T or w.T} H={w.H} B={w.block} k={w.topk} F={w.forced} "
+          f"own={w.own} {w.dtype}", flush=True)
+    x = cuda_inputs(w, T=T)
+    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, keep_score=False,
+                  forced_blocks=w.forced, force_own=w.own)
+    assert st.single_ok
+    st.run_pool()
+    st.run_lse_bound()
+    bound = st.lse_bound.clone()
+    st.run_single_topk()
+    torch.cuda.synchronize()
+    hx = {n: host(t) for n, t in x.items()}
+    ora = O.forward_all(hx["q"], hx["k"], hx["v"], hx["gates"], w.block, w.topk,
+                        forced=w.forced, own=w.own)
+    ora["bound"] = O.lse_group_bound(hx["q"], hx["k"], w.block)
+    _cache[name] = (w, x, st, bound, ora)
+    return _cache[name]
+
+
+def check_cmp(name, st, ora, w):
+    g = host(st.lse).double().numpy()
+    d = np.abs(g - ora["lse"])
+    assert d.max() < 1e-4, f"max |dLSE| {d.max():.3e}"
+    oc = host(st.o_cmp).double().numpy()
+    d = np.abs(oc - ora["ocmp"])
+    assert d.max() < 1e-2 and d.mean() < 1e-3, f"O_cmp max {d.max():.3e} mean {d.mean():.3e}"
+    frac, diff = check_selection(host(st.sel).numpy(), ora["score"], ora["sel"], w.topk,
+                                 forced=st.forced, qblocks=own_rows(w.H, st.Nb, st.own))
+    print(f"[{name}] rows held to exact index parity: {frac:.1%}, near-tie rows differing: "
+          f"{len(diff)}", flush=True)
+
+
+def valid_waves(st):
+    """Redo flags of the waves that hold at least one query (the others never fail)."""
+    T, H = st.q.shape[0], st.q.shape[1]
+    n_wg = -(-T // 256)
+    first = (np.arange(n_wg * 4) * 64)        # first query of each wave of one head
+    return np.tile(first < T, H)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_lse_bound(name):
+    """The bound pass against the oracle's group-mean bound, and below the exact LSE."""
+    w, x, st, bound, ora = run_case(name)
+    g = host(bound).double().numpy()
+    d = np.abs(g - ora["bound"])
+    assert d.max() < 1e-4, f"max |d bound| {d.max():.3e}"
+    assert (g <= ora["lse"] + 1e-4).all()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_single_pass_against_oracle(name):
+    w, x, st, bound, ora = run_case(name)
+    check_cmp(name, st, ora, w)
+    redo = host(st.redo).numpy()
+    print(f"[{name}] waves redone: {int((redo != 0).sum())} of {int(valid_waves(st).sum())} "
+          f"(log-sum-exp too: {int((redo & 2 != 0).sum())})", flush=True)
+    assert set(np.unique(redo)) <= {0, 1, 2, 3}
+    assert (redo[~valid_waves(st)] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["v14", "b32_forced_own", "tiny_s"])
+def test_bound_above_lse_reruns_everything(name):
+    """A 'bound' 0.5 above the true LSE makes Z < 1 for every query: every wave with queries
+    fails its Z check (flag bit 1) and the exact passes recompute everything."""
+    w, x, st, bound, ora = run_case(name)
+    high = torch.from_numpy(ora["lse"] + 0.5).float().cuda()
+    st.sel.fill_(-7)
+    st.o_cmp.fill_(float("nan"))
+    st.run_single_topk(lse_bound=high)
+    torch.cuda.synchronize()
+    redo = host(st.redo).numpy()
+    v = valid_waves(st)
+    assert ((redo[v] & 2) != 0).all() and (redo[~v] == 0).all()
+    check_cmp(name, st, ora, w)
+
+
+@pytest.mark.parametrize("name,drop", [("v14", 12.0), ("v3_ragged", 40.0), ("b16_many", 20.0),
+                                       ("v14_fp16", 100.0)])
+def test_far_low_bound_fails_the_z_check(name, drop):
+    """A bound 12-100 below the LSE (Z_t = e^12..e^100, past 2^15, up to f32 overflow): the
+    fp16 operands of P.V may overflow, the Z check fails everywhere, and the exact passes
+    give the results."""
+    w, x, st, bound, ora = run_case(name)
+    low = torch.from_numpy(ora["lse"] - drop).float().cuda()
+    st.run_single_topk(lse_bound=low)
+    torch.cuda.synchronize()
+    redo = host(st.redo).numpy()
+    v = valid_waves(st)
+    assert ((redo[v] & 2) != 0).all() and (redo[~v] == 0).all()
+    check_cmp(name, st, ora, w)
+
+
+@pytest.mark.parametrize("name", ["v14", "b16_many", "v14_fp16"])
+def test_low_bound_within_range(name):
+    """A bound 8 below the LSE (Z_t about e^8 = 2^11.5, inside [1, 2^15]): weights up to
+    2^11.5 pass P.V in fp16, the Z check holds, and the results stay those of the exact
+    method."""
+    w, x, st, bound, ora = run_case(name)
+    low = torch.from_numpy(ora["lse"] - 8.0).float().cuda()
+    st.run_single_topk(lse_bound=low)
+    torch.cuda.synchronize()
+    redo = host(st.redo).numpy()
+    assert ((redo & 2) == 0).all()
+    check_cmp(name, st, ora, w)
+    print(f"[{name}] waves redone: {int((redo != 0).sum())}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["v14", "v14_ref_own", "b32_ragged"])
+def test_uneven_bound(name):
+    """Each query's bound lowered by its own random amount in [0, 4): the upper bounds rank the
+    blocks differently from the scores, which the check must catch or survive."""
+    w, x, st, bound, ora = run_case(name)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    low = bound - 4.0 * torch.rand(bound.shape, device="cuda", generator=gen)
+    st.run_single_topk(lse_bound=low)
+    torch.cuda.synchronize()
+    check_cmp(name, st, ora, w)
+    print(f"[{name}] waves redone: {int((host(st.redo) != 0).sum())}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["v14", "v14_ref_own", "b32_forced_own", "v14_fp16"])
+def test_forward_single_vs_two_pass(name):
+    """The whole forward pass in either mode against the oracle's output and selection."""
+    w, x, st, bound, ora = run_case(name)
+    hx_out = ora["out"]
+    for mode in (S.CMP_SINGLE, S.CMP_TWO_PASS):
+        sel = torch.empty(w.H, st.Nb, st.k_eff, dtype=torch.int32, device="cuda")
+        out, _ = S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk,
+                                   sel_idx=sel, forced_blocks=w.forced, force_own=w.own,
+                                   cmp_mode=mode)
+        torch.cuda.synchronize()
+        check_selection(host(sel).numpy(), ora["score"], ora["sel"], w.topk, forced=st.forced,
+                        qblocks=own_rows(w.H, st.Nb, st.own))
+        check_out(out, hx_out, what=f"out mode {mode}")
