@@ -57,6 +57,9 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   static_assert(kRecsPerWave * kWaves == kRecs, "each wave copies whole records");
   constexpr int kNtPerQB = 4 / kQB;
   __shared__ uint4 lds[kRing][kRecs * 64];
+  // (single pass) each lane's parts of Z_t for its 4 column tiles: read, added to and written
+  // back once per tile, so that no register holds them through the logits
+  __shared__ floatx4 zpart[kBound ? kWaves : 1][64];
 
   const int64_t n_qtiles = (a.T + kQueries - 1) / kQueries;
   const int64_t total = (int64_t)a.H * n_qtiles;
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     }
     lsum[nt] = 0.f;
   }
+  if constexpr (kBound) zpart[wave][lane] = floatx4{0.f, 0.f, 0.f, 0.f};  // this lane's own
   // running top-k: lane e holds entry e (score, block index) of each query block's list;
   // th_v / th_j mirror entry K-1 (the current k-th best) in scalar registers
   float tk_v[kQB], th_v[kQB];
@@ -246,7 +250,11 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
           for (int r = 0; r < 4; ++r)
             p[s2][nt][r] = fast_exp2(acc[s2][nt][r] - off[nt]);
       if constexpr (kBound) {
-        // this lane's part of Z_t
+        // this lane's part of Z_t; the empty asm ties the LDS read to the weights, so that
+        // the compiler cannot hoist it (and the 4 registers) above the logits
+        int zl = lane;
+        asm volatile("" : "+v"(zl) : "v"(p[1][3][3]));
+        floatx4 zz = zpart[wave][zl];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           float z = p[0][nt][0];
@@ -254,8 +262,9 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
           for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int r = (s2 == 0 ? 1 : 0); r < 4; ++r) z += p[s2][nt][r];
-          lsum[nt] += z;
+          zz[nt] += z;
         }
+        zpart[wave][zl] = zz;
       }
       // column sums over the queries of each query block
       float tots[kQB];
@@ -470,7 +479,8 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       float L2[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        float z = lsum[nt] + __shfl_xor(lsum[nt], 16);
+        float z = zpart[wave][lane][nt];
+        z += __shfl_xor(z, 16);
         z += __shfl_xor(z, 32);
         const int64_t t = q0 + 16 * nt + li;
         zfail |= t < a.T && !(z >= 1.0f && z <= 0x1p15f);
