@@ -266,8 +266,10 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         }
         zpart[wave][zl] = zz;
       }
-      // column sums over the queries of each query block
+      // column sums over the queries of each query block (the single pass's are only upper
+      // bounds: it adds the packed fp16 weights, and its check allows for their rounding)
       float tots[kQB];
+      halfx8 hs[kQB];
       auto column_sums = [&]() {
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
@@ -288,17 +290,26 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       for (int nt = 0; nt < 4; ++nt) {
         const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
                                  p[1][nt][0], p[1][nt][1], p[1][nt][2], p[1][nt][3]);
+        if constexpr (kBound) hs[nt / kNtPerQB] = (nt % kNtPerQB == 0) ? pb : hs[nt / kNtPerQB] + pb;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const halfx8 vt = *reinterpret_cast<const halfx8*>(&L[512 + mt * 64 + lane]);
           o[mt][nt] = mfma16h(vt, pb, o[mt][nt]);
         }
       }
-      column_sums();
+      if constexpr (kBound) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) tots[qb] = row_reduce_scatter8_h(hs[qb], lane);
+      } else {
+        column_sums();
+      }
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
         const float tot = tots[qb];
-        const int64_t qblk = (q0 + 16 * qb * kNtPerQB) / a.B;
+        // single pass: B = 64 / kQB (a shift; the division stays in the exact kernels, whose
+        // register allocation it happens to suit)
+        const int64_t qblk = kBound ? (q0 + 16 * qb * kNtPerQB) / (64 / kQB)
+                                    : (q0 + 16 * qb * kNtPerQB) / a.B;
         if constexpr (kTopk) {
           if (qblk < a.Nb) {
             // lanes with bit 1 clear hold the 32 distinct keys of this tile; a block can only
@@ -415,11 +426,14 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), kth));
     // Every block outside the list has a bound <= the list's last entry th_v (it fell below
     // the threshold of its tile, was pushed out from the last place, or tied with it), and
-    // the threshold only rises. With at most 64 candidates every one is listed. The sums of
-    // the bounds and of the exact scores round in different orders: 2^-12 margin.
+    // the threshold only rises. With at most 64 candidates every one is listed. A bound is a
+    // sum of fp16-rounded weights taken in fp16: each of its 64 terms passes at most 6
+    // roundings of 2^-11 relative (packing, 3 sums over column tiles, 2 halvings of the lane
+    // reduction), 6 * 2^-11 < 2^-8 in all, and the at most 136 roundings of values below 2^-14
+    // add at most 2^-25 each, < 2^-17 in all.
     const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
     const float rmax = nc <= Kc ? -1.0f : th_v[qi];
-    fail |= !(at != 0 && (rmax < 0.f || rmax * (1.0f + 0x1p-12f) < sk));
+    fail |= !(at != 0 && (rmax < 0.f || rmax * (1.0f + 0x1p-8f) + 0x1p-17f < sk));
     tk_j[qi] = __builtin_amdgcn_ds_permute(4 * rank, j);  // entry of exact rank e to lane e
   };
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace s3r {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -181,6 +183,36 @@ __device__ __forceinline__ float row_reduce_scatter8(const float (&v)[2][4], int
   const float keep = b0 ? b[1] : b[0];
   const float send = b0 ? b[0] : b[1];
   const float c = keep + dpp<kDppXor1>(send);
+  return c + dpp<kDppXor2>(c);
+}
+
+// row_reduce_scatter8 on fp16 values packed as pack8h packs them (element e: v[e/4][e%4]):
+// the first two halvings add packed pairs, the last two run in f32. Each fp16 addition rounds
+// to 2^-11 relative (2^-25 absolute below 2^-14).
+__device__ __forceinline__ float row_reduce_scatter8_h(const halfx8& v, int lane) {
+  typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+  const bool b3 = lane & 8, b2 = lane & 4, b0 = lane & 1;
+  auto word = [&](int i) { return __builtin_bit_cast(uint32_t, halfx2{v[2 * i], v[2 * i + 1]}); };
+  auto dpp_u = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  auto add = [](uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(halfx2, a) + __builtin_bit_cast(halfx2, b));
+  };
+  uint32_t a[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const uint32_t keep = b3 ? word(2 + x) : word(x);
+    const uint32_t send = b3 ? word(x) : word(2 + x);
+    a[x] = add(keep, dpp_u(send, std::integral_constant<int, kDppRor8>{}));
+  }
+  const uint32_t keep = b2 ? a[1] : a[0];
+  const uint32_t send = b2 ? a[0] : a[1];
+  const halfx2 b = __builtin_bit_cast(halfx2, add(keep, dpp_u(send, std::integral_constant<int, kDppHalfMirror>{})));
+  const float lo = (float)b[0], hi = (float)b[1];
+  const float k0 = b0 ? hi : lo;
+  const float s0 = b0 ? lo : hi;
+  const float c = k0 + dpp<kDppXor1>(s0);
   return c + dpp<kDppXor2>(c);
 }
 
