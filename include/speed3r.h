@@ -68,7 +68,7 @@ typedef enum { S3R_BF16 = 0, S3R_FP16 = 1 } s3r_dtype;
  *                     (speed3r_cmp_lse_bound, then speed3r_cmp_single_topk), with the two
  *                     exact passes rerun where its check fails. Needs the folded selection
  *                     (B <= 64, n_sel - F' <= 64) and Nb >= 8; S3R_ERR_UNSUPPORTED otherwise.
- *   S3R_CMP_AUTO      (0) the single pass where it applies and k <= 21 (or every candidate
+ *   S3R_CMP_AUTO      (0) the single pass where it applies and k <= 32 (or every candidate
  *                     block fits its list of 64), the two passes otherwise. */
 typedef enum { S3R_CMP_AUTO = 0, S3R_CMP_TWO_PASS = 1, S3R_CMP_SINGLE = 2 } s3r_cmp_mode;
 

@@ -39,6 +39,8 @@ CASES = {
                     14 * 1374),
     "b32_forced_own": (dataclasses.replace(_tiny_s, name="b32_fo", H=2, block=32, topk=5,
                                            forced=3, own=True), 3000),
+    # k = 32: the list of 64 holds only 2k, so more query blocks fail the check and rerun
+    "v14_k32": (dataclasses.replace(_v8, name="v14_k32", H=2, topk=32), 14 * 1374),
     # exactly one group of 8 blocks
     "one_group": (dataclasses.replace(_tiny_s, name="one_group", H=2, block=64, topk=3), 8 * 64),
 }
