@@ -210,16 +210,21 @@ def test_selection_branch_on_oracle_indices(name):
     check_out(st.out, ora["out"])
 
 
+@pytest.mark.parametrize("mode", ["two_pass", "single"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_end_to_end(name):
-    """speed3r_sparse_attn_fwd against the oracle; rows where a near-tie flipped the chosen
-    set are compared with the oracle run on the GPU's own indices."""
+def test_end_to_end(name, mode):
+    """speed3r_sparse_attn_fwd with either compression mode against the oracle; rows where a
+    near-tie flipped the chosen set are compared with the oracle run on the GPU's own
+    indices."""
     w, x, hx, st, ora = run_case(name)
+    if mode == "single" and not st.single_ok:
+        pytest.skip("the single pass needs B <= 64, at most 64 chosen blocks and Nb >= 8")
     Nb = st.Nb
     k_eff = st.k_eff
     sel = torch.empty(w.H, Nb, k_eff, dtype=torch.int32, device="cuda")
     out, _ = S.sparse_attn_fwd(x["q"], x["k"], x["v"], x["gates"], w.block, w.topk, sel_idx=sel,
-                               forced_blocks=w.forced, force_own=w.own)
+                               forced_blocks=w.forced, force_own=w.own,
+                               cmp_mode=S.CMP_SINGLE if mode == "single" else S.CMP_TWO_PASS)
     torch.cuda.synchronize()
     gsel = host(sel).numpy()
     ref = ora["out"]
@@ -232,9 +237,13 @@ def test_end_to_end(name):
         ref = np.ascontiguousarray(r["out"].reshape(w.H, Nb * w.block, 64)[:, :T]
                                    .transpose(1, 0, 2))
     mx, mean = check_out(out, ref)
-    print(f"[{name}] out max-abs {mx:.3e} mean-abs {mean:.3e}")
-    # the fused entry point runs the same kernels as the staged path: same indices
-    np.testing.assert_array_equal(gsel, host(st.sel).numpy())
+    print(f"[{name}] {mode} out max-abs {mx:.3e} mean-abs {mean:.3e}")
+    if mode == "two_pass":
+        # the entry point runs the same kernels as the staged path: same indices
+        np.testing.assert_array_equal(gsel, host(st.sel).numpy())
+    else:
+        check_selection(gsel, ora["score"], ora["sel"], w.topk, forced=st.forced,
+                        qblocks=own_rows(w.H, Nb, st.own))
 
 
 def test_deterministic_and_strided_inputs():
