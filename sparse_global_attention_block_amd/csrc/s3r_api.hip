@@ -235,7 +235,7 @@ TrainLayout train_layout(const Dims& d) {
 // Backward workspace: operand tiles, per-token scalars, pooled gradients, selection bitmap
 // and the per-token gate gradients (reduced per head when the gates are per head).
 struct BwdLayout {
-  size_t qtiles, raw_bwd, pooled_bwd, qs, dkc, dvc, bitmap, dg_tok, end;
+  size_t qtiles, raw_bwd, pooled_bwd, qs, dkc, dvc, dkv_part, bitmap, dg_tok, end;
   int64_t bm_words;
 };
 
@@ -249,6 +249,7 @@ BwdLayout bwd_layout(const Dims& d) {
   B.qs = off; off += align256((size_t)d.H * d.T * 8 * sizeof(float));
   B.dkc = off; off += align256((size_t)d.H * d.Nb * kD * sizeof(float));
   B.dvc = off; off += align256((size_t)d.H * d.Nb * kD * sizeof(float));
+  B.dkv_part = off; off += 2 * align256((size_t)kDkvParts * d.H * d.Nb * kD * sizeof(float));
   B.bitmap = off; off += align256((size_t)d.H * d.Nb * B.bm_words * sizeof(uint32_t));
   B.dg_tok = off; off += align256((size_t)d.T * d.H * 2 * sizeof(float));
   B.end = off;
@@ -684,6 +685,9 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
   b.sel = (const int32_t*)(tw + L.sel); b.n_sel = (int32_t)d.k_eff;
   b.bitmap = (const uint32_t*)(ws + BL.bitmap); b.bm_words = BL.bm_words;
   b.dkc = (float*)(ws + BL.dkc); b.dvc = (float*)(ws + BL.dvc);
+  b.dkc_part = (float*)(ws + BL.dkv_part);
+  b.dvc_part = (float*)(ws + BL.dkv_part +
+                        align256((size_t)kDkvParts * d.H * d.Nb * kD * sizeof(float)));
   b.dq = dq; b.dk = dk; b.dv = dv;
 
   // selection bitmap (cleared with a kernel, not a memset)

@@ -356,8 +356,11 @@ hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------
 // Compression dKc, dVc. A work-group of kWaves waves owns kWaves pooled tiles (32 pooled keys
-// per wave, held as B operands: K hi, K lo, Vc rows) and streams every query tile of the head
-// (its 8 KB of row images + the 32 queries' scalars) through a 2-slot LDS ring. Per query tile: S (queries x
+// per wave, held as B operands: K hi, K lo, Vc rows) and streams one of kDkvParts equal parts
+// of the head's query tiles (its 8 KB of row images + the 32 queries' scalars) through a
+// 2-slot LDS ring, writing its partial sums; dkv_combine adds the parts in order. (One work-
+// group fills a CU: with the query tiles split, 16 heads x 84 groups make 21 full rounds of
+// 256 CUs instead of 5.25.) Per query tile: S (queries x
 // keys, so that P^T and dS^T come out with queries in the k-slots), dP = dout . Vc^T,
 // dVc += (g0 P)^T . dout, dKc += dS^T . q.
 // ---------------------------------------------------------------------------------------
@@ -375,10 +378,12 @@ cmp_dkv_kernel(BwdArgs a) {
   static_assert(kDkvAhead == 1 || kDkvAhead == 2, "one or two tiles in flight");
   __shared__ uint4 lds[2][kQU4 + kSU4];
   const int64_t n_groups = (a.n_ctiles + kWaves - 1) / kWaves;
-  const int64_t total = (int64_t)a.H * n_groups;
+  const int64_t total = (int64_t)a.H * kDkvParts * n_groups;
   const int64_t logical = xcd_logical_id(blockIdx.x, total);
   if (logical >= total) return;
-  const int h = (int)(logical / n_groups);
+  // consecutive work-groups (one XCD) share a head and a part: they stream the same tiles
+  const int h = (int)(logical / (kDkvParts * n_groups));
+  const int part = (int)(logical / n_groups % kDkvParts);
   const int64_t grp = logical % n_groups;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
@@ -411,6 +416,7 @@ cmp_dkv_kernel(BwdArgs a) {
     }
 
   const int64_t n = a.n_ktiles;  // query tiles
+  const int64_t t_begin = part * n / kDkvParts, t_end = (part + 1) * n / kDkvParts;
   const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) + (int64_t)h * n * kQU4;
   const float* qs = a.qs + (int64_t)h * a.T * 8;
   // Only the row images R(q), R(dout) (8 KB) are read; each thread scatters its 16-byte
@@ -520,16 +526,16 @@ cmp_dkv_kernel(BwdArgs a) {
     stash(st, (int)((tau + 1) & 1));
     lds_barrier();
   };
-  fetch(0, 0);
-  stash(0, 0);
-  if constexpr (kDkvAhead == 2) fetch(0, 1);
+  fetch(0, t_begin);
+  stash(0, (int)(t_begin & 1));
+  if constexpr (kDkvAhead == 2) fetch(0, t_begin + 1);
   lds_barrier();
   if constexpr (kDkvAhead == 1) {
-    for (int64_t tau = 0; tau < n; ++tau) body(tau, 0, 0);
+    for (int64_t tau = t_begin; tau < t_end; ++tau) body(tau, 0, 0);
   } else {
-    for (int64_t tau = 0; tau < n; tau += 2) {
+    for (int64_t tau = t_begin; tau < t_end; tau += 2) {
       body(tau, 1, 0);
-      if (tau + 1 < n) body(tau + 1, 0, 1);
+      if (tau + 1 < t_end) body(tau + 1, 0, 1);
     }
   }
   if (!active) return;
@@ -541,18 +547,42 @@ cmp_dkv_kernel(BwdArgs a) {
       if (j >= a.Nb) continue;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int64_t o = ((int64_t)h * a.Nb + j) * kD + 16 * mt + li;
-        a.dkc[o] = a.scale * dK[s][mt][r];
-        a.dvc[o] = dV[s][mt][r];
+        const int64_t o = ((int64_t)part * a.H * a.Nb + (int64_t)h * a.Nb + j) * kD + 16 * mt + li;
+        a.dkc_part[o] = dK[s][mt][r];
+        a.dvc_part[o] = dV[s][mt][r];
       }
     }
 }
 
+// dKc = scale * (part 0 + part 1 + ...), dVc likewise, in that order (repeatable bits)
+__global__ __launch_bounds__(256) void dkv_combine_kernel(BwdArgs a, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4* pk = reinterpret_cast<const float4*>(a.dkc_part) + i;
+  const float4* pv = reinterpret_cast<const float4*>(a.dvc_part) + i;
+  float4 k = pk[0], v = pv[0];
+#pragma unroll
+  for (int p = 1; p < kDkvParts; ++p) {
+    const float4 k2 = pk[p * n4], v2 = pv[p * n4];
+    k.x += k2.x; k.y += k2.y; k.z += k2.z; k.w += k2.w;
+    v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+  }
+  reinterpret_cast<float4*>(a.dkc)[i] =
+      make_float4(a.scale * k.x, a.scale * k.y, a.scale * k.z, a.scale * k.w);
+  reinterpret_cast<float4*>(a.dvc)[i] = v;
+}
+
 hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.H * ((a.n_ctiles + kDkvWaves - 1) / kDkvWaves);
+  const int64_t total =
+      (int64_t)a.H * kDkvParts * ((a.n_ctiles + kDkvWaves - 1) / kDkvWaves);
   const dim3 g3((unsigned)(((total + 7) / 8) * 8)), b3(64 * kDkvWaves);
   if (a.half) hipLaunchKernelGGL((cmp_dkv_kernel<kDkvWaves, true>), g3, b3, 0, s, a);
   else hipLaunchKernelGGL((cmp_dkv_kernel<kDkvWaves, false>), g3, b3, 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n4 = (int64_t)a.H * a.Nb * kD / 4;
+  hipLaunchKernelGGL(dkv_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a,
+                     n4);
   return hipGetLastError();
 }
 

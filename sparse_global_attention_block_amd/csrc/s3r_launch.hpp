@@ -177,6 +177,8 @@ struct BwdArgs {
   const int32_t* sel; int32_t n_sel;
   const uint32_t* bitmap; int64_t bm_words;  // [H][Nb][bm_words]: bit i of row u = i selected u
   float* dkc; float* dvc;           // [H][Nb][64]
+  float* dkc_part; float* dvc_part; // [kDkvParts][H][Nb][64]: cmp_dkv's sums over each part
+                                    // of the query tiles, added in order into dkc, dvc
   float* dq; float* dk; float* dv;  // [T][H][64]
 };
 
@@ -186,7 +188,8 @@ hipError_t launch_gate_reduce(const float* dg_tok, int64_t T, int32_t H, float* 
                               hipStream_t s);
 hipError_t launch_sel_bitmap(const BwdArgs& a, uint32_t* bitmap, hipStream_t s);
 hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s);
-hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s);
+hipError_t launch_cmp_dkv(const BwdArgs& a, hipStream_t s);  // also adds its parts
+constexpr int kDkvParts = 4;  // cmp_dkv work-groups per (head, group of pooled tiles)
 hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_sel_dkv(const BwdArgs& a, hipStream_t s);
 
