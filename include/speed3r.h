@@ -272,7 +272,8 @@ s3r_status speed3r_sparse_attn_fwd_train(const s3r_params* p, const void* q, con
 
 /* Bytes of scratch speed3r_sparse_attn_bwd needs: operand tiles of q, dout, k, v and the
  * block means, per-token scalars, the pooled gradients, a [H][Nb][ceil(Nb/32)] selection
- * bitmap and per-token gate gradients (about 19 GB at T = 1,374,000, H = 16, B = 64). */
+ * bitmap, per-token gate gradients and four partial sums of the pooled gradients (about
+ * 19.7 GB at T = 1,374,000, H = 16, B = 64). */
 size_t speed3r_bwd_workspace_size(const s3r_params* p);
 
 /* Gradients of the sparse forward pass. q, k, v, gates and p must be those of the
