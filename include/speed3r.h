@@ -217,9 +217,10 @@ s3r_status speed3r_cmp_lse_bound(const s3r_params* p, const void* q, const void*
  *   (1 + 2^-12) is below the k-th exact score, so that no unlisted block can belong to the
  *   top k. redo (int32 [H * ceil(T/256)][4], speed3r_redo_flag_count entries, 16-byte
  *   aligned; one per wave) receives bit 1 where the first check failed and bit 0 where the
- *   second did. Then, in the same call, speed3r_cmp_lse reruns on the 256 queries around
- *   each wave with bit 1, and speed3r_cmp_fused_topk on those around any flagged wave, so
- *   every output ends as the two exact passes would give it. Requires B <= 64,
+ *   second did. Then, in the same call, speed3r_cmp_lse and speed3r_cmp_fused_topk rerun on
+ *   the 256 queries around each wave with bit 1, and the selection part of
+ *   speed3r_cmp_fused_topk (not O_cmp, which stands) on those around a wave with bit 0 only,
+ *   so every output ends as the two exact passes would give it. Requires B <= 64,
  *   n_sel - F' <= 64 and Nb >= 8 (S3R_ERR_UNSUPPORTED otherwise). */
 s3r_status speed3r_cmp_single_topk(const s3r_params* p, const void* q, const void* workspace,
                                    size_t workspace_bytes, const float* lse_bound, float* lse,

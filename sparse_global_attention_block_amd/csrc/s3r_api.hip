@@ -206,12 +206,15 @@ s3r_status run_single(CmpArgs a, const float* lse_bound, float* lse, int32_t* re
   if ((st = hip_status(launch_cmp_single_topk(a, stream))) != S3R_OK) return st;
   a.redo_out = nullptr;
   a.redo_in = redo;
-  a.redo_mask = 2;  // the log-sum-exp again where the Z check failed
+  a.redo_mask = 2;  // where a Z check failed: the log-sum-exp, then everything of pass 2
+  a.redo_skip = 0;
   a.lse_bias = 0.f;
-  if ((st = hip_status(launch_cmp_rerun(a, stream, false))) != S3R_OK) return st;
-  a.redo_mask = 3;  // probabilities, O_cmp and the selection where either check failed
+  if ((st = hip_status(launch_cmp_rerun(a, stream, false, false))) != S3R_OK) return st;
   a.lse_in = lse;
-  return hip_status(launch_cmp_rerun(a, stream, true));
+  if ((st = hip_status(launch_cmp_rerun(a, stream, true, false))) != S3R_OK) return st;
+  a.redo_mask = 1;  // where only a selection was not proven: the scores and the top-k
+  a.redo_skip = 2;
+  return hip_status(launch_cmp_rerun(a, stream, true, true));
 }
 
 // Regions the training forward pass adds after the forward workspace: what the backward

@@ -44,15 +44,18 @@ constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 // kBound (with kTopk): the single pass over the pooled tokens described below.
 // kDeep: tiles in flight for the exact reruns after the single pass, where a few lone
 // work-groups sweep all tiles and the latency of each copy, not the chip's throughput, decides.
+// kScoresOnly (rerun of pass 2 with the running top-k where only the single pass's selection
+// was not proven: its O_cmp stands): no V^T records, no P.V, no O_cmp write.
 template <bool kFused, int kQB, int kWaves, bool kTopk = false, bool kHalf = false,
-          bool kBound = false, int kDeep = 0>
+          bool kBound = false, int kDeep = 0, bool kScoresOnly = false>
 // (second bound: resident waves per SIMD the register allocation must allow)
 __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArgs a) {
   static_assert(!kBound || (kFused && kTopk), "the single pass keeps the running top-k");
   constexpr int kAhead = kDeep ? kDeep : (kFused ? kFusedAhead : kLseAhead);  // tiles in flight
   constexpr int kRing = kAhead + 1;
   constexpr int kQueries = 64 * kWaves;
-  constexpr int kRecs = kFused ? 12 : 8;  // records of a tile this pass reads
+  static_assert(!kScoresOnly || (kFused && kTopk && !kBound), "a rerun of the top-k pass");
+  constexpr int kRecs = (kFused && !kScoresOnly) ? 12 : 8;  // records of a tile this pass reads
   constexpr int kRecsPerWave = kRecs / kWaves;
   static_assert(kRecsPerWave * kWaves == kRecs, "each wave copies whole records");
   constexpr int kNtPerQB = 4 / kQB;
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   if (logical >= total) return;
   if (a.redo_in) {  // exact rerun of the work-groups the single pass flagged
     const int4 f = *reinterpret_cast<const int4*>(a.redo_in + 4 * logical);
-    if (((f.x | f.y | f.z | f.w) & a.redo_mask) == 0) return;
+    const int any = f.x | f.y | f.z | f.w;
+    if ((any & a.redo_mask) == 0 || (any & a.redo_skip) != 0) return;
   }
   const int h = (int)(logical / n_qtiles);
   const int64_t qt = logical % n_qtiles;
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         }
       };
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < (kScoresOnly ? 0 : 4); ++nt) {
         const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
                                  p[1][nt][0], p[1][nt][1], p[1][nt][2], p[1][nt][3]);
         if constexpr (kBound) hs[nt / kNtPerQB] = (nt % kNtPerQB == 0) ? pb : hs[nt / kNtPerQB] + pb;
@@ -533,7 +537,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < (kScoresOnly ? 0 : 4); ++nt) {
       const int64_t t = q0 + 16 * nt + li;
       if (t < a.T) {
 #pragma unroll
@@ -590,16 +594,22 @@ static hipError_t launch_single_t(const CmpArgs& a, hipStream_t s) {
 
 constexpr int kRerunAhead = 3;
 
+template <bool kHalf, bool kScoresOnly>
+static void launch_rerun_fused(const CmpArgs& a, hipStream_t s) {
+  const dim3 g3 = cmp_grid(a, kFusedWaves), b4(64 * 4);
+  switch (a.B) {
+    case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, kHalf, false, kRerunAhead, kScoresOnly>), g3, b4, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, kHalf, false, kRerunAhead, kScoresOnly>), g3, b4, 0, s, a); break;
+    default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, kHalf, false, kRerunAhead, kScoresOnly>), g3, b4, 0, s, a); break;
+  }
+}
+
 template <bool kHalf>
-static hipError_t launch_rerun_t(const CmpArgs& a, hipStream_t s, bool fused) {
+static hipError_t launch_rerun_t(const CmpArgs& a, hipStream_t s, bool fused, bool scores_only) {
   const dim3 b4(64 * 4);
   if (fused) {
-    const dim3 g3 = cmp_grid(a, kFusedWaves);
-    switch (a.B) {
-      case 16: hipLaunchKernelGGL((cmp_kernel<true, 4, kFusedWaves, true, kHalf, false, kRerunAhead>), g3, b4, 0, s, a); break;
-      case 32: hipLaunchKernelGGL((cmp_kernel<true, 2, kFusedWaves, true, kHalf, false, kRerunAhead>), g3, b4, 0, s, a); break;
-      default: hipLaunchKernelGGL((cmp_kernel<true, 1, kFusedWaves, true, kHalf, false, kRerunAhead>), g3, b4, 0, s, a); break;
-    }
+    if (scores_only) launch_rerun_fused<kHalf, true>(a, s);
+    else launch_rerun_fused<kHalf, false>(a, s);
   } else {
     hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false, kHalf, false, kRerunAhead>),
                        cmp_grid(a, kLseWaves), b4, 0, s, a);
@@ -619,8 +629,9 @@ hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s) {
 hipError_t launch_cmp_single_topk(const CmpArgs& a, hipStream_t s) {
   return a.half ? launch_single_t<true>(a, s) : launch_single_t<false>(a, s);
 }
-hipError_t launch_cmp_rerun(const CmpArgs& a, hipStream_t s, bool fused) {
-  return a.half ? launch_rerun_t<true>(a, s, fused) : launch_rerun_t<false>(a, s, fused);
+hipError_t launch_cmp_rerun(const CmpArgs& a, hipStream_t s, bool fused, bool scores_only) {
+  return a.half ? launch_rerun_t<true>(a, s, fused, scores_only)
+                : launch_rerun_t<false>(a, s, fused, scores_only);
 }
 
 }  // namespace s3r

@@ -47,8 +47,9 @@ struct CmpArgs {
   int32_t topk;            // k (chosen per row, clamped to the candidates)
   int32_t own;             // each query block also keeps its own block
   float lse_bias;          // added to every log-sum-exp the LSE pass writes (natural log)
-  const int32_t* redo_in;  // if set: only work-groups with a flag & redo_mask of their 4 run
-  int32_t redo_mask;
+  const int32_t* redo_in;  // if set: only work-groups whose 4 flags, or-ed, meet redo_mask and
+  int32_t redo_mask;       // miss redo_skip run
+  int32_t redo_skip;
   int32_t* redo_out;       // single pass: [work-group][4 waves], bit 0 = selection not proven,
                            // bit 1 = Z check failed (the log-sum-exp must be recomputed)
 };
@@ -199,8 +200,9 @@ hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_single_topk(const CmpArgs& a, hipStream_t s);
-// the exact passes on the work-groups redo_in flags (fused: pass 2 with the running top-k)
-hipError_t launch_cmp_rerun(const CmpArgs& a, hipStream_t s, bool fused);
+// the exact passes on the work-groups redo_in flags (fused: pass 2 with the running top-k;
+// scores_only: without P.V and O_cmp)
+hipError_t launch_cmp_rerun(const CmpArgs& a, hipStream_t s, bool fused, bool scores_only);
 constexpr int kFusedTopkMaxK = 64;  // the running top-k keeps one entry per lane
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sel(const AttnArgs& a, hipStream_t s);
