@@ -434,7 +434,8 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     // sum of fp16-rounded weights taken in fp16: each of its 64 terms passes at most 6
     // roundings of 2^-11 relative (packing, 3 sums over column tiles, 2 halvings of the lane
     // reduction), 6 * 2^-11 < 2^-8 in all, and the at most 136 roundings of values below 2^-14
-    // add at most 2^-25 each, < 2^-17 in all.
+    // add at most 2^-25 each, < 2^-17 in all (fp16 subnormals are kept: the kernels run with
+    // f16 denormals on, the compiler's default; flushing them would cost up to 2^-14 each).
     const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
     const float rmax = nc <= Kc ? -1.0f : th_v[qi];
     fail |= !(at != 0 && (rmax < 0.f || rmax * (1.0f + 0x1p-8f) + 0x1p-17f < sk));
