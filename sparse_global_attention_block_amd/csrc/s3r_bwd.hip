@@ -368,6 +368,8 @@ constexpr int kDkvWaves = 8;
 constexpr int kDkvAhead = 1;  // query tiles in flight beyond the one being computed on (2 is
                               // built and measured 5 % slower)
 
+__device__ __forceinline__ int tr_swizzle(int l) { return l ^ ((l >> 3) & 7); }
+
 template <int kWaves, bool kHalf>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
 cmp_dkv_kernel(BwdArgs a) {
@@ -421,7 +423,12 @@ cmp_dkv_kernel(BwdArgs a) {
   const float* qs = a.qs + (int64_t)h * a.T * 8;
   // Only the row images R(q), R(dout) (8 KB) are read; each thread scatters its 16-byte
   // chunks into the transposed images TR(q), TR(dout) while staging, which halves the bytes
-  // streamed.
+  // streamed. In LDS the TR records are swizzled (lane l's 16 bytes at slot tr_swizzle(l)):
+  // each 2-byte store instruction has every lane write the same dim modulo 8, which in the
+  // plain layout puts all 64 lanes in 2 of the 32 banks; the swizzle spreads them over 16,
+  // and it only permutes slots inside aligned groups of 8, so the operand reads stay free of
+  // conflicts.
+  const int tr_lane = tr_swizzle(lane);
   int rsrc[kChunks], tr_pos[kChunks][8];
 #pragma unroll
   for (int x = 0; x < kChunks; ++x) {
@@ -434,7 +441,7 @@ cmp_dkv_kernel(BwdArgs a) {
     for (int j = 0; j < 8; ++j) {
       int trec, tlane, tslot;
       vt_position(m, d0 + j, trec, tlane, tslot);
-      tr_pos[x][j] = trbase * 8 + (trec * 64 + tlane) * 8 + tslot;  // in u16 units
+      tr_pos[x][j] = trbase * 8 + (trec * 64 + tr_swizzle(tlane)) * 8 + tslot;  // u16 units
     }
   }
   // staging registers; with kDkvAhead = 2 two tiles are in flight and the loop is unrolled
@@ -516,8 +523,8 @@ cmp_dkv_kernel(BwdArgs a) {
                                 dc[1][s][1], dc[1][s][2], dc[1][s][3]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const bf16x8 tro = *reinterpret_cast<const bf16x8*>(&L[768 + mt * 64 + lane]);
-          const bf16x8 trq = *reinterpret_cast<const bf16x8*>(&L[256 + mt * 64 + lane]);
+          const bf16x8 tro = *reinterpret_cast<const bf16x8*>(&L[768 + mt * 64 + tr_lane]);
+          const bf16x8 trq = *reinterpret_cast<const bf16x8*>(&L[256 + mt * 64 + tr_lane]);
           dV[s][mt] = mfma16(ap, tro, dV[s][mt]);
           dK[s][mt] = mfma16(ac, trq, dK[s][mt]);
         }
