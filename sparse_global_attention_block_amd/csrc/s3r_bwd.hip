@@ -29,8 +29,13 @@ namespace s3r {
 
 // ---------------------------------------------------------------------------------------
 // Operand images. Thread (row m, dims 8*d8..+7) of a 256-thread work-group; the TR group is
-// assembled in LDS and written linearly.
+// assembled in LDS (swizzled like cmp_dkv's: each 2-byte store has every lane on the same dim
+// modulo 8) and written linearly.
 // ---------------------------------------------------------------------------------------
+// Slot of lane l's 16 bytes in a transposed record staged in LDS: a permutation inside each
+// aligned group of 8 slots, so 16-byte lane reads through it stay free of bank conflicts.
+__device__ __forceinline__ int tr_swizzle(int l) { return l ^ ((l >> 3) & 7); }
+
 // kKind 0: 2-byte source of type kHalf; 1: f32 source. R records are written in the input
 // type (kHalf), TR records in bf16.
 template <int kKind, bool kHalf>
@@ -72,10 +77,11 @@ __global__ __launch_bounds__(256) void rec_pack_kernel(RecPackArgs a) {
       for (int e = 0; e < 8; ++e) {
         int rec, lane, slot;
         vt_position(m, d8 * 8 + e, rec, lane, slot);
-        stage[(rec * 64 + lane) * 8 + slot] = bf16_bits(x[e]);
+        stage[(rec * 64 + tr_swizzle(lane)) * 8 + slot] = bf16_bits(x[e]);
       }
       __syncthreads();
-      reinterpret_cast<uint4*>(out + a.tr_off)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+      reinterpret_cast<uint4*>(out + a.tr_off)[tid] =
+          reinterpret_cast<const uint4*>(stage)[(tid & ~63) | tr_swizzle(tid & 63)];
       __syncthreads();
     }
   }
@@ -367,8 +373,6 @@ hipError_t launch_cmp_dq(const BwdArgs& a, hipStream_t s) {
 constexpr int kDkvWaves = 8;
 constexpr int kDkvAhead = 1;  // query tiles in flight beyond the one being computed on (2 is
                               // built and measured 5 % slower)
-
-__device__ __forceinline__ int tr_swizzle(int l) { return l ^ ((l >> 3) & 7); }
 
 template <int kWaves, bool kHalf>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void

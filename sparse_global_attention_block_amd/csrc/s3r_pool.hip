@@ -125,7 +125,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 
 // One work-group per (head, group of kPackTiles tiles of 32 tokens). Thread (key m, dims d8)
 // copies 16 bytes of k into its K record slot and scatters 8 values of v, converted to fp16,
-// into the V^T records through LDS. Tokens beyond T are zero.
+// into the V^T records through LDS. Tokens beyond T are zero. In LDS, lane l's 16 bytes of a
+// V^T record sit at slot l ^ ((l >> 3) & 7): every lane of one 2-byte store writes the same
+// dim modulo 8, which the plain layout puts in 2 of the 32 banks; the copy out reads through
+// the same swizzle (a permutation inside aligned groups of 8 slots, free of conflicts).
 constexpr int kPackTiles = 4;
 template <bool kHalf>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
@@ -151,11 +154,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     for (int e = 0; e < 8; ++e) {
       int rec, lane, slot;
       vt_position(m, d8 * 8 + e, rec, lane, slot);
-      vt[(rec * 64 + lane) * 8 + slot] = f16_bits(vx[e]);  // exact for fp16 inputs
+      vt[(rec * 64 + (lane ^ ((lane >> 3) & 7))) * 8 + slot] = f16_bits(vx[e]);  // exact for fp16
     }
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(out + 4 * kRecBytes);
-    dst[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+    const int l = tid & 63;
+    dst[tid] = reinterpret_cast<const uint4*>(stage)[(tid & ~63) | (l ^ ((l >> 3) & 7))];
     __syncthreads();
   }
 }
