@@ -1,4 +1,5 @@
-// Compression branch: attention of every query to all pooled (coarse) tokens, in two passes.
+// Compression branch: attention of every query to all pooled (coarse) tokens, in two passes
+// or (the default where it applies) in a single pass from a lower bound of the log-sum-exp.
 //
 // Speed3R technical summary (gist.science), "Methodologie" section 1: the compression branch
 // attends at coarse resolution to pooled tokens and produces the score matrix that steers the
@@ -24,6 +25,16 @@
 // kAhead tiles ahead of the one being computed, so no registers are held for tiles in flight.
 // A software pipeline inside one wave (logits of tile t+1 on the matrix cores while the VALU
 // works on tile t) was measured slower on MI355X: its second accumulator set costs occupancy.
+//
+// Single pass (kBound). Its offset is a lower bound L'_t <= L_t (from the LSE pass over the
+// means of groups of 8 pooled keys: Jensen), so every weight u_tj = 2^(c_tj - L'_t) >= P_tj.
+// One sweep accumulates O_cmp * Z_t and Z_t = sum_j u_tj, and per key block the upper bound
+// sum_t u_tj of its score; a running list keeps the 64 blocks of largest bound. At the end
+// L_t = L'_t + log2 Z_t, O_cmp = O / Z, and the listed blocks are rescored exactly (their
+// logits recomputed on the same MFMA sequence) and ranked. A wave whose Z_t leave [1, 2^15] or
+// whose list cannot prove the top k (its last bound not below the k-th score) sets a redo flag;
+// the exact passes rerun only on the flagged work-groups (kDeep, kScoresOnly), so the outputs
+// are those of the two passes up to rounding.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
@@ -41,7 +52,7 @@ constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 // indices at the end. The entries are ordered by (score desc, block index asc), a total order,
 // so the final set does not depend on the order in which blocks arrive, and the decision is
 // made on exactly the f32 column sums the score matrix would have held.
-// kBound (with kTopk): the single pass over the pooled tokens described below.
+// kBound (with kTopk): the single pass (above).
 // kDeep: tiles in flight for the exact reruns after the single pass, where a few lone
 // work-groups sweep all tiles and the latency of each copy, not the chip's throughput, decides.
 // kScoresOnly (rerun of pass 2 with the running top-k where only the single pass's selection
