@@ -137,6 +137,8 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
     gsel = sel_gpu[h, rows].cpu().numpy()
     same = float((gsel == r["sel"]).all(axis=-1).mean())
     err_max, err_sum, n = 0.0, 0.0, 0
+    exc_max, exc_sum = 0.0, 0.0  # error beyond the output's own rounding (half an ulp of ref)
+    bits = 11 if out_gpu.dtype == torch.float16 else 8
     ref = r
     if same < 1.0:
         ref = O.forward_rows(hq, hk, hv, hg, w.block, w.topk, np.zeros(len(rows), np.int32),
@@ -148,6 +150,10 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
         d = abs(g - ref["out"][a, :nn])
         err_max = max(err_max, float(d.max()))
         err_sum += float(d.sum())
+        ax = np.maximum(np.abs(ref["out"][a, :nn]), 2.0 ** -14 if bits == 11 else 2.0 ** -126)
+        exc = np.maximum(d - np.exp2(np.floor(np.log2(ax)) - bits), 0.0)
+        exc_max = max(exc_max, float(exc.max()))
+        exc_sum += float(exc.sum())
         n += d.size
     return {
         "value": T / t_full, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
@@ -155,7 +161,8 @@ def cpu_baseline(w, x, sel_gpu, out_gpu, n_rows=48, seed=0):
                   f"query blocks of {w.block} ({t_rows:.2f} s); full job extrapolated as "
                   f"H*(pool + Nb*row) = {t_full:.0f} s",
     }, {"rows": len(rows), "rows_same_selection": same, "out_max_abs": err_max,
-        "out_mean_abs": err_sum / max(1, n)}
+        "out_mean_abs": err_sum / max(1, n), "out_max_beyond_rounding": exc_max,
+        "out_mean_beyond_rounding": exc_sum / max(1, n)}
 
 
 def time_backward(w: W.Workload, x, reps: int):
