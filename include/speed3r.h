@@ -195,8 +195,12 @@ int64_t speed3r_redo_flag_count(const s3r_params* p);
  * pooled keys 8g..8g+7 (g < floor(Nb / 8); the pooling stores them scaled like the pooled
  * keys, as hi + lo pairs of the input type), lse_bound[h][t] = log sum_g 8 exp(scale * q_t .
  * G_g) (f32 [H][T], natural log). Convexity of exp (Jensen) makes each group's term at most
- * the sum of exp over its 8 keys, so lse_bound <= the log-sum-exp of speed3r_cmp_lse (up to
- * rounding). S3R_ERR_UNSUPPORTED if Nb < 8. */
+ * the sum of exp over its 8 keys, so the exact value is <= the log-sum-exp of speed3r_cmp_lse.
+ * The kernel multiplies the queries by the hi parts of the group keys alone (the scaled keys
+ * rounded to the input type), so each logit may move by up to 2^-8 (bf16; fp16: 2^-11) of
+ * scale * sum_d |q_d G_gd|; the single pass only needs a value low enough, which its Z check
+ * verifies (a bound above the log-sum-exp makes it rerun the exact passes there).
+ * S3R_ERR_UNSUPPORTED if Nb < 8. */
 s3r_status speed3r_cmp_lse_bound(const s3r_params* p, const void* q, const void* workspace,
                                  size_t workspace_bytes, float* lse_bound, hipStream_t stream);
 

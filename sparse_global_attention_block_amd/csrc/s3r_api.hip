@@ -192,7 +192,7 @@ s3r_status run_lse_bound(const Dims& d, CmpArgs a, const unsigned char* ws, cons
   a.Nb = d.Nb_g;
   a.lse = lse_bound;
   a.lse_bias = logf((float)kGroupBlocks);
-  return hip_status(launch_cmp_lse(a, stream));
+  return hip_status(launch_cmp_lse_bound(a, stream));
 }
 
 // The single pass from the bound, then the two exact passes on the work-groups it flagged.

@@ -52,7 +52,9 @@ constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 // indices at the end. The entries are ordered by (score desc, block index asc), a total order,
 // so the final set does not depend on the order in which blocks arrive, and the decision is
 // made on exactly the f32 column sums the score matrix would have held.
-// kBound (with kTopk): the single pass (above).
+// kBound with kFused (and kTopk): the single pass (above). kBound without kFused: the bound
+// pass, pass 1 over the group keys on their hi parts alone (half the MFMAs and half the
+// records): its result need not be exact, only low enough, which the single pass checks.
 // kDeep: tiles in flight for the exact reruns after the single pass, where a few lone
 // work-groups sweep all tiles and the latency of each copy, not the chip's throughput, decides.
 // kScoresOnly (rerun of pass 2 with the running top-k where only the single pass's selection
@@ -61,19 +63,23 @@ template <bool kFused, int kQB, int kWaves, bool kTopk = false, bool kHalf = fal
           bool kBound = false, int kDeep = 0, bool kScoresOnly = false>
 // (second bound: resident waves per SIMD the register allocation must allow)
 __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArgs a) {
-  static_assert(!kBound || (kFused && kTopk), "the single pass keeps the running top-k");
+  static_assert(!kBound || !kFused || kTopk, "the single pass keeps the running top-k");
+  static_assert(!kBound || kFused || kDeep == 0, "the bound pass has no rerun");
+  constexpr bool kSingle = kBound && kFused;   // the single pass
+  constexpr bool kHiOnly = kBound && !kFused;  // the bound pass: hi parts of the keys only
   constexpr int kAhead = kDeep ? kDeep : (kFused ? kFusedAhead : kLseAhead);  // tiles in flight
   constexpr int kRing = kAhead + 1;
   constexpr int kQueries = 64 * kWaves;
   static_assert(!kScoresOnly || (kFused && kTopk && !kBound), "a rerun of the top-k pass");
-  constexpr int kRecs = (kFused && !kScoresOnly) ? 12 : 8;  // records of a tile this pass reads
+  // records of a tile this pass reads
+  constexpr int kRecs = (kFused && !kScoresOnly) ? 12 : (kHiOnly ? 4 : 8);
   constexpr int kRecsPerWave = kRecs / kWaves;
   static_assert(kRecsPerWave * kWaves == kRecs, "each wave copies whole records");
   constexpr int kNtPerQB = 4 / kQB;
   __shared__ uint4 lds[kRing][kRecs * 64];
   // (single pass) each lane's parts of Z_t for its 4 column tiles: read, added to and written
   // back once per tile, so that no register holds them through the logits
-  __shared__ floatx4 zpart[kBound ? kWaves : 1][64];
+  __shared__ floatx4 zpart[kSingle ? kWaves : 1][64];
 
   const int64_t n_qtiles = (a.T + kQueries - 1) / kQueries;
   const int64_t total = (int64_t)a.H * n_qtiles;
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t t = q0 + 16 * nt + li;
-    if constexpr (kBound) {
+    if constexpr (kSingle) {
       // a lower bound of L_t (base 2), lowered by kBoundMargin so that rounding cannot lift
       // it above L_t
       off[nt] = (t < a.T) ? a.lse_in[(int64_t)h * a.T + t] * kLog2e - kBoundMargin : INFINITY;
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     }
     lsum[nt] = 0.f;
   }
-  if constexpr (kBound) zpart[wave][lane] = floatx4{0.f, 0.f, 0.f, 0.f};  // this lane's own
+  if constexpr (kSingle) zpart[wave][lane] = floatx4{0.f, 0.f, 0.f, 0.f};  // this lane's own
   // running top-k: lane e holds entry e (score, block index) of each query block's list;
   // th_v / th_j mirror entry K-1 (the current k-th best) in scalar registers
   float tk_v[kQB], th_v[kQB];
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   // length of the running list: k for the exact pass; the single pass ranks upper bounds and
   // keeps every candidate up to one per lane
   auto list_len = [&](int64_t qblk, bool& own) {
-    if constexpr (kBound) {
+    if constexpr (kSingle) {
       own = a.own && qblk >= a.forced;
       const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
       return (int)(nc < 64 ? nc : 64);
@@ -187,16 +193,23 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     for (int s2 = 0; s2 < 2; ++s2) {
       const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(&L[(2 * s2 + 0) * 64 + lane]);
       const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(&L[(2 * s2 + 1) * 64 + lane]);
-      const bf16x8 l0 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 0) * 64 + lane]);
-      const bf16x8 l1 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 1) * 64 + lane]);
+      bf16x8 l0, l1;
+      if constexpr (!kHiOnly) {
+        l0 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 0) * 64 + lane]);
+        l1 = *reinterpret_cast<const bf16x8*>(&L[256 + (2 * s2 + 1) * 64 + lane]);
+      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         // pass 2 subtracts its fixed offset on the VALU instead (registers)
         floatx4 x = mfma_in<kHalf>(h0, qb[nt][0],
                                    kFused ? floatx4{0.f, 0.f, 0.f, 0.f} : cneg[kFused ? 0 : nt]);
         x = mfma_in<kHalf>(h1, qb[nt][1], x);
-        x = mfma_in<kHalf>(l0, qb[nt][0], x);
-        acc[s2][nt] = mfma_in<kHalf>(l1, qb[nt][1], x);
+        if constexpr (kHiOnly) {
+          acc[s2][nt] = x;
+        } else {
+          x = mfma_in<kHalf>(l0, qb[nt][0], x);
+          acc[s2][nt] = mfma_in<kHalf>(l1, qb[nt][1], x);
+        }
       }
     }
   };
@@ -264,7 +277,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             p[s2][nt][r] = fast_exp2(acc[s2][nt][r] - off[nt]);
-      if constexpr (kBound) {
+      if constexpr (kSingle) {
         // this lane's part of Z_t; the empty asm ties the LDS read to the weights, so that
         // the compiler cannot hoist it (and the 4 registers) above the logits
         int zl = lane;
@@ -305,14 +318,14 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       for (int nt = 0; nt < (kScoresOnly ? 0 : 4); ++nt) {
         const halfx8 pb = pack8h(p[0][nt][0], p[0][nt][1], p[0][nt][2], p[0][nt][3],
                                  p[1][nt][0], p[1][nt][1], p[1][nt][2], p[1][nt][3]);
-        if constexpr (kBound) hs[nt / kNtPerQB] = (nt % kNtPerQB == 0) ? pb : hs[nt / kNtPerQB] + pb;
+        if constexpr (kSingle) hs[nt / kNtPerQB] = (nt % kNtPerQB == 0) ? pb : hs[nt / kNtPerQB] + pb;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const halfx8 vt = *reinterpret_cast<const halfx8*>(&L[512 + mt * 64 + lane]);
           o[mt][nt] = mfma16h(vt, pb, o[mt][nt]);
         }
       }
-      if constexpr (kBound) {
+      if constexpr (kSingle) {
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) tots[qb] = row_reduce_scatter8_h(hs[qb], lane);
       } else {
@@ -323,7 +336,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         const float tot = tots[qb];
         // single pass: B = 64 / kQB (a shift; the division stays in the exact kernels, whose
         // register allocation it happens to suit)
-        const int64_t qblk = kBound ? (q0 + 16 * qb * kNtPerQB) / (64 / kQB)
+        const int64_t qblk = kSingle ? (q0 + 16 * qb * kNtPerQB) / (64 / kQB)
                                     : (q0 + 16 * qb * kNtPerQB) / a.B;
         if constexpr (kTopk) {
           if (qblk < a.Nb) {
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     }
   } else {
     float zinv[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (kBound) {
+    if constexpr (kSingle) {
       // Z_t and the exact L_t = offset + log2 Z_t. Z_t >= 1 proves offset <= L_t, i.e. every
       // weight was at least its probability, so each block's accumulated sum bounds its score
       // from above; Z_t <= 2^15 proves that no weight (each is at most Z_t) overflowed fp16 in
@@ -594,6 +607,13 @@ static hipError_t launch_cmp_t(const CmpArgs& a, hipStream_t s, bool fused, bool
 }
 
 template <bool kHalf>
+static hipError_t launch_bound_t(const CmpArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((cmp_kernel<false, 1, kLseWaves, false, kHalf, true>), cmp_grid(a, kLseWaves),
+                     dim3(64 * kLseWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool kHalf>
 static hipError_t launch_single_t(const CmpArgs& a, hipStream_t s) {
   const dim3 g3 = cmp_grid(a, kFusedWaves), b3(64 * kFusedWaves);
   switch (a.B) {
@@ -637,6 +657,9 @@ hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s) { return launch_cmp(a
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) { return launch_cmp(a, s, true, false); }
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s) {
   return launch_cmp(a, s, true, true);
+}
+hipError_t launch_cmp_lse_bound(const CmpArgs& a, hipStream_t s) {
+  return a.half ? launch_bound_t<true>(a, s) : launch_bound_t<false>(a, s);
 }
 hipError_t launch_cmp_single_topk(const CmpArgs& a, hipStream_t s) {
   return a.half ? launch_single_t<true>(a, s) : launch_single_t<false>(a, s);

@@ -197,6 +197,7 @@ hipError_t launch_sel_dkv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_cmp_lse(const CmpArgs& a, hipStream_t s);
+hipError_t launch_cmp_lse_bound(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_fused_topk(const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_single_topk(const CmpArgs& a, hipStream_t s);

@@ -92,14 +92,36 @@ def valid_waves(st):
     return np.tile(first < T, H)
 
 
+def bound_tolerance(hq, hk, w):
+    """[H, T] limit on |GPU bound - oracle bound| (natural log). The bound pass multiplies the
+    queries by the group keys' hi parts alone, the scaled keys rounded to the input type: each
+    element x moves by at most u|x| (u = 2^-8 for bf16, 2^-11 for fp16, whose values below
+    2^-14 move by at most 2^-25 instead), so the logit of group g by at most
+    u * scale * sum_d |q_d G_gd| (+ 2^-25 ln2 sum_d |q_d| for fp16), and a log-sum-exp moves by
+    at most the largest change of its terms. 1 % and 1e-5 more cover the f32 arithmetic."""
+    q = np.abs(hq.double().numpy()).transpose(1, 0, 2)            # [H, T, D]
+    kc = O.pool(hk, w.block)
+    G = kc.shape[1] // 8
+    means = np.abs(kc[:, :G * 8].reshape(kc.shape[0], G, 8, -1).mean(axis=2))  # [H, G, D]
+    scale = q.shape[-1] ** -0.5
+    u = 2.0 ** -11 if w.dtype == "fp16" else 2.0 ** -8
+    tol = u * scale * np.matmul(q, means.transpose(0, 2, 1)).max(axis=-1)
+    if w.dtype == "fp16":
+        tol += 2.0 ** -25 * np.log(2.0) * q.sum(axis=-1)
+    return 1.01 * tol + 1e-5
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_lse_bound(name):
-    """The bound pass against the oracle's group-mean bound, and below the exact LSE."""
+    """The bound pass against the oracle's group-mean bound, within what rounding the group
+    keys to the input type allows, and (within the same) below the exact LSE."""
     w, x, st, bound, ora = run_case(name)
     g = host(bound).double().numpy()
+    tol = bound_tolerance(host(x["q"]), host(x["k"]), w)
     d = np.abs(g - ora["bound"])
-    assert d.max() < 1e-4, f"max |d bound| {d.max():.3e}"
-    assert (g <= ora["lse"] + 1e-4).all()
+    print(f"[{name}] bound: max |d| {d.max():.2e}, max |d|/limit {(d / tol).max():.2f}", flush=True)
+    assert (d <= tol).all(), f"max |d bound| {d.max():.3e}"
+    assert (g <= ora["lse"] + tol).all()
 
 
 @pytest.mark.parametrize("name", list(CASES))
