@@ -109,18 +109,34 @@ struct Flash {
         }
     }
     const halfx8 ones = pack8h(1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f);
+    // the weights of all column tiles first and one (rarely taken) branch for the tile, so
+    // that the exps and the matrix products share one scheduling region; the column tiles
+    // that need it are rescaled before their products, as if taken one at a time
+    halfx8 pb[NT];
+    bool big_any = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       bool big;
-      halfx8 pb = weights(acc, nt, mult, big);
-      if (__builtin_expect(__any(big) || fresh, 0)) {
-        rescale(acc, nt, mult);
-        pb = weights(acc, nt, mult, big);
+      pb[nt] = weights(acc, nt, mult, big);
+      big_any |= big;
+    }
+    if (__builtin_expect(__any(big_any) || fresh, 0)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        bool big;
+        (void)weights(acc, nt, mult, big);
+        if (__any(big) || fresh) {
+          rescale(acc, nt, mult);
+          pb[nt] = weights(acc, nt, mult, big);
+        }
       }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        o[mt][nt] = mfma16h(__builtin_bit_cast(halfx8, v[mt]), pb, o[mt][nt]);
-      l[nt] = mfma16h(ones, pb, l[nt]);
+        o[mt][nt] = mfma16h(__builtin_bit_cast(halfx8, v[mt]), pb[nt], o[mt][nt]);
+      l[nt] = mfma16h(ones, pb[nt], l[nt]);
     }
     if (__builtin_expect(fresh, 0)) {
       bool unset = false;
