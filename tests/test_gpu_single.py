@@ -209,3 +209,35 @@ def test_forward_single_vs_two_pass(name):
         check_selection(host(sel).numpy(), ora["score"], ora["sel"], w.topk, forced=st.forced,
                         qblocks=own_rows(w.H, st.Nb, st.own))
         check_out(out, hx_out, what=f"out mode {mode}")
+
+
+def test_tight_bound_lifted_by_rounding():
+    """Keys constant over each group of 8 blocks make the group-mean bound exact (Jensen's
+    inequality is then an equality), so rounding the scaled group keys to bf16 in the bound
+    pass can lift the GPU's bound above the true log-sum-exp. The Z check must flag those
+    waves, and the exact reruns must give the oracle's results."""
+    T, H, B, k = 1024, 2, 16, 8
+    gen = torch.Generator().manual_seed(31)
+    q = torch.randn(T, H, 64, generator=gen).to(torch.bfloat16)
+    groups = torch.randn(T // (8 * B), H, 64, generator=gen) * 2.0
+    kk = groups.repeat_interleave(8 * B, dim=0).to(torch.bfloat16)
+    v = torch.randn(T, H, 64, generator=gen).to(torch.bfloat16)
+    gates = torch.rand(H, 2, generator=gen)
+    print(f"[single tight] T={T} H={H} B={B} k={k}", flush=True)
+    x = {"q": q.cuda(), "k": kk.cuda(), "v": v.cuda(), "gates": gates.cuda()}
+    st = S.Stages(x["q"], x["k"], x["v"], x["gates"], B, k, keep_score=False)
+    assert st.single_ok
+    st.run_pool()
+    st.run_lse_bound()
+    bound = host(st.lse_bound).double().numpy()
+    st.run_single_topk()
+    torch.cuda.synchronize()
+    ora = O.forward_all(q, kk, v, gates, B, k)
+    exact_bound = O.lse_group_bound(q, kk, B)
+    assert np.abs(exact_bound - ora["lse"]).max() < 1e-9  # the bound is exact here
+    above = int((bound > ora["lse"]).sum())
+    redo = host(st.redo).numpy()
+    print(f"[single tight] queries whose GPU bound exceeds the LSE: {above} of {bound.size}; "
+          f"waves flagged by the Z check: {int(((redo & 2) != 0).sum())}", flush=True)
+    w = dataclasses.replace(_tiny_s, name="tight", H=H, block=B, topk=k)
+    check_cmp("tight", st, ora, w)
