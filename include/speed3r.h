@@ -349,6 +349,25 @@ s3r_status speed3r_sparse_attn_fwd_windows(const s3r_params* p, const s3r_window
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 
+/* ---- Measured ceilings (not part of the method) -------------------------------------------
+ * The pages print no kernel figures; the kernels' roofline fractions are quoted against the
+ * vendor's peaks and against what these two plain kernels reach on the same chip. */
+
+/* Streaming copy of `bytes` (a multiple of 16; src and dst 16-byte aligned, not overlapping)
+ * from src to dst: one 16-byte load and store per element, 4 in flight per thread. It moves
+ * 2 * bytes through HBM. S3R_ERR_INVALID_ARG on a null or misaligned pointer or a bad size. */
+s3r_status speed3r_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/* Floating-point operations one speed3r_calib_mfma call performs (-1 for a bad argument):
+ * work_groups * 4 waves * iters * 8 chains * 16384 (one 16x16x32 bf16 matrix product). */
+int64_t speed3r_calib_mfma_flops(int32_t work_groups, int32_t iters);
+
+/* A loop of independent v_mfma_f32_16x16x32_bf16 products (8 accumulators per wave, 4 waves
+ * per work-group, `iters` rounds); one f32 per thread is written to sink [work_groups * 256]
+ * so the work is kept. S3R_ERR_INVALID_ARG on a null or misaligned sink or a size below 1. */
+s3r_status speed3r_calib_mfma(float* sink, int32_t work_groups, int32_t iters,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

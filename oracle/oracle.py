@@ -77,12 +77,19 @@ def lib():
         L.s3r_oracle_backward.restype = None
         L.s3r_oracle_num_threads.argtypes = []
         L.s3r_oracle_num_threads.restype = ctypes.c_int
+        L.s3r_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.s3r_oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return int(lib().s3r_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's loops over independent rows (results do not depend on it)."""
+    lib().s3r_oracle_set_num_threads(int(n))
 
 
 def _f32(x) -> np.ndarray:

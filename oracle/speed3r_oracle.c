@@ -336,6 +336,17 @@ int s3r_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the OpenMP loops over independent rows use from now on (timing at one thread and at
+ * every core); the results do not depend on it. */
+void s3r_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
+
 /* Gradient of the forward pass for one head h, with the selection sel ([Nb][nsel]) fixed.
  * dout is the gradient of out ([T][H][D] addressed like the inputs, dst/dsh); dq, dk, dv are
  * [T][H][D] (contiguous, only head h written, zero them first); dgate is [T][2] for per-token

@@ -106,6 +106,11 @@ EXPORTS = {
                                                        ctypes.POINTER(Windows)] +
                                         [ctypes.c_void_p] * 6 +
                                         [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "speed3r_calib_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]),
+    "speed3r_calib_mfma_flops": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32]),
+    "speed3r_calib_mfma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p]),
 }
 
 _lib = None
@@ -158,6 +163,8 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, t
                 x.stride(2) != 1:
             raise ValueError("q, k, v must be one of bf16/fp16, [T, H, D] with a contiguous "
                              "last dimension")
+        if x.device != q.device or x.device.type != "cuda":
+            raise ValueError("q, k, v must be on one GPU (the kernels read device memory)")
     gst = 0
     if gates is not None and gates.dim() == 3:
         gst = gates.stride(0)
@@ -206,6 +213,48 @@ def runs_single(p: Params) -> bool:
     return ok and p.cmp_mode == CMP_AUTO and (2 * most <= 64 or Nb - forced <= 64)
 
 
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_out(out: torch.Tensor, q: torch.Tensor, what: str = "out"):
+    """A [T, H, 64] result buffer: q's shape, type and device, contiguous."""
+    _need(isinstance(out, torch.Tensor) and tuple(out.shape) == tuple(q.shape) and
+          out.dtype == q.dtype and out.device == q.device and out.is_contiguous(),
+          f"{what} must be a contiguous {q.dtype} tensor of shape {tuple(q.shape)} on "
+          f"{q.device}")
+
+
+def _check_gates(gates: torch.Tensor, q: torch.Tensor):
+    """Gates are float32 [H, 2] (contiguous) or per token [T, H, 2] with strides (2H, 2, 1)."""
+    T, H, _ = q.shape
+    ok = isinstance(gates, torch.Tensor) and gates.dtype == torch.float32 and \
+        gates.device == q.device
+    if ok and gates.dim() == 2:
+        ok = tuple(gates.shape) == (H, 2) and gates.is_contiguous()
+    elif ok and gates.dim() == 3:
+        ok = tuple(gates.shape) == (T, H, 2) and tuple(gates.stride()) == (2 * H, 2, 1)
+    else:
+        ok = False
+    _need(ok, f"gates must be float32 [H, 2] (contiguous) or [T, H, 2] with strides "
+              f"(2H, 2, 1) on {q.device}")
+
+
+def _check_sel(sel_idx: torch.Tensor, p: Params, device):
+    """A selection buffer: int32 [H, Nb, num_selected(p)], contiguous, on the inputs' device."""
+    shape = (p.H, num_blocks(p), num_selected(p))
+    _need(isinstance(sel_idx, torch.Tensor) and sel_idx.dtype == torch.int32 and
+          tuple(sel_idx.shape) == shape and sel_idx.is_contiguous() and
+          sel_idx.device == device,
+          f"sel_idx must be a contiguous int32 tensor of shape {shape} on {device}")
+
+
+def _check_workspace(ws: torch.Tensor, device):
+    _need(isinstance(ws, torch.Tensor) and ws.dtype == torch.uint8 and ws.is_contiguous() and
+          ws.device == device, f"workspace must be a contiguous uint8 tensor on {device}")
+
+
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator hands out 512-byte aligned blocks, more than the 256 required
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -218,10 +267,15 @@ def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Full forward pass. Returns (out [T, H, 64] in the input type, sel_idx or None)."""
     p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
+    _check_gates(gates, q)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _check_out(out, q)
+    if sel_idx is not None:
+        _check_sel(sel_idx, p, q.device)
     if workspace is None:
         workspace = alloc_workspace(workspace_size(p), q.device)
+    _check_workspace(workspace, q.device)
     st = lib().speed3r_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gates),
                                        _ptr(out), _ptr(sel_idx), _ptr(workspace),
                                        workspace.numel(), _stream())
@@ -283,8 +337,10 @@ def dense_attn_fwd(q, k, v, scale: float = 0.0, out=None, workspace=None):
     p = make_params(q, k, v, 64, 1, scale)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _check_out(out, q)
     if workspace is None:
         workspace = alloc_workspace(dense_workspace_size(p), q.device)
+    _check_workspace(workspace, q.device)
     _check("speed3r_dense_attn_fwd", lib().speed3r_dense_attn_fwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream()))
@@ -313,11 +369,13 @@ def sparse_attn_fwd_train(q, k, v, gates, block: int, topk: int, scale: float = 
                           force_own: bool = False, cmp_mode: int = CMP_AUTO) -> Trained:
     """Forward pass that keeps the state speed3r_sparse_attn_bwd needs."""
     p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
+    _check_gates(gates, q)
     out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     sel = torch.empty(q.shape[1], num_blocks(p), num_selected(p), dtype=torch.int32,
                       device=q.device)
     if workspace is None:
         workspace = alloc_workspace(train_workspace_size(p), q.device)
+    _check_workspace(workspace, q.device)
     _check("speed3r_sparse_attn_fwd_train", lib().speed3r_sparse_attn_fwd_train(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(out), _ptr(sel),
         _ptr(workspace), workspace.numel(), _stream()))
@@ -357,8 +415,13 @@ def window_permute(layout, src: torch.Tensor, dst: Optional[torch.Tensor] = None
                    inverse: bool = False) -> torch.Tensor:
     """Reorder a [T, H, 64] bf16/fp16 tensor into window order (or back, inverse=True)."""
     w = make_windows(layout)
+    _need(src.dim() == 3 and src.dtype in _DTYPES and src.stride(2) == 1,
+          "src must be a bf16/fp16 [T, H, 64] tensor with a contiguous last dimension")
     if dst is None:
         dst = torch.empty(src.shape, dtype=src.dtype, device=src.device)
+    _need(tuple(dst.shape) == tuple(src.shape) and dst.dtype == src.dtype and
+          dst.device == src.device and dst.stride(2) == 1,
+          "dst must have src's shape, type and device, with a contiguous last dimension")
     _check("speed3r_window_permute", lib().speed3r_window_permute(
         ctypes.byref(w), src.shape[1], _ptr(src), src.stride(0), src.stride(1), _ptr(dst),
         dst.stride(0), dst.stride(1), int(inverse), _stream()))
@@ -379,11 +442,16 @@ def sparse_attn_fwd_windows(q, k, v, gates, block: int, topk: int, layout, scale
     """Forward pass with 2-D windows as blocks; out in the caller's token order, sel_idx over
     blocks of the window order."""
     p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
+    _check_gates(gates, q)
     w = make_windows(layout)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _check_out(out, q)
+    if sel_idx is not None:
+        _check_sel(sel_idx, p, q.device)
     if workspace is None:
         workspace = alloc_workspace(windows_workspace_size(p, layout), q.device)
+    _check_workspace(workspace, q.device)
     _check("speed3r_sparse_attn_fwd_windows", lib().speed3r_sparse_attn_fwd_windows(
         ctypes.byref(p), ctypes.byref(w), _ptr(q), _ptr(k), _ptr(v), _ptr(gates), _ptr(out),
         _ptr(sel_idx), _ptr(workspace), workspace.numel(), _stream()))
@@ -472,3 +540,24 @@ class Stages:
         self.run_topk()
         self.run_sel()
         return self
+
+
+def calib_copy(src: torch.Tensor, dst: torch.Tensor) -> int:
+    """Streaming copy kernel (a measured HBM ceiling): copies src into dst (same size, 16-byte
+    multiple, contiguous). Returns the bytes it moves through HBM (read + written)."""
+    _need(src.is_contiguous() and dst.is_contiguous() and src.device == dst.device and
+          src.numel() * src.element_size() == dst.numel() * dst.element_size(),
+          "src and dst must be contiguous tensors of one size on one device")
+    n = src.numel() * src.element_size()
+    _check("speed3r_calib_copy", lib().speed3r_calib_copy(_ptr(src), _ptr(dst), n, _stream()))
+    return 2 * n
+
+
+def calib_mfma(sink: torch.Tensor, work_groups: int, iters: int) -> int:
+    """Loop of bf16 matrix products (a measured MFMA ceiling). sink: float32, at least
+    work_groups * 256 elements. Returns the floating-point operations performed."""
+    _need(sink.dtype == torch.float32 and sink.is_contiguous() and
+          sink.numel() >= work_groups * 256, "sink must be float32 [work_groups * 256]")
+    _check("speed3r_calib_mfma", lib().speed3r_calib_mfma(_ptr(sink), work_groups, iters,
+                                                          _stream()))
+    return int(lib().speed3r_calib_mfma_flops(work_groups, iters))

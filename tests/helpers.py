@@ -17,6 +17,21 @@ OUT_MAX_ABS = 2e-2
 OUT_MEAN_ABS = 2e-3
 GAP = 1e-3
 
+# Derived index rules. The contract's absolute gap of 1e-3 covers almost no row at 1000 views,
+# where scores spread over 21,469 blocks (about 6 % of rows for k = 16). The GPU's block scores
+# were measured against the oracle's on every small parity case (all block sizes, forced and
+# own blocks, fp16): at most 2.34e-5 apart at 3 views x 1374 tokens (B = 64, bf16), and at
+# most 8.3e-6 (bf16 inputs) / 3.6e-5 (fp16 inputs) apart relative to the score; on 496
+# sampled rows at 1000 views, 1.04e-5 absolute and 1.08e-5 relative. Two blocks can only
+# trade places if their oracle scores are closer than the two GPU errors together, so with a
+# factor 10 of margin the selected set must equal the oracle's wherever the gap exceeds
+#   GAP_ABS = 10 x 2.34e-5 (the 3-view maximum), or
+#   SCORE_REL_ERR[dtype] x 10 x S_(k)  (S_(k) = the oracle's k-th score of the row),
+# besides the contract's 1e-3. Elsewhere every GPU-chosen block must score within the same
+# threshold of S_(k).
+GAP_ABS = 2.5e-4
+SCORE_REL_ERR = {"bf16": 1e-5, "fp16": 4e-5}
+
 
 def cuda_inputs(w: W.Workload, T=None, views=None) -> Dict[str, torch.Tensor]:
     return W.make_inputs(w, device="cuda", T=T, views=views)
@@ -35,21 +50,25 @@ def row_gaps(score_row_f32: np.ndarray, k: int) -> float:
 
 
 def check_selection(gpu_sel: np.ndarray, ora_score: np.ndarray, ora_sel: np.ndarray, k: int,
-                    forced: int = 0, qblocks=None):
+                    forced: int = 0, qblocks=None, dtype: str = "bf16", stats=None):
     """Index parity. Every row starts with the forced blocks 0..forced-1; with `qblocks` (the
     query block of each row: own blocks on) a row whose query block is past the prefix also
     holds that block. The k (at most the candidates left) chosen among the other blocks follow,
     sorted together with the own block, then -1 padding. Of the chosen, rows whose oracle gap
-    over the candidates exceeds GAP must match exactly; on the other rows every GPU-chosen
-    block must score within GAP of the oracle's k-th score. Returns the fraction of rows held
-    to the exact rule and the list of differing rows."""
+    over the candidates exceeds the contract's GAP, GAP_ABS or 10 x SCORE_REL_ERR x S_(k) must
+    match exactly; on the other rows every GPU-chosen block must score within that threshold
+    of the oracle's k-th score. Returns the fraction of rows held to an exact rule and the list
+    of differing rows; `stats` (a dict), if given, receives the fraction of rows under each
+    rule and how many rows chose the oracle's set."""
     rows = gpu_sel.reshape(-1, gpu_sel.shape[-1])
     osel = ora_sel.reshape(-1, ora_sel.shape[-1])
     osc = ora_score.reshape(-1, ora_score.shape[-1])
     own = None if qblocks is None else np.asarray(qblocks).reshape(-1)
     assert rows.shape == osel.shape
     Nb = osc.shape[1]
+    rel = 10 * SCORE_REL_ERR[dtype]
     exact, differing = 0, []
+    n_contract = n_abs = n_rel = n_same = 0
     for r in range(rows.shape[0]):
         row, orow = rows[r], osel[r]
         np.testing.assert_array_equal(row[:forced], np.arange(forced), err_msg=f"row {r}")
@@ -67,17 +86,27 @@ def check_selection(gpu_sel: np.ndarray, ora_score: np.ndarray, ora_sel: np.ndar
         assert len(got) == kr, f"row {r}: {len(got)} chosen blocks, expected {kr}"
         free = osc[r][cand]
         gap = row_gaps(free, kr) if kr > 0 else math.inf
+        kth = -np.sort(-free.astype(np.float64))[kr - 1] if 0 < kr else math.inf
+        thr = min(GAP, GAP_ABS, rel * kth)
         same = np.array_equal(got, want)
-        if gap > GAP:
+        n_same += same
+        n_contract += gap > GAP
+        n_abs += gap > GAP_ABS
+        n_rel += gap > rel * kth
+        if gap > thr:
             exact += 1
-            assert same, f"row {r}: gap {gap:.3e} > {GAP} but GPU {row} != oracle {orow}"
+            assert same, (f"row {r}: gap {gap:.3e} > {thr:.3e} (k-th score {kth:.3e}) but GPU "
+                          f"{row} != oracle {orow}")
         elif not same:
-            kth = -np.sort(-free.astype(np.float64))[kr - 1]
             assert cand[got].all(), f"row {r}: a forced or own block was chosen twice"
-            assert (osc[r][got] >= kth - GAP).all(), f"row {r}: GPU picked a far block"
+            assert (osc[r][got] >= kth - thr).all(), f"row {r}: GPU picked a far block"
             assert np.array_equal(np.sort(got), got) and len(set(got)) == len(got)
             differing.append(r)
-    return exact / max(1, rows.shape[0]), differing
+    n = max(1, rows.shape[0])
+    if stats is not None:
+        stats.update(rows=rows.shape[0], exact_rule=exact / n, contract_gap=n_contract / n,
+                     abs_gap=n_abs / n, rel_gap=n_rel / n, same_set=n_same / n)
+    return exact / n, differing
 
 
 def own_rows(H: int, Nb: int, own: bool):
@@ -118,4 +147,6 @@ def check_out(gpu_out: torch.Tensor, ref: np.ndarray, what="out",
         f"{what}: max-abs {d.max():.3e} (beyond output rounding {excess.max():.3e}) > {max_abs}"
     assert excess.mean() <= mean_abs, \
         f"{what}: mean-abs {d.mean():.3e} (beyond output rounding {excess.mean():.3e}) > {mean_abs}"
+    # the contract's mean-abs bound also holds for the plain difference, rounding included
+    assert d.mean() <= mean_abs, f"{what}: plain mean-abs {d.mean():.3e} > {mean_abs}"
     return float(d.max()), float(d.mean())

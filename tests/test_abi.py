@@ -327,3 +327,41 @@ def test_runs_single_matches_the_library(T, B, k, F, own):
         if mode == S.CMP_SINGLE and got == 0:
             continue
         assert S.runs_single(p) == (got > two), (mode, got, two)
+
+
+def test_binding_rejects_bad_result_buffers():
+    """The binding checks every tensor it turns into a pointer (no GPU needed: the checks
+    run before any call). q, k, v must sit on one GPU; out must be q's shape, type and
+    device, contiguous; gates float32 [H, 2] or [T, H, 2] with strides (2H, 2, 1); sel_idx
+    int32 [H, Nb, num_selected] contiguous (a selection with forced or own blocks is longer
+    than topk, and a short buffer would take out-of-bounds device writes)."""
+    import torch
+
+    T, H = 256, 2
+    q = torch.zeros(T, H, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="one GPU"):
+        S.make_params(q, q, q, 16, 4)
+    # result buffers, checked against q's own device (CPU here)
+    S._check_out(torch.empty_like(q), q)
+    for bad in (torch.empty(T, H, 64, dtype=torch.float32),       # wrong type
+                torch.empty(T, H + 1, 64, dtype=torch.bfloat16),   # wrong shape
+                torch.empty(T, 64, H, dtype=torch.bfloat16).transpose(1, 2)):  # strided
+        with pytest.raises(ValueError, match="out"):
+            S._check_out(bad, q)
+    S._check_gates(torch.ones(H, 2), q)
+    S._check_gates(torch.ones(T, H, 2), q)
+    for bad in (torch.ones(H, 2, dtype=torch.bfloat16), torch.ones(2, H).t(), torch.ones(H, 3),
+                torch.ones(T, H, 4)[:, :, :2], torch.ones(T + 1, H, 2)):
+        with pytest.raises(ValueError, match="gates"):
+            S._check_gates(bad, q)
+    p = params(T=T, H=H, B=16, k=4, forced=3, own=1)
+    n_sel = S.num_selected(p)
+    assert n_sel == 3 + 1 + 4
+    S._check_sel(torch.empty(H, T // 16, n_sel, dtype=torch.int32), p, q.device)
+    for bad in (torch.empty(H, T // 16, 4, dtype=torch.int32),      # sized for topk only
+                torch.empty(H, T // 16, n_sel, dtype=torch.int64),
+                torch.empty(H, n_sel, T // 16, dtype=torch.int32).transpose(1, 2)):
+        with pytest.raises(ValueError, match="sel_idx"):
+            S._check_sel(bad, p, q.device)
+    with pytest.raises(ValueError, match="workspace"):
+        S._check_workspace(torch.empty(64, dtype=torch.float32), q.device)

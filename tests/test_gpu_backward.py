@@ -103,7 +103,7 @@ def run_case(name):
     Nb = gsel.shape[1]
     F = min(w.forced, Nb)
     check_selection(gsel, ora_f["score"], ora_f["sel"], w.topk, forced=F,
-                    qblocks=own_rows(w.H, Nb, w.own and F < Nb))
+                    qblocks=own_rows(w.H, Nb, w.own and F < Nb), dtype=w.dtype)
     ref = O.backward(hx["q"], hx["k"], hx["v"], hg, host(dout), w.block, gsel)
     ref["forward"] = ora_f
     ref["dout"] = host(dout)

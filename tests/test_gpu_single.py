@@ -79,7 +79,8 @@ def check_cmp(name, st, ora, w):
     d = np.abs(oc - ora["ocmp"])
     assert d.max() < 1e-2 and d.mean() < 1e-3, f"O_cmp max {d.max():.3e} mean {d.mean():.3e}"
     frac, diff = check_selection(host(st.sel).numpy(), ora["score"], ora["sel"], w.topk,
-                                 forced=st.forced, qblocks=own_rows(w.H, st.Nb, st.own))
+                                 forced=st.forced, qblocks=own_rows(w.H, st.Nb, st.own),
+                                 dtype=w.dtype)
     print(f"[{name}] rows held to exact index parity: {frac:.1%}, near-tie rows differing: "
           f"{len(diff)}", flush=True)
 
@@ -207,7 +208,7 @@ def test_forward_single_vs_two_pass(name):
                                    cmp_mode=mode)
         torch.cuda.synchronize()
         check_selection(host(sel).numpy(), ora["score"], ora["sel"], w.topk, forced=st.forced,
-                        qblocks=own_rows(w.H, st.Nb, st.own))
+                        qblocks=own_rows(w.H, st.Nb, st.own), dtype=w.dtype)
         check_out(out, hx_out, what=f"out mode {mode}")
 
 

@@ -79,7 +79,7 @@ def test_windowed_forward_against_oracle(name):
     H, Nb = gsel.shape[:2]
     F = min(w.forced, Nb)
     frac, diff = check_selection(gsel, ora["score"], ora["sel"], w.topk, forced=F,
-                                 qblocks=own_rows(H, Nb, w.own and F < Nb))
+                                 qblocks=own_rows(H, Nb, w.own and F < Nb), dtype=w.dtype)
     print(f"[{name}] exact-index rows {frac:.1%}, near-tie rows differing {len(diff)}")
     ref = ora["out"]
     if not np.array_equal(gsel, ora["sel"]):
