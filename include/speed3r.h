@@ -21,8 +21,12 @@
  *     16-byte aligned. Query blocks and key blocks both have size B = params.block.
  *   - Numerics: logits are products of the input type accumulated in f32 (the pooled keys as a
  *     hi + lo pair of the input type); softmax runs in f32 with base-2 exponentials; the P.V
- *     products take fp16 operands with f32 accumulation, so values of v must stay below 65504
- *     in magnitude.
+ *     products take fp16 operands with f32 accumulation. bf16 values of v are held as fp16
+ *     after multiplying by 2^-8 (the outputs are multiplied back), which represents every
+ *     bf16 value below 65504 * 2^8 (about 1.68e7) in magnitude, exactly from 2^-6 up and
+ *     within 2^-17 below; fp16 values are held as they are. A bf16 value of v at or beyond
+ *     that limit becomes an infinity in its fp16 record, and every output that attends to it
+ *     is non-finite (never a wrong finite number).
  *   - Every pointer is device memory owned by the caller; the library never allocates, frees
  *     or synchronises. All work is enqueued on `stream` (NULL = the default stream) and the
  *     call returns before it completes. Asynchronous faults surface at the caller's next

@@ -15,6 +15,12 @@ namespace {
 // (38.7 GB at H = 16, Nb = 24576), and the exact tie search of the top-k kernel indexes up to 2^16.
 constexpr int64_t kMaxBlocks = 96 * 256;
 
+// The P.V products take fp16 value records. bf16 values are stored times 2^-8 (exact for
+// magnitudes 2^-6..2^24, within 2^-17 absolute below) and the outputs multiplied back by 2^8,
+// so bf16 values up to 65504 * 2^8 (about 1.68e7) in magnitude are represented; fp16 values
+// are stored as they are.
+constexpr float kVMultBf16 = 0x1p-8f;
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Dims {
@@ -133,6 +139,7 @@ PoolArgs pool_args(const s3r_params* p, const Dims& d, const void* k, const void
   a.k_st = p->k_stride_t; a.k_sh = p->k_stride_h; a.v_st = p->v_stride_t; a.v_sh = p->v_stride_h;
   a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.key_mult = d.scale * kLog2e;
+  a.v_mult = d.half ? 1.0f : kVMultBf16;
   a.k_mean = k_mean; a.v_mean = v_mean;
   a.tiles = (unsigned char*)ws + L.pooled;
   a.group_tiles = d.n_gtiles > 0 ? (unsigned char*)ws + L.groups : nullptr;
@@ -146,6 +153,7 @@ PackArgs pack_args(const s3r_params* p, const Dims& d, const void* k, const void
   a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.k_st = p->k_stride_t; a.k_sh = p->k_stride_h; a.v_st = p->v_stride_t; a.v_sh = p->v_stride_h;
   a.T = d.T; a.n_tiles = d.n_ktiles; a.H = d.H; a.half = d.half;
+  a.v_mult = d.half ? 1.0f : kVMultBf16;
   a.tiles = tiles;
   return a;
 }
@@ -158,6 +166,7 @@ CmpArgs cmp_args(const s3r_params* p, const Dims& d, const void* q, const void* 
   a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.tiles = (const unsigned char*)ws + L.pooled;
   a.ld = d.ld;
+  a.v_unscale = d.half ? 1.0f : 1.0f / kVMultBf16;
   return a;
 }
 
@@ -168,6 +177,7 @@ AttnArgs attn_args(const s3r_params* p, const Dims& d, const void* q,
   a.q = (const uint16_t*)q; a.q_st = p->q_stride_t; a.q_sh = p->q_stride_h;
   a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ktiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.logit_mult = d.scale * kLog2e;
+  a.v_unscale = d.half ? 1.0f : 1.0f / kVMultBf16;
   a.tiles = raw_tiles;
   a.k_eff = (int32_t)d.k_eff;
   a.gate_st = p->gate_stride_t;

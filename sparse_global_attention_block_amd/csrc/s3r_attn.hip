@@ -154,10 +154,11 @@ struct Flash {
     update(acc, rec + 4, lo, hi, mult, g);
   }
 
-  // 1 / softmax denominator per query, 0 for an empty softmax
-  __device__ void finish(float (&inv)[NT]) {
+  // unscale / softmax denominator per query (unscale undoes the power of two the value
+  // records were stored with), 0 for an empty softmax
+  __device__ void finish(float (&inv)[NT], float unscale) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) inv[nt] = (l[nt][0] > 0.f) ? 1.0f / l[nt][0] : 0.f;
+    for (int nt = 0; nt < NT; ++nt) inv[nt] = (l[nt][0] > 0.f) ? unscale / l[nt][0] : 0.f;
   }
 };
 
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   wait_vmem<0>();  // O_cmp has landed
 
   float inv[NT];
-  f.finish(inv);
+  f.finish(inv, a.v_unscale);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int64_t t = q0 + 16 * nt + li;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
     __syncthreads();
   }
   float inv[4];
-  f.finish(inv);
+  f.finish(inv, a.v_unscale);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t t = q0 + 16 * nt + li;

@@ -510,7 +510,8 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       if (g == 0 && t < a.T) a.lse[(int64_t)h * a.T + t] = (m + __log2f(l)) * kLn2 + a.lse_bias;
     }
   } else {
-    float zinv[4] = {1.f, 1.f, 1.f, 1.f};
+    // 1 / Z_t (single pass) times the undoing of the value records' power of two
+    float zinv[4] = {a.v_unscale, a.v_unscale, a.v_unscale, a.v_unscale};
     if constexpr (kSingle) {
       // Z_t and the exact L_t = offset + log2 Z_t. Z_t >= 1 proves offset <= L_t, i.e. every
       // weight was at least its probability, so each block's accumulated sum bounds its score
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
         const int64_t t = q0 + 16 * nt + li;
         zfail |= t < a.T && !(z >= 1.0f && z <= 0x1p15f);
         L2[nt] = (t < a.T && z > 0.f) ? off[nt] + __log2f(z) : INFINITY;
-        zinv[nt] = z > 0.f ? 1.0f / z : 0.f;
+        zinv[nt] = z > 0.f ? a.v_unscale / z : 0.f;
         if (g == 0 && t < a.T) a.lse[(int64_t)h * a.T + t] = L2[nt] * kLn2;
       }
       lds_barrier();  // every wave is done with the ring: each takes a quarter of it

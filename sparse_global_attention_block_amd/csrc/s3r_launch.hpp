@@ -14,6 +14,8 @@ struct PoolArgs {
   int32_t H, B;
   int32_t half;            // inputs are fp16 (else bf16)
   float key_mult;          // scale * log2(e), folded into the packed pooled keys
+  float v_mult;            // power of two the pooled values are multiplied by before their
+                           // fp16 records are written (kept in fp16 range; see v_unscale)
   float* k_mean; float* v_mean;  // optional f32 [H][Nb][64]
   unsigned char* tiles;    // [H][n_tiles][12 KB]
   unsigned char* group_tiles;  // optional [H][n_gtiles][12 KB] (K records only): key g is the
@@ -26,6 +28,7 @@ struct PackArgs {
   int64_t T, n_tiles;
   int32_t H;
   int32_t half;            // inputs are fp16 (else bf16)
+  float v_mult;            // power of two applied to v before its fp16 V^T records
   unsigned char* tiles;    // [H][n_tiles][8 KB]
 };
 
@@ -39,6 +42,7 @@ struct CmpArgs {
   float* lse;              // [H][T] natural log (written by the LSE pass, read by the fused pass)
   const float* lse_in;
   float* o_cmp;            // [T][H][64]
+  float v_unscale;         // 1 / v_mult of the pooled value records, applied to O_cmp
   float* score;            // [H][Nb][ld]
   int64_t ld;
   int32_t* sel;            // running top-k output [H][Nb][n_sel] (fused selection only)
@@ -78,6 +82,7 @@ struct AttnArgs {
   int32_t H, B;
   int32_t half;            // q, k and out are fp16 (else bf16)
   float logit_mult;        // scale * log2(e)
+  float v_unscale;         // 1 / v_mult of the raw value records, applied to the output
   const unsigned char* tiles;  // raw packed k/v tiles
   // selection only
   const int32_t* sel; int32_t k_eff;  // k_eff = entries per selection row (n_sel)

@@ -13,8 +13,8 @@ namespace s3r {
 // d8 = tid%8) sums block 32*tile + m over its tokens, 8 dims of k and of v at a time, in f32,
 // then divides by the block's token count (IEEE division). Writes the f32 means (optional)
 // and one pooled tile: the mean keys scaled by key_mult = scale*log2(e) as a hi + lo pair in the
-// input type (hi = round(x), lo = round(x - hi); bf16 or fp16), and the mean values as fp16
-// V^T records. Optionally also the group keys (means of 8 consecutive scaled pooled keys) of
+// input type (hi = round(x), lo = round(x - hi); bf16 or fp16), and the mean values times
+// v_mult (a power of two) as fp16 V^T records. Optionally also the group keys (means of 8 consecutive scaled pooled keys) of
 // the bound pass, in the K records of group tiles.
 template <bool kHalf>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   for (int e = 0; e < 8; ++e) {
     int rec, lane, slot;
     vt_position(m, d8 * 8 + e, rec, lane, slot);
-    vt[(rec * 64 + lane) * 8 + slot] = f16_bits(vs[e]);
+    vt[(rec * 64 + lane) * 8 + slot] = f16_bits(vs[e] * a.v_mult);
   }
   if (a.group_tiles) {
     // group key 4*tile + wave: the mean of the scaled pooled keys 8*(4*tile + wave)..+7, held
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 // One work-group per (head, group of kPackTiles tiles of 32 tokens). Thread (key m, dims d8)
-// copies 16 bytes of k into its K record slot and scatters 8 values of v, converted to fp16,
-// into the V^T records through LDS. Tokens beyond T are zero. In LDS, lane l's 16 bytes of a
+// copies 16 bytes of k into its K record slot and scatters 8 values of v, times v_mult and
+// converted to fp16, into the V^T records through LDS. Tokens beyond T are zero. In LDS, lane l's 16 bytes of a
 // V^T record sit at slot l ^ ((l >> 3) & 7): every lane of one 2-byte store writes the same
 // dim modulo 8, which the plain layout puts in 2 of the 32 banks; the copy out reads through
 // the same swizzle (a permutation inside aligned groups of 8 slots, free of conflicts).
@@ -154,7 +154,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     for (int e = 0; e < 8; ++e) {
       int rec, lane, slot;
       vt_position(m, d8 * 8 + e, rec, lane, slot);
-      vt[(rec * 64 + (lane ^ ((lane >> 3) & 7))) * 8 + slot] = f16_bits(vx[e]);  // exact for fp16
+      // exact for fp16 inputs (v_mult = 1) and for bf16 values of magnitude 2^-6..2^24
+      vt[(rec * 64 + (lane ^ ((lane >> 3) & 7))) * 8 + slot] = f16_bits(vx[e] * a.v_mult);
     }
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(out + 4 * kRecBytes);

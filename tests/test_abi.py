@@ -365,3 +365,4 @@ def test_binding_rejects_bad_result_buffers():
             S._check_sel(bad, p, q.device)
     with pytest.raises(ValueError, match="workspace"):
         S._check_workspace(torch.empty(64, dtype=torch.float32), q.device)
+

@@ -301,7 +301,11 @@ def test_dense_against_oracle(dtype):
         for h in (0, w.H - 1):
             for t0, nt in ((0, 37), (T - 50, 50)):
                 ref = O.dense_rows(hx["q"], hx["k"], hx["v"], h, t0, nt)
-                check_out(out[t0:t0 + nt, h], ref, what=f"dense {name} h={h} t0={t0}")
+                # dense outputs here are dominated by the x3 special-token values (|x| of
+                # 2-8, where bf16 rounding alone averages 4e-3-8e-3): the error beyond the
+                # output's rounding is held to both bounds, the plain mean is not
+                check_out(out[t0:t0 + nt, h], ref, what=f"dense {name} h={h} t0={t0}",
+                          plain_mean=False)
 
 
 def test_invalid_call_touches_nothing():
