@@ -57,7 +57,9 @@ typedef enum {
                               separate top-k kernel is needed (speed3r_topk, and B = 128 or
                               more than 64 chosen blocks) */
   S3R_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
-  S3R_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
+  S3R_ERR_HIP = 4,         /* a kernel launch failed (hipGetLastError) */
+  S3R_ERR_SCRATCH = 5      /* speed3r_sparse_attn_fwd_noalloc: the problem needs more than
+                              speed3r_noalloc_scratch_bytes() of workspace */
 } s3r_status;
 
 /* Element type of q, k, v and out. The model runs in bf16 or fp16 (README "Notice" 3). */
@@ -352,6 +354,27 @@ s3r_status speed3r_sparse_attn_fwd_windows(const s3r_params* p, const s3r_window
                                            const float* gates, void* out, int32_t* sel_idx,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
+
+/* ---- Forward pass without allocation -------------------------------------------------------
+ * For callers that cannot allocate device memory at call time (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same forward pass as
+ * speed3r_sparse_attn_fwd, with its workspace taken from a fixed array the library holds in
+ * device memory (one per GPU it runs on, kept until the process ends). */
+
+/* Size of that array: the largest speed3r_workspace_size the no-allocation entry point takes
+ * (512 MiB, e.g. 32 views x 1374 tokens x 16 heads at B = 64, k = 16). */
+size_t speed3r_noalloc_scratch_bytes(void);
+
+/* speed3r_sparse_attn_fwd without a workspace argument: arguments, results and errors as
+ * there, plus S3R_ERR_SCRATCH (nothing launched) when speed3r_workspace_size(p) exceeds
+ * speed3r_noalloc_scratch_bytes(). Calls nothing that allocates. The first call on a device
+ * looks up that device's array (S3R_ERR_HIP if the lookup fails). Every call on one GPU uses
+ * the same array: calls that overlap on one GPU (several streams, or several host threads
+ * without ordering) race and give wrong results; calls ordered on one stream are safe. Every
+ * part of the array a call reads is first written by that call, so nothing carries over. */
+s3r_status speed3r_sparse_attn_fwd_noalloc(const s3r_params* p, const void* q, const void* k,
+                                           const void* v, const float* gates, void* out,
+                                           int32_t* sel_idx, hipStream_t stream);
 
 /* ---- Measured ceilings (not part of the method) -------------------------------------------
  * The pages print no kernel figures; the kernels' roofline fractions are quoted against the

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/speed3r.h"
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
@@ -379,6 +381,33 @@ WindowCopyArgs copy_args(const WindowLayout& w, int64_t T, int32_t H, int32_t in
   return a;
 }
 
+// ---------------------------------------------------------------------------------------
+// Workspace without allocation: a fixed device array (one copy per GPU, held until the
+// process ends) that speed3r_sparse_attn_fwd_noalloc uses in place of a caller workspace.
+// Host code must not pass `scratch` itself to a kernel (on the host it names a stand-in, not
+// the device copy): its device address is looked up once per device and kept.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(512) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (the current device), looked up on first use.
+s3r_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return S3R_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return S3R_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return S3R_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +419,7 @@ const char* speed3r_status_string(s3r_status s) {
     case S3R_ERR_UNSUPPORTED: return "S3R_ERR_UNSUPPORTED";
     case S3R_ERR_WORKSPACE: return "S3R_ERR_WORKSPACE";
     case S3R_ERR_HIP: return "S3R_ERR_HIP";
+    case S3R_ERR_SCRATCH: return "S3R_ERR_SCRATCH";
   }
   return "S3R_ERR_UNKNOWN";
 }
@@ -583,6 +613,26 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
   const Layout L = layout(d);
   if ((st = check_ws(workspace, workspace_bytes, L.end)) != S3R_OK) return st;
   return run_forward(p, d, L, q, k, v, gates, out, sel_idx, (unsigned char*)workspace, nullptr,
+                     stream);
+}
+
+size_t speed3r_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+s3r_status speed3r_sparse_attn_fwd_noalloc(const s3r_params* p, const void* q, const void* k,
+                                           const void* v, const float* gates, void* out,
+                                           int32_t* sel_idx, hipStream_t stream) {
+  Dims d;
+  s3r_status st = check_params(p, &d);
+  if (st != S3R_OK) return st;
+  if (p->cmp_mode == S3R_CMP_SINGLE && !d.single_ok) return S3R_ERR_UNSUPPORTED;
+  if (!tok_ok(q) || !tok_ok(k) || !tok_ok(v) || !gates || !aligned(gates, 4) || !out ||
+      !aligned(out, 8) || (sel_idx && !aligned(sel_idx, 4)))
+    return S3R_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  if (L.end > kScratchBytes) return S3R_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != S3R_OK) return st;
+  return run_forward(p, d, L, q, k, v, gates, out, sel_idx, (unsigned char*)ws, nullptr,
                      stream);
 }
 

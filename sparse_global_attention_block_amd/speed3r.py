@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspeed3r.so")
 
-S3R_OK, S3R_ERR_INVALID_ARG, S3R_ERR_UNSUPPORTED, S3R_ERR_WORKSPACE, S3R_ERR_HIP = range(5)
+(S3R_OK, S3R_ERR_INVALID_ARG, S3R_ERR_UNSUPPORTED, S3R_ERR_WORKSPACE, S3R_ERR_HIP,
+ S3R_ERR_SCRATCH) = range(6)
 CMP_AUTO, CMP_TWO_PASS, CMP_SINGLE = range(3)  # s3r_cmp_mode
 
 
@@ -106,6 +107,9 @@ EXPORTS = {
                                                        ctypes.POINTER(Windows)] +
                                         [ctypes.c_void_p] * 6 +
                                         [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "speed3r_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "speed3r_sparse_attn_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Params)] +
+                                        [ctypes.c_void_p] * 6 + [ctypes.c_void_p]),
     "speed3r_calib_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p]),
     "speed3r_calib_mfma_flops": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32]),
@@ -280,6 +284,30 @@ def sparse_attn_fwd(q, k, v, gates, block: int, topk: int, scale: float = 0.0,
                                        _ptr(out), _ptr(sel_idx), _ptr(workspace),
                                        workspace.numel(), _stream())
     _check("speed3r_sparse_attn_fwd", st)
+    return out, sel_idx
+
+
+def noalloc_scratch_bytes() -> int:
+    """Largest workspace sparse_attn_fwd_noalloc takes (the library's fixed device array)."""
+    return int(lib().speed3r_noalloc_scratch_bytes())
+
+
+def sparse_attn_fwd_noalloc(q, k, v, gates, block: int, topk: int, out: torch.Tensor,
+                            sel_idx: Optional[torch.Tensor] = None, scale: float = 0.0,
+                            forced_blocks: int = 0, force_own: bool = False,
+                            cmp_mode: int = CMP_AUTO):
+    """The forward pass with the library's fixed workspace array: nothing is allocated, by
+    the library or here (out, and sel_idx if wanted, come from the caller). Calls on one GPU
+    must not overlap."""
+    p = make_params(q, k, v, block, topk, scale, gates, forced_blocks, force_own, cmp_mode)
+    _check_gates(gates, q)
+    _check_out(out, q)
+    if sel_idx is not None:
+        _check_sel(sel_idx, p, q.device)
+    st = lib().speed3r_sparse_attn_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(gates), _ptr(out), _ptr(sel_idx),
+                                               _stream())
+    _check("speed3r_sparse_attn_fwd_noalloc", st)
     return out, sel_idx
 
 

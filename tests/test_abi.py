@@ -33,7 +33,7 @@ def test_header_symbols_are_exported():
 
 def test_status_strings():
     for code, name in enumerate(["S3R_OK", "S3R_ERR_INVALID_ARG", "S3R_ERR_UNSUPPORTED",
-                                 "S3R_ERR_WORKSPACE", "S3R_ERR_HIP"]):
+                                 "S3R_ERR_WORKSPACE", "S3R_ERR_HIP", "S3R_ERR_SCRATCH"]):
         assert S.status_string(code) == name
     assert S.status_string(99) == "S3R_ERR_UNKNOWN"
 
@@ -366,3 +366,19 @@ def test_binding_rejects_bad_result_buffers():
     with pytest.raises(ValueError, match="workspace"):
         S._check_workspace(torch.empty(64, dtype=torch.float32), q.device)
 
+
+def test_noalloc_entry_point_validates_before_touching_the_device():
+    """The allocation-free forward pass rejects bad arguments and problems larger than its
+    fixed array before its first device call (so these run without a GPU)."""
+    L = S.lib()
+    cap = S.noalloc_scratch_bytes()
+    assert cap == 512 << 20
+    call = lambda pp, q=FAKE: L.speed3r_sparse_attn_fwd_noalloc(  # noqa: E731
+        ctypes.byref(pp), q, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert call(params(k=0)) == S.S3R_ERR_INVALID_ARG
+    assert call(params(D=32)) == S.S3R_ERR_UNSUPPORTED
+    assert call(params(), q=None) == S.S3R_ERR_INVALID_ARG
+    big = params(T=137_400, H=16, B=64, k=16)
+    assert S.workspace_size(big) > cap
+    assert call(big) == S.S3R_ERR_SCRATCH
+    assert S.workspace_size(params(T=43_968, H=16, B=64, k=16)) <= cap
