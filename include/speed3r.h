@@ -100,8 +100,10 @@ typedef struct {
   int32_t cmp_mode;     /* s3r_cmp_mode; 0 (zero-initialised) is automatic */
 } s3r_params;
 
-/* Human-readable name of a status code (static storage). */
-const char* speed3r_status_string(s3r_status s);
+/* Human-readable name of a status code (static storage); any other int gives
+ * "S3R_ERR_UNKNOWN". The code is taken as an int so that a value outside the enumeration is
+ * well defined. */
+const char* speed3r_status_string(int status);
 
 /* Nb = ceil(T / B), the number of key blocks (= query blocks). -1 if p is invalid. */
 int64_t speed3r_num_blocks(const s3r_params* p);

@@ -412,8 +412,8 @@ s3r_status scratch_address(void** out) {
 
 extern "C" {
 
-const char* speed3r_status_string(s3r_status s) {
-  switch (s) {
+const char* speed3r_status_string(int status) {
+  switch (status) {
     case S3R_OK: return "S3R_OK";
     case S3R_ERR_INVALID_ARG: return "S3R_ERR_INVALID_ARG";
     case S3R_ERR_UNSUPPORTED: return "S3R_ERR_UNSUPPORTED";
