@@ -8,13 +8,16 @@
 //
 // One work-group (4 waves) per score row. The row is streamed once with 16-byte loads and no
 // part of it is held in registers (so many rows are in flight per CU); in step 2 only the few
-// threads whose maximum reaches theta read their entries again.
-//  1. Each thread's maximum key over its entries (order-preserving 32-bit keys); theta = the
-//     k-th largest of those 256 maxima (bitwise search in one wave). The k largest thread
-//     maxima are k distinct entries >= theta, so every entry of the true top-k is >= theta.
-//  2. Entries >= theta (usually a few dozen) are compacted into LDS. Each
-//     candidate's rank is its number of better candidates; rank < k selects it, and its
-//     output slot is the number of selected candidates with a smaller index.
+// threads whose maximum reaches theta read entries again, and most of them one chunk.
+//  1. Each thread's maximum key over its entries (order-preserving 32-bit keys), the chunk
+//     that holds it, and the largest key among its other chunks; theta = the k-th largest of
+//     the 256 thread maxima (bitwise search in one wave). The k largest thread maxima are k
+//     distinct entries >= theta, so every entry of the true top-k is >= theta.
+//  2. Entries >= theta (usually a few dozen) are compacted into LDS: a thread whose other
+//     chunks all lie below theta re-reads only the chunk of its maximum, the others (ties, or
+//     several large entries in one thread) re-read all their chunks. Each candidate's rank is
+//     its number of better candidates; rank < k selects it, and its output slot is the number
+//     of selected candidates with a smaller index.
 //  3. If more than kCap candidates survive (heavy ties), an exact fallback finds the k-th key
 //     and the cut inside the tied keys by bitwise search over all entries (re-reading the
 //     row), then writes the selected indices in ascending order with block-wide prefix counts.
@@ -25,10 +28,11 @@ namespace s3r {
 
 constexpr int kCap = 256;
 
-// Unsigned key whose order equals the float order; -0 is folded onto +0 first.
+// Unsigned key whose order equals the float order; -0 is folded onto +0 first. Negative
+// numbers have every bit flipped, the others only the sign bit.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ int wave_sum(int x) {
@@ -74,15 +78,20 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     return *reinterpret_cast<const float4*>(src + (j0 < Nb ? j0 : 0));
   };
 
-  // 1. thread maxima, theta
-  uint32_t tmax = 0;
+  // 1. thread maxima (and where they are), theta
+  uint32_t tmax = 0;  // largest key of this thread's entries
+  uint32_t t2 = 0;    // largest key among its chunks other than cbest
+  int cbest = 0;      // first chunk holding tmax
 #pragma unroll 4
   for (int c = 0; c < nchunks; ++c) {
     int j0;
     const float4 v = load4(c, j0);
     const uint32_t m01 = max(key_of(v.x, j0), key_of(v.y, j0 + 1));
     const uint32_t m23 = max(key_of(v.z, j0 + 2), key_of(v.w, j0 + 3));
-    tmax = max(tmax, max(m01, m23));
+    const uint32_t m = max(m01, m23);
+    t2 = max(t2, min(tmax, m));  // the smaller of the old best and this chunk is "other"
+    cbest = m > tmax ? c : cbest;
+    tmax = max(tmax, m);
   }
   tmax_s[tid] = tmax;
   if (tid == 0) s_count = 0;
@@ -106,10 +115,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const uint32_t theta = s_theta;
 
   // 2. candidates >= theta: only a thread whose maximum reaches theta can hold one, so only
-  //    those threads (typically k or a few more of the 256) read their entries again
-  if (tmax >= theta)
-#pragma unroll 4
-  for (int c = 0; c < nchunks; ++c) {
+  //    those threads (typically k or a few more of the 256) read entries again: the chunk of
+  //    their maximum, or every chunk if another one also reaches theta
+  auto take = [&](int c) {
     int j0;
     const float4 v = load4(c, j0);
     const float f[4] = {v.x, v.y, v.z, v.w};
@@ -124,6 +132,12 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         }
       }
     }
+  };
+  if (t2 >= theta) {
+#pragma unroll 4
+    for (int c = 0; c < nchunks; ++c) take(c);
+  } else if (tmax >= theta) {
+    take(cbest);
   }
   __syncthreads();
   const int C = s_count;
