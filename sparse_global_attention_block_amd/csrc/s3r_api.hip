@@ -96,7 +96,8 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->single = d->single_ok && (p->cmp_mode == S3R_CMP_SINGLE ||
                                (p->cmp_mode == S3R_CMP_AUTO &&
                                 (2 * most <= kFusedTopkMaxK || d->Nb - d->forced <= 64)));
-  // the separate top-k kernel holds a score row in registers; the folded one has no limit
+  // the separate top-k kernel's exact tie search indexes a row with 16 bits and the score
+  // matrix grows as Nb^2; the folded selection has no limit
   if (!d->fold_topk && d->Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;
   return S3R_OK;
 }
