@@ -259,7 +259,7 @@ BwdLayout bwd_layout(const Dims& d) {
   BwdLayout B;
   size_t off = 0;
   B.bm_words = (d.Nb + 31) / 32;
-  B.qtiles = off; off += align256((size_t)d.H * d.n_ktiles * kQTileBytes);
+  B.qtiles = off; off += align256((size_t)d.H * d.n_ktiles * kQImgBytes);
   B.raw_bwd = off; off += align256((size_t)d.H * d.n_ktiles * kBwdTileBytes);
   B.pooled_bwd = off; off += align256((size_t)d.H * d.n_ctiles * kBwdTileBytes);
   B.qs = off; off += align256((size_t)d.H * d.T * 8 * sizeof(float));
@@ -703,10 +703,10 @@ s3r_status speed3r_sparse_attn_bwd(const s3r_params* p, const void* q, const voi
     return hip_status(launch_rec_pack(r, kind, stream));
   };
   const int64_t nk = d.n_ktiles, nc = d.n_ctiles, Nb64 = d.Nb * kD;
-  if ((st = pack(q, p->q_stride_t, p->q_stride_h, d.T, nk, ws + BL.qtiles, kQTileBytes, 0, 4096,
+  if ((st = pack(q, p->q_stride_t, p->q_stride_h, d.T, nk, ws + BL.qtiles, kQImgBytes, 0, -1,
                  0)) != S3R_OK ||
-      (st = pack(dout, dout_stride_t, dout_stride_h, d.T, nk, ws + BL.qtiles, kQTileBytes, 8192,
-                 12288, 0)) != S3R_OK ||
+      (st = pack(dout, dout_stride_t, dout_stride_h, d.T, nk, ws + BL.qtiles, kQImgBytes, 4096,
+                 -1, 0)) != S3R_OK ||
       (st = pack(v, p->v_stride_t, p->v_stride_h, d.T, nk, ws + BL.raw_bwd, kBwdTileBytes, 0, -1,
                  0)) != S3R_OK ||
       (st = pack(k, p->k_stride_t, p->k_stride_h, d.T, nk, ws + BL.raw_bwd, kBwdTileBytes, -1,

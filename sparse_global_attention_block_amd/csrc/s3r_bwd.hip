@@ -423,11 +423,12 @@ cmp_dkv_kernel(BwdArgs a) {
 
   const int64_t n = a.n_ktiles;  // query tiles
   const int64_t t_begin = part * n / kDkvParts, t_end = (part + 1) * n / kDkvParts;
-  const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) + (int64_t)h * n * kQU4;
+  constexpr int kImgU4 = kQImgBytes / 16;  // 512: R(q) then R(dout)
+  const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) + (int64_t)h * n * kImgU4;
   const float* qs = a.qs + (int64_t)h * a.T * 8;
-  // Only the row images R(q), R(dout) (8 KB) are read; each thread scatters its 16-byte
-  // chunks into the transposed images TR(q), TR(dout) while staging, which halves the bytes
-  // streamed. In LDS the TR records are swizzled (lane l's 16 bytes at slot tr_swizzle(l)):
+  // The query images hold only the row images R(q), R(dout) (8 KB); each thread scatters its
+  // 16-byte chunks into the transposed images TR(q), TR(dout) while staging, which halves the
+  // bytes streamed. In LDS the TR records are swizzled (lane l's 16 bytes at slot tr_swizzle(l)):
   // each 2-byte store instruction has every lane write the same dim modulo 8, which in the
   // plain layout puts all 64 lanes in 2 of the 32 banks; the swizzle spreads them over 16,
   // and it only permutes slots inside aligned groups of 8, so the operand reads stay free of
@@ -437,7 +438,7 @@ cmp_dkv_kernel(BwdArgs a) {
 #pragma unroll
   for (int x = 0; x < kChunks; ++x) {
     const int c = tid + x * kThreads;                      // chunk 0..511
-    rsrc[x] = (c < 256) ? c : 512 + (c - 256);             // uint4 index of the chunk
+    rsrc[x] = (c < 256) ? c : 512 + (c - 256);             // uint4 index in the LDS tile
     const int trbase = (c < 256) ? 256 : 768;              // its TR group
     const int rec = (c & 255) >> 6, lp = c & 63;
     const int m = 16 * (rec >> 1) + (lp & 15), d0 = 32 * (rec & 1) + 8 * (lp >> 4);
@@ -454,7 +455,7 @@ cmp_dkv_kernel(BwdArgs a) {
   auto fetch = [&](int b, int64_t t) {
     t = t < n ? t : n - 1;  // past the end the last tile is re-read (and never used)
 #pragma unroll
-    for (int x = 0; x < kChunks; ++x) r0[b][x] = qtl[t * kQU4 + rsrc[x]];
+    for (int x = 0; x < kChunks; ++x) r0[b][x] = qtl[t * kImgU4 + tid + x * kThreads];
     if (tid < kSU4) {
       const int64_t qi = t * kTileKeys + (tid >> 1);
       r2[b] = (qi < a.T) ? reinterpret_cast<const uint4*>(qs + qi * 8)[tid & 1]
@@ -760,18 +761,80 @@ hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Selection dk, dv. One work-group of 4 waves per (head, key block u). The block's key tiles
-// (1, 2 or 4 of 32 keys) are spread over the waves; waves that share a tile split the query
-// blocks that selected u (read in ascending order from the bitmap row) by rank, and their
-// partial sums are added in LDS in a fixed order. Per selecting query tile: S = q . K^T,
-// dP = dout . V^T, dv += (g1 P)^T . dout, dk += dS^T . q. The epilogue adds the compression
+// Selection dk, dv. One work-group of 4 waves per (head, key block u); wave w owns key tile
+// kt = w % KT of the block (KT = B/32 tiles of 32 keys, at least 1) and split w / KT of the
+// query tiles. Per selecting query tile: S = q . K^T, dP = dout . V^T, dv += (g1 P)^T . dout,
+// dk += dS^T . q. The epilogue adds the split sums in fixed order, then the compression
 // branch's pooled gradients spread over the block, dKc_u / n_u and dVc_u / n_u, and writes dk,
 // dv for every token of the block.
+//
+// The query blocks that chose u are listed in LDS first (bitmap row, ascending; up to
+// kSdListCap at a time), then their tiles stream through an LDS ring: a stage is the NSPLIT
+// tiles that the splits consume together, copied with global_load_lds by all four waves, up
+// to DEPTH - 1 stages ahead of the one computed on. Only the row images R(q), R(dout) and the
+// tile's 32 rows of per-query scalars are copied (9 KB a tile); the transposed operands
+// (queries in the k-slots, for dv and dk) are read from the row images with
+// ds_read_b64_tr_b16, which hands lane i of each 16-lane group column i of the four 16-element
+// rows that the group's lanes address. The ring is read with inline-asm LDS reads, each block
+// waiting for its own reads: an ordinary LDS read would make the compiler wait for every copy
+// in flight, since it cannot tell the ring's slots apart.
 // ---------------------------------------------------------------------------------------
-template <bool kHalf>
+constexpr int kSdTileLds = 9 * 1024;  // R(q) 4 KB, R(dout) 4 KB, scalars 32 x 8 floats
+constexpr int kSdRingTiles = 8;       // 72 KB of query tiles
+constexpr int kSdListCap = 1024;      // selecting query blocks listed at a time
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 4-byte global->LDS copy per lane: lane l's 4 bytes at src land at dst + 4 l (dst the same
+// for every lane). Out of line of the kernel template for the same reason as copy16_to_lds.
+__device__ __forceinline__ void copy4_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Two fp16 values -> the same two values rounded to bf16 (nearest even).
+__device__ __forceinline__ uint32_t f16x2_to_bf16x2(uint32_t w) {
+  return bf16_bits(in_to_float<true>(w & 0xFFFFu)) |
+         ((uint32_t)bf16_bits(in_to_float<true>(w >> 16)) << 16);
+}
+
+// Waits until at most p stages of L copies each are still in flight (p <= P).
+template <int L, int P>
+__device__ __forceinline__ void wait_stages(int64_t p) {
+  if constexpr (P <= 0) {
+    wait_vmem<0>();
+  } else {
+    if (p >= P) wait_vmem<P * L>();
+    else wait_stages<L, P - 1>(p);
+  }
+}
+
+template <int KT, bool kHalf>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void sel_dkv_kernel(
     BwdArgs a) {
-  __shared__ floatx4 red[3][16][64];
+  constexpr int NSPLIT = 4 / KT;                // waves sharing a key tile
+  constexpr int STAGE = NSPLIT * kSdTileLds;    // bytes per stage
+  constexpr int DEPTH = kSdRingTiles / NSPLIT;  // stages in the ring
+  constexpr int LOADS = 3 * NSPLIT;             // copies per wave per stage
+  static_assert(DEPTH >= 2, "at least one stage ahead");
+  static_assert((NSPLIT - 1) * KT * 16 * 64 * 16 <= kSdRingTiles * kSdTileLds,
+                "the split sums fit in the ring");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kSdRingTiles * kSdTileLds];
+  __shared__ int list[kSdListCap];
+  __shared__ int wsum[16];
   const int64_t total = (int64_t)a.H * a.Nb;
   const int64_t logical = xcd_logical_id(blockIdx.x, total);
   if (logical >= total) return;
@@ -779,9 +842,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int64_t u = logical % a.Nb;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int kt_per = (a.B <= kTileKeys) ? 1 : a.B / kTileKeys;
-  const int nsplit = 4 / kt_per;
-  const int kt = wave % kt_per, split = wave / kt_per;
+  const int kt = wave % KT, split = wave / KT;
   const int64_t k_lo = u * a.B;
   const int64_t k_hi = (k_lo + a.B < a.T) ? k_lo + a.B : a.T;
   const int64_t tile = k_lo / kTileKeys + kt;
@@ -811,91 +872,258 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       dV[s][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-  const uint4* qtl = reinterpret_cast<const uint4*>(a.qtiles) +
-                     (int64_t)h * a.n_ktiles * (kQTileBytes / 16);
-  const float* qs = a.qs + (int64_t)h * a.T * 8;
-  auto process = [&](int64_t i) {
-    const int64_t b_lo = i * a.B;
-    const int64_t b_hi = (b_lo + a.B < a.T) ? b_lo + a.B : a.T;
-    for (int64_t qt = b_lo / kTileKeys; qt * kTileKeys < b_hi; ++qt) {
-      const bf16x8* Q = reinterpret_cast<const bf16x8*>(qtl + qt * (kQTileBytes / 16));
-      float l2[2][4], g1[2][4], dl[2][4];
+  const uint32_t* bm = a.bitmap + ((int64_t)h * a.Nb + u) * a.bm_words;
+  // Lists the set bits of the bitmap row whose rank (ascending order) lies in
+  // [lo, lo + kSdListCap) and returns the row's count. 256 words per round, one per thread,
+  // four rounds loaded together; ranks from a scan over the threads.
+  auto build_list = [&](int64_t lo) -> int64_t {
+    int64_t base = 0;
+    for (int64_t w0 = 0; w0 < a.bm_words; w0 += 1024) {
+      uint32_t wd[4];
+      int cnt[4], inc[4];
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = qt * kTileKeys + 16 * qh + 4 * g + r;
-          l2[qh][r] = INFINITY;
-          g1[qh][r] = 0.f;
-          dl[qh][r] = 0.f;
-          if (t >= b_lo && t < b_hi) {
-            l2[qh][r] = qs[t * 8 + 3];
-            g1[qh][r] = qs[t * 8 + 4];
-            dl[qh][r] = qs[t * 8 + 5];
-          }
-        }
-      float pg[2][2][4], ds[2][2][4];
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const bf16x8 qa0 = Q[(2 * qh) * 64 + lane];
-        const bf16x8 qa1 = Q[(2 * qh + 1) * 64 + lane];
-        const bf16x8 oa0 = Q[512 + (2 * qh) * 64 + lane];
-        const bf16x8 oa1 = Q[512 + (2 * qh + 1) * 64 + lane];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          floatx4 x = mfma_in<kHalf>(qa0, kr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          x = mfma_in<kHalf>(qa1, kr[s][1], x);
-          floatx4 y = mfma_in<kHalf>(oa0, vr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          y = mfma_in<kHalf>(oa1, vr[s][1], y);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(x[r], a.logit_mult, -l2[qh][r]));
-            pg[qh][s][r] = g1[qh][r] * p;
-            ds[qh][s][r] = p * fmaf(g1[qh][r], y[r], -dl[qh][r]);
-          }
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int64_t w = w0 + 256 * r + tid;
+        wd[r] = (w < a.bm_words) ? bm[w] : 0u;
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 ap = pack8(pg[0][s][0], pg[0][s][1], pg[0][s][2], pg[0][s][3], pg[1][s][0],
-                                pg[1][s][1], pg[1][s][2], pg[1][s][3]);
-        const bf16x8 as = pack8(ds[0][s][0], ds[0][s][1], ds[0][s][2], ds[0][s][3], ds[1][s][0],
-                                ds[1][s][1], ds[1][s][2], ds[1][s][3]);
+      for (int r = 0; r < 4; ++r) {
+        cnt[r] = __builtin_popcount(wd[r]);
+        inc[r] = wave_inclusive_sum(cnt[r], lane);
+        if (lane == 63) wsum[4 * r + wave] = inc[r];
+      }
+      __syncthreads();
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const bf16x8 tro = Q[768 + mt * 64 + lane];
-          const bf16x8 trq = Q[256 + mt * 64 + lane];
-          dV[s][mt] = mfma16(ap, tro, dV[s][mt]);
-          dK[s][mt] = mfma16(as, trq, dK[s][mt]);
+      for (int r = 0; r < 4; ++r) {
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int x = wsum[4 * r + w];
+          before += (w < wave) ? x : 0;
+          all += x;
         }
+        int64_t rank = base + before + inc[r] - cnt[r] - lo;
+        const int64_t word = w0 + 256 * r + tid;
+        uint32_t bits = wd[r];
+        while (bits) {
+          const int b = __builtin_ctz(bits);
+          bits &= bits - 1;
+          if (rank >= 0 && rank < kSdListCap) list[rank] = (int)(word * 32 + b);
+          ++rank;
+        }
+        base += all;
+      }
+      __syncthreads();
+    }
+    return base;
+  };
+
+  const unsigned char* qtl = a.qtiles + (int64_t)h * a.n_ktiles * kQImgBytes;
+  const float* qs = a.qs + (int64_t)h * a.T * 8;
+  const uint32_t ring_lds = lds_address(ring);
+  // lane offsets of the transposed reads (lane 16g + 4j + q addresses query row 4g + j, dims
+  // 4q..4q+3 of a 16-dim group) and of the scalar reads (rows 4g + r)
+  const uint32_t tr_lane = (16 * ((lane & 3) >> 1) + 4 * g + ((lane >> 2) & 3)) * 16 +
+                           8 * (lane & 1);
+  const uint32_t qs_lane = 8192 + 128 * g;
+
+  // item i of the list: query tile i % KT of block list[i / KT] (for B = 16 the 32-row tile
+  // holding the block)
+  auto item_tile = [&](int blk, int64_t i) -> int64_t {
+    return (int64_t)blk * a.B / kTileKeys + i % KT;
+  };
+  // copies of stage n: per tile, wave w copies R(q) record w, R(dout) record w and scalar
+  // rows 8w..8w+7; items past the list re-read a valid tile that is never used
+  auto issue = [&](int64_t n, int64_t n_items) {
+    unsigned char* st = ring + (n % DEPTH) * STAGE;
+#pragma unroll
+    for (int j = 0; j < NSPLIT; ++j) {
+      const int64_t i = n * NSPLIT + j;
+      int64_t qt = (i < n_items) ? item_tile(list[i / KT], i) : 0;
+      qt = (qt < a.n_ktiles) ? qt : a.n_ktiles - 1;
+      const unsigned char* src = qtl + qt * kQImgBytes;
+      unsigned char* dst = st + j * kSdTileLds;
+      copy16_to_lds(src + wave * kRecBytes + 16 * lane, dst + wave * kRecBytes);
+      copy16_to_lds(src + 4096 + wave * kRecBytes + 16 * lane, dst + 4096 + wave * kRecBytes);
+      int64_t t = qt * kTileKeys + 8 * wave + (lane >> 3);
+      t = (t < a.T) ? t : a.T - 1;
+      copy4_to_lds(qs + t * 8 + (lane & 7), dst + 8192 + 256 * wave);
+    }
+  };
+
+  auto compute = [&](int64_t n, int64_t n_items) {
+    const int64_t i = n * NSPLIT + split;
+    if (i >= n_items) return;
+    const int64_t blk = list[i / KT];
+    const int64_t qt = item_tile((int)blk, i);
+    const int64_t b_lo = blk * a.B;
+    const int64_t b_hi = (b_lo + a.B < a.T) ? b_lo + a.B : a.T;
+    if (qt * kTileKeys >= b_hi) return;
+    const uint32_t sb = ring_lds + (uint32_t)((n % DEPTH) * STAGE + split * kSdTileLds);
+
+    // row images and per-row scalars in one block (one wait)
+    u32x4 rq[4], ro[4];
+    float l2[2][4];
+    u32x2 gd[2][4];  // (g1, g1 dout . O_sel) per row
+    asm volatile(
+        "ds_read_b128 %0, %24\n\t"
+        "ds_read_b128 %1, %24 offset:1024\n\t"
+        "ds_read_b128 %2, %24 offset:2048\n\t"
+        "ds_read_b128 %3, %24 offset:3072\n\t"
+        "ds_read_b128 %4, %24 offset:4096\n\t"
+        "ds_read_b128 %5, %24 offset:5120\n\t"
+        "ds_read_b128 %6, %24 offset:6144\n\t"
+        "ds_read_b128 %7, %24 offset:7168\n\t"
+        "ds_read_b32 %8, %25 offset:12\n\t"
+        "ds_read_b32 %9, %25 offset:44\n\t"
+        "ds_read_b32 %10, %25 offset:76\n\t"
+        "ds_read_b32 %11, %25 offset:108\n\t"
+        "ds_read_b32 %12, %25 offset:524\n\t"
+        "ds_read_b32 %13, %25 offset:556\n\t"
+        "ds_read_b32 %14, %25 offset:588\n\t"
+        "ds_read_b32 %15, %25 offset:620\n\t"
+        "ds_read_b64 %16, %25 offset:16\n\t"
+        "ds_read_b64 %17, %25 offset:48\n\t"
+        "ds_read_b64 %18, %25 offset:80\n\t"
+        "ds_read_b64 %19, %25 offset:112\n\t"
+        "ds_read_b64 %20, %25 offset:528\n\t"
+        "ds_read_b64 %21, %25 offset:560\n\t"
+        "ds_read_b64 %22, %25 offset:592\n\t"
+        "ds_read_b64 %23, %25 offset:624\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(rq[0]), "=&v"(rq[1]), "=&v"(rq[2]), "=&v"(rq[3]), "=&v"(ro[0]), "=&v"(ro[1]),
+          "=&v"(ro[2]), "=&v"(ro[3]), "=&v"(l2[0][0]), "=&v"(l2[0][1]), "=&v"(l2[0][2]),
+          "=&v"(l2[0][3]), "=&v"(l2[1][0]), "=&v"(l2[1][1]), "=&v"(l2[1][2]), "=&v"(l2[1][3]),
+          "=&v"(gd[0][0]), "=&v"(gd[0][1]), "=&v"(gd[0][2]), "=&v"(gd[0][3]), "=&v"(gd[1][0]),
+          "=&v"(gd[1][1]), "=&v"(gd[1][2]), "=&v"(gd[1][3])
+        : "v"(sb + 16 * lane), "v"(sb + qs_lane)
+        : "memory");
+
+    float pg[2][2][4], ds[2][2][4];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      float g1[4], dl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = qt * kTileKeys + 16 * qh + 4 * g + r;
+        const bool in = t >= b_lo && t < b_hi;
+        l2[qh][r] = in ? l2[qh][r] : INFINITY;
+        // (element copies first: a bit cast of a vector element reads element 0)
+        const uint32_t gx = gd[qh][r].x, gy = gd[qh][r].y;
+        g1[r] = in ? __builtin_bit_cast(float, gx) : 0.f;
+        dl[r] = in ? __builtin_bit_cast(float, gy) : 0.f;
+      }
+      const bf16x8 qa0 = __builtin_bit_cast(bf16x8, rq[2 * qh]);
+      const bf16x8 qa1 = __builtin_bit_cast(bf16x8, rq[2 * qh + 1]);
+      const bf16x8 oa0 = __builtin_bit_cast(bf16x8, ro[2 * qh]);
+      const bf16x8 oa1 = __builtin_bit_cast(bf16x8, ro[2 * qh + 1]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        floatx4 x = mfma_in<kHalf>(qa0, kr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        x = mfma_in<kHalf>(qa1, kr[s][1], x);
+        floatx4 y = mfma_in<kHalf>(oa0, vr[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        y = mfma_in<kHalf>(oa1, vr[s][1], y);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(x[r], a.logit_mult, -l2[qh][r]));
+          pg[qh][s][r] = g1[r] * p;
+          ds[qh][s][r] = p * fmaf(g1[r], y[r], -dl[r]);
+        }
+      }
+    }
+
+    // P^T and dS^T operands (keys 16s.., queries in the k-slots)
+    u32x4 apw[2], asw[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      apw[s] = __builtin_bit_cast(u32x4, pack8(pg[0][s][0], pg[0][s][1], pg[0][s][2], pg[0][s][3],
+                                               pg[1][s][0], pg[1][s][1], pg[1][s][2], pg[1][s][3]));
+      asw[s] = __builtin_bit_cast(u32x4, pack8(ds[0][s][0], ds[0][s][1], ds[0][s][2], ds[0][s][3],
+                                               ds[1][s][0], ds[1][s][1], ds[1][s][2], ds[1][s][3]));
+    }
+    // Transposed operands: [mt][query half], record (2 half + mt / 2), dims 16 (mt % 2)...
+    // The P^T, dS^T operands pass through the block: they are formed from every S and dP
+    // product, so no matrix product still reads a register when the block's reads land in
+    // registers the compiler has freed (it does not see the LDS writes inside the asm).
+    u32x2 tq[4][2], to[4][2];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %20\n\t"
+        "ds_read_b64_tr_b16 %1, %20 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %20 offset:512\n\t"
+        "ds_read_b64_tr_b16 %3, %20 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %5, %20 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %6, %20 offset:1536\n\t"
+        "ds_read_b64_tr_b16 %7, %20 offset:3584\n\t"
+        "ds_read_b64_tr_b16 %8, %20 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %9, %20 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %10, %20 offset:4608\n\t"
+        "ds_read_b64_tr_b16 %11, %20 offset:6656\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:5120\n\t"
+        "ds_read_b64_tr_b16 %13, %20 offset:7168\n\t"
+        "ds_read_b64_tr_b16 %14, %20 offset:5632\n\t"
+        "ds_read_b64_tr_b16 %15, %20 offset:7680\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(tq[0][0]), "=&v"(tq[0][1]), "=&v"(tq[1][0]), "=&v"(tq[1][1]), "=&v"(tq[2][0]),
+          "=&v"(tq[2][1]), "=&v"(tq[3][0]), "=&v"(tq[3][1]), "=&v"(to[0][0]), "=&v"(to[0][1]),
+          "=&v"(to[1][0]), "=&v"(to[1][1]), "=&v"(to[2][0]), "=&v"(to[2][1]), "=&v"(to[3][0]),
+          "=&v"(to[3][1]), "+v"(apw[0]), "+v"(apw[1]), "+v"(asw[0]), "+v"(asw[1])
+        : "v"(sb + tr_lane)
+        : "memory");
+    bf16x8 trq[4], tro[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      u32x4 wq = {tq[mt][0].x, tq[mt][0].y, tq[mt][1].x, tq[mt][1].y};
+      u32x4 wo = {to[mt][0].x, to[mt][0].y, to[mt][1].x, to[mt][1].y};
+      if constexpr (kHalf) {  // the products with P and dS take both operands in bf16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wq[e] = f16x2_to_bf16x2(wq[e]);
+          wo[e] = f16x2_to_bf16x2(wo[e]);
+        }
+      }
+      trq[mt] = __builtin_bit_cast(bf16x8, wq);
+      tro[mt] = __builtin_bit_cast(bf16x8, wo);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 ap = __builtin_bit_cast(bf16x8, apw[s]);
+      const bf16x8 as = __builtin_bit_cast(bf16x8, asw[s]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        dV[s][mt] = mfma16(ap, tro[mt], dV[s][mt]);
+        dK[s][mt] = mfma16(as, trq[mt], dK[s][mt]);
       }
     }
   };
 
-  if (active) {
-    // The bitmap row is read 64 words at a time, one per lane (most words are zero: a key
-    // block is chosen by a few dozen of the Nb query blocks); the set bits are then visited in
-    // ascending order, so every wave sees the same ranks and the split is deterministic.
-    const uint32_t* bm = a.bitmap + ((int64_t)h * a.Nb + u) * a.bm_words;
-    int64_t rank = 0;
-    for (int64_t w0 = 0; w0 < a.bm_words; w0 += 64) {
-      const uint32_t word = (w0 + lane < a.bm_words) ? bm[w0 + lane] : 0u;
-      uint64_t nz = __ballot(word != 0u);
-      while (nz) {
-        const int l = __builtin_ctzll(nz);
-        nz &= nz - 1;
-        uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)word, l);
-        while (bits) {
-          const int b = __builtin_ctz(bits);
-          bits &= bits - 1;
-          if (rank++ % nsplit == split) process((w0 + l) * 32 + b);
-        }
+  // every wave takes part in listing, copying and the barriers; waves whose key tile lies past
+  // the end of the sequence skip the products
+  const int64_t n_sel = build_list(0);
+  for (int64_t lo = 0; lo < n_sel; lo += kSdListCap) {
+    if (lo > 0) {
+      __syncthreads();  // the ring and the list are no longer read
+      build_list(lo);
+    }
+    const int64_t n_items = ((n_sel - lo < kSdListCap) ? n_sel - lo : kSdListCap) * KT;
+    const int64_t n_stages = (n_items + NSPLIT - 1) / NSPLIT;
+    int64_t issued = 0;
+    for (; issued < DEPTH - 1 && issued < n_stages; ++issued) issue(issued, n_items);
+    for (int64_t n = 0; n < n_stages; ++n) {
+      wait_stages<LOADS, DEPTH - 2>(issued - n - 1);  // this wave's copies of stage n landed
+      lds_barrier();  // everyone's copies of stage n landed; stage n - 1 has been read
+      if (issued < n_stages) {
+        issue(issued, n_items);
+        ++issued;
       }
+      if (active) compute(n, n_items);
     }
   }
-  if (nsplit > 1) {  // add the partial sums of the waves that share a tile, in split order
+  if (NSPLIT > 1) {  // add the partial sums of the waves that share a tile, in split order
+    floatx4(*red)[16][64] = reinterpret_cast<floatx4(*)[16][64]>(ring);
+    __syncthreads();  // the ring is free
     if (split > 0) {
-      const int slot = (split - 1) * kt_per + kt;
+      const int slot = (split - 1) * KT + kt;
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -906,8 +1134,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
     __syncthreads();
     if (split == 0) {
-      for (int sp = 1; sp < nsplit; ++sp) {
-        const int slot = (sp - 1) * kt_per + kt;
+      for (int sp = 1; sp < NSPLIT; ++sp) {
+        const int slot = (sp - 1) * KT + kt;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -922,6 +1150,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const float inv_n = 1.0f / (float)(k_hi - k_lo);
   const float* dkc = a.dkc + ((int64_t)h * a.Nb + u) * kD;
   const float* dvc = a.dvc + ((int64_t)h * a.Nb + u) * kD;
+  float ck[4], cv[4];  // the pooled gradients spread over the block, read before any store
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    ck[mt] = dkc[16 * mt + li] * inv_n;
+    cv[mt] = dvc[16 * mt + li] * inv_n;
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -930,10 +1164,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       if (t < k_lo || t >= k_hi) continue;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int dim = 16 * mt + li;
-        const int64_t o = (t * a.H + h) * kD + dim;
-        a.dk[o] = a.scale * dK[s][mt][r] + dkc[dim] * inv_n;
-        a.dv[o] = dV[s][mt][r] + dvc[dim] * inv_n;
+        const int64_t o = (t * a.H + h) * kD + 16 * mt + li;
+        a.dk[o] = a.scale * dK[s][mt][r] + ck[mt];
+        a.dv[o] = dV[s][mt][r] + cv[mt];
       }
     }
 }
@@ -941,8 +1174,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 hipError_t launch_sel_dkv(const BwdArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.H * a.Nb;
   const dim3 g3((unsigned)(((total + 7) / 8) * 8)), b3(256);
-  if (a.half) hipLaunchKernelGGL((sel_dkv_kernel<true>), g3, b3, 0, s, a);
-  else hipLaunchKernelGGL((sel_dkv_kernel<false>), g3, b3, 0, s, a);
+  switch (a.B) {
+    case 16:
+    case 32:
+      if (a.half) hipLaunchKernelGGL((sel_dkv_kernel<1, true>), g3, b3, 0, s, a);
+      else hipLaunchKernelGGL((sel_dkv_kernel<1, false>), g3, b3, 0, s, a);
+      break;
+    case 64:
+      if (a.half) hipLaunchKernelGGL((sel_dkv_kernel<2, true>), g3, b3, 0, s, a);
+      else hipLaunchKernelGGL((sel_dkv_kernel<2, false>), g3, b3, 0, s, a);
+      break;
+    case 128:
+      if (a.half) hipLaunchKernelGGL((sel_dkv_kernel<4, true>), g3, b3, 0, s, a);
+      else hipLaunchKernelGGL((sel_dkv_kernel<4, false>), g3, b3, 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

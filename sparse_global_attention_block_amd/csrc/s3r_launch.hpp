@@ -137,9 +137,12 @@ struct WindowCopyArgs {
 //   TR (dims as lanes):  record mt, lane l -> dim 16mt + l%16, slot e -> row vkey(l/16, e).
 // R images are in the input type (bf16 or fp16: they meet q, k in the logits and dP
 // products), TR images always bf16 (they meet P and dS in the dq, dk, dv products).
-// Query tile (16 KB per 32 queries): [R(q)][TR(q)][R(dout)][TR(dout)].
+// Query image (8 KB per 32 queries): [R(q)][R(dout)]; the kernels that need the transposed
+// images build them on chip (cmp_dkv: a 16 KB LDS tile [R(q)][TR(q)][R(dout)][TR(dout)];
+// sel_dkv: transposing LDS reads).
 // Raw backward tile (8 KB per 32 keys): [R(v)][TR(k)].
 // Pooled backward tile (8 KB per 32 pooled keys): [R(Vc)][TR(Kc)], from the f32 means.
+constexpr int kQImgBytes = 8 * 1024;
 constexpr int kQTileBytes = 16 * 1024;
 constexpr int kBwdTileBytes = 8 * 1024;
 
