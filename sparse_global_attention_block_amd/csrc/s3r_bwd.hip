@@ -779,7 +779,7 @@ hipError_t launch_sel_dq(const BwdArgs& a, hipStream_t s) {
 // waiting for its own reads: an ordinary LDS read would make the compiler wait for every copy
 // in flight, since it cannot tell the ring's slots apart.
 // ---------------------------------------------------------------------------------------
-constexpr int kSdTileLds = 9 * 1024;  // R(q) 4 KB, R(dout) 4 KB, scalars 32 x 8 floats
+constexpr int kSdTileLds = 9 * 1024;  // R(q) 4 KB, R(dout) 4 KB, scalars (512 B used)
 constexpr int kSdRingTiles = 8;       // 72 KB of query tiles
 constexpr int kSdListCap = 1024;      // selecting query blocks listed at a time
 
@@ -921,97 +921,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const unsigned char* qtl = a.qtiles + (int64_t)h * a.n_ktiles * kQImgBytes;
   const float* qs = a.qs + (int64_t)h * a.T * 8;
   const uint32_t ring_lds = lds_address(ring);
-  // lane offsets of the transposed reads (lane 16g + 4j + q addresses query row 4g + j, dims
-  // 4q..4q+3 of a 16-dim group) and of the scalar reads (rows 4g + r)
-  const uint32_t tr_lane = (16 * ((lane & 3) >> 1) + 4 * g + ((lane >> 2) & 3)) * 16 +
-                           8 * (lane & 1);
-  const uint32_t qs_lane = 8192 + 128 * g;
+  // LDS layout of a tile. Records: 16-byte chunk c of a record sits in slot tau(c), with
+  // tau(16 g' + i) = 16 g' + (i ^ 8 (g' & 1)) (an involution; the copying lane l fetches chunk
+  // tau(l)), so that the 32 lanes of a half-wave in a transposed read hit 16 distinct bank
+  // groups (rows 0..7 of dim chunks g' and g' + 1 would otherwise share them); the row reads
+  // stay conflict-free. Scalars: field-major, [L_sel, g1, g1 dout . O_sel, unused][32 rows].
+  const int tau_lane = lane ^ (8 * ((lane >> 4) & 1));
+  // transposed reads: lane 16g + 4j + q addresses query row i = 4g + j, dims 4q..4q+3 of a
+  // 16-dim group, i.e. chunk 16 g' + i with g' = 2 (mt & 1) + (q >> 1); the (mt, half) part of
+  // the address is the immediate offset
+  const int tq_hi = (lane & 3) >> 1;
+  const uint32_t tr_lane =
+      (16 * tq_hi + ((4 * g + ((lane >> 2) & 3)) ^ (8 * tq_hi))) * 16 + 8 * (lane & 1);
+  const uint32_t qs_lane = 8192 + 16 * g;  // rows 4g..4g+3 of a field
 
   // item i of the list: query tile i % KT of block list[i / KT] (for B = 16 the 32-row tile
-  // holding the block)
-  auto item_tile = [&](int blk, int64_t i) -> int64_t {
-    return (int64_t)blk * a.B / kTileKeys + i % KT;
+  // holding the block); tile indices fit 32 bits (T < 2^31)
+  auto item_tile = [&](int blk, int i) -> int {
+    return (int)((int64_t)blk * a.B / kTileKeys) + i % KT;
   };
+  const int n_qtiles = (int)a.n_ktiles;
+  const int T32 = (int)a.T;
   // copies of stage n: per tile, wave w copies R(q) record w, R(dout) record w and scalar
-  // rows 8w..8w+7; items past the list re-read a valid tile that is never used
-  auto issue = [&](int64_t n, int64_t n_items) {
+  // field w (qs[t][3 + w] of the tile's 32 rows, by lanes 0..31); items past the list re-read
+  // a valid tile that is never used
+  auto issue = [&](int n, int n_items) {
     unsigned char* st = ring + (n % DEPTH) * STAGE;
 #pragma unroll
     for (int j = 0; j < NSPLIT; ++j) {
-      const int64_t i = n * NSPLIT + j;
-      int64_t qt = (i < n_items) ? item_tile(list[i / KT], i) : 0;
-      qt = (qt < a.n_ktiles) ? qt : a.n_ktiles - 1;
-      const unsigned char* src = qtl + qt * kQImgBytes;
+      const int i = n * NSPLIT + j;
+      int qt = (i < n_items) ? item_tile(__builtin_amdgcn_readfirstlane(list[i / KT]), i) : 0;
+      qt = (qt < n_qtiles) ? qt : n_qtiles - 1;
+      const unsigned char* src = qtl + (int64_t)qt * kQImgBytes;
       unsigned char* dst = st + j * kSdTileLds;
-      copy16_to_lds(src + wave * kRecBytes + 16 * lane, dst + wave * kRecBytes);
-      copy16_to_lds(src + 4096 + wave * kRecBytes + 16 * lane, dst + 4096 + wave * kRecBytes);
-      int64_t t = qt * kTileKeys + 8 * wave + (lane >> 3);
-      t = (t < a.T) ? t : a.T - 1;
-      copy4_to_lds(qs + t * 8 + (lane & 7), dst + 8192 + 256 * wave);
+      copy16_to_lds(src + wave * kRecBytes + 16 * tau_lane, dst + wave * kRecBytes);
+      copy16_to_lds(src + 4096 + wave * kRecBytes + 16 * tau_lane, dst + 4096 + wave * kRecBytes);
+      int t = qt * kTileKeys + (lane & 31);
+      t = (t < T32) ? t : T32 - 1;
+      if (lane < 32) copy4_to_lds(qs + (int64_t)t * 8 + 3 + wave, dst + 8192 + 128 * wave);
     }
   };
 
-  auto compute = [&](int64_t n, int64_t n_items) {
-    const int64_t i = n * NSPLIT + split;
+  auto compute = [&](int n, int n_items) {
+    const int i = n * NSPLIT + split;
     if (i >= n_items) return;
-    const int64_t blk = list[i / KT];
-    const int64_t qt = item_tile((int)blk, i);
-    const int64_t b_lo = blk * a.B;
+    const int blk = __builtin_amdgcn_readfirstlane(list[i / KT]);
+    const int qt = item_tile(blk, i);
+    // rows of the tile inside the block: [lo_rel, hi_rel)
+    const int64_t b_lo = (int64_t)blk * a.B;
     const int64_t b_hi = (b_lo + a.B < a.T) ? b_lo + a.B : a.T;
-    if (qt * kTileKeys >= b_hi) return;
+    const int64_t t0 = (int64_t)qt * kTileKeys;
+    if (t0 >= b_hi) return;
+    const int lo_rel = (b_lo > t0) ? (int)(b_lo - t0) : 0;
+    const int hi_rel = (b_hi - t0 < kTileKeys) ? (int)(b_hi - t0) : kTileKeys;
     const uint32_t sb = ring_lds + (uint32_t)((n % DEPTH) * STAGE + split * kSdTileLds);
 
     // row images and per-row scalars in one block (one wait)
-    u32x4 rq[4], ro[4];
-    float l2[2][4];
-    u32x2 gd[2][4];  // (g1, g1 dout . O_sel) per row
+    u32x4 rq[4], ro[4], l2v[2], g1v[2], dlv[2];
     asm volatile(
-        "ds_read_b128 %0, %24\n\t"
-        "ds_read_b128 %1, %24 offset:1024\n\t"
-        "ds_read_b128 %2, %24 offset:2048\n\t"
-        "ds_read_b128 %3, %24 offset:3072\n\t"
-        "ds_read_b128 %4, %24 offset:4096\n\t"
-        "ds_read_b128 %5, %24 offset:5120\n\t"
-        "ds_read_b128 %6, %24 offset:6144\n\t"
-        "ds_read_b128 %7, %24 offset:7168\n\t"
-        "ds_read_b32 %8, %25 offset:12\n\t"
-        "ds_read_b32 %9, %25 offset:44\n\t"
-        "ds_read_b32 %10, %25 offset:76\n\t"
-        "ds_read_b32 %11, %25 offset:108\n\t"
-        "ds_read_b32 %12, %25 offset:524\n\t"
-        "ds_read_b32 %13, %25 offset:556\n\t"
-        "ds_read_b32 %14, %25 offset:588\n\t"
-        "ds_read_b32 %15, %25 offset:620\n\t"
-        "ds_read_b64 %16, %25 offset:16\n\t"
-        "ds_read_b64 %17, %25 offset:48\n\t"
-        "ds_read_b64 %18, %25 offset:80\n\t"
-        "ds_read_b64 %19, %25 offset:112\n\t"
-        "ds_read_b64 %20, %25 offset:528\n\t"
-        "ds_read_b64 %21, %25 offset:560\n\t"
-        "ds_read_b64 %22, %25 offset:592\n\t"
-        "ds_read_b64 %23, %25 offset:624\n\t"
+        "ds_read_b128 %0, %14\n\t"
+        "ds_read_b128 %1, %14 offset:1024\n\t"
+        "ds_read_b128 %2, %14 offset:2048\n\t"
+        "ds_read_b128 %3, %14 offset:3072\n\t"
+        "ds_read_b128 %4, %14 offset:4096\n\t"
+        "ds_read_b128 %5, %14 offset:5120\n\t"
+        "ds_read_b128 %6, %14 offset:6144\n\t"
+        "ds_read_b128 %7, %14 offset:7168\n\t"
+        "ds_read_b128 %8, %15\n\t"
+        "ds_read_b128 %9, %15 offset:64\n\t"
+        "ds_read_b128 %10, %15 offset:128\n\t"
+        "ds_read_b128 %11, %15 offset:192\n\t"
+        "ds_read_b128 %12, %15 offset:256\n\t"
+        "ds_read_b128 %13, %15 offset:320\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(rq[0]), "=&v"(rq[1]), "=&v"(rq[2]), "=&v"(rq[3]), "=&v"(ro[0]), "=&v"(ro[1]),
-          "=&v"(ro[2]), "=&v"(ro[3]), "=&v"(l2[0][0]), "=&v"(l2[0][1]), "=&v"(l2[0][2]),
-          "=&v"(l2[0][3]), "=&v"(l2[1][0]), "=&v"(l2[1][1]), "=&v"(l2[1][2]), "=&v"(l2[1][3]),
-          "=&v"(gd[0][0]), "=&v"(gd[0][1]), "=&v"(gd[0][2]), "=&v"(gd[0][3]), "=&v"(gd[1][0]),
-          "=&v"(gd[1][1]), "=&v"(gd[1][2]), "=&v"(gd[1][3])
-        : "v"(sb + 16 * lane), "v"(sb + qs_lane)
+          "=&v"(ro[2]), "=&v"(ro[3]), "=&v"(l2v[0]), "=&v"(l2v[1]), "=&v"(g1v[0]),
+          "=&v"(g1v[1]), "=&v"(dlv[0]), "=&v"(dlv[1])
+        : "v"(sb + 16 * tau_lane), "v"(sb + qs_lane)
         : "memory");
 
     float pg[2][2][4], ds[2][2][4];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
-      float g1[4], dl[4];
+      float l2[4], g1[4], dl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = qt * kTileKeys + 16 * qh + 4 * g + r;
-        const bool in = t >= b_lo && t < b_hi;
-        l2[qh][r] = in ? l2[qh][r] : INFINITY;
+        const int rel = 16 * qh + 4 * g + r;
+        const bool in = rel >= lo_rel && rel < hi_rel;
         // (element copies first: a bit cast of a vector element reads element 0)
-        const uint32_t gx = gd[qh][r].x, gy = gd[qh][r].y;
-        g1[r] = in ? __builtin_bit_cast(float, gx) : 0.f;
-        dl[r] = in ? __builtin_bit_cast(float, gy) : 0.f;
+        const uint32_t wl = l2v[qh][r], wg = g1v[qh][r], wd = dlv[qh][r];
+        l2[r] = in ? __builtin_bit_cast(float, wl) : INFINITY;
+        g1[r] = in ? __builtin_bit_cast(float, wg) : 0.f;
+        dl[r] = in ? __builtin_bit_cast(float, wd) : 0.f;
       }
       const bf16x8 qa0 = __builtin_bit_cast(bf16x8, rq[2 * qh]);
       const bf16x8 qa1 = __builtin_bit_cast(bf16x8, rq[2 * qh + 1]);
@@ -1025,7 +1026,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         y = mfma_in<kHalf>(oa1, vr[s][1], y);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(x[r], a.logit_mult, -l2[qh][r]));
+          const float p = fast_exp2(fmaf(x[r], a.logit_mult, -l2[r]));
           pg[qh][s][r] = g1[r] * p;
           ds[qh][s][r] = p * fmaf(g1[r], y[r], -dl[r]);
         }
@@ -1105,11 +1106,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       __syncthreads();  // the ring and the list are no longer read
       build_list(lo);
     }
-    const int64_t n_items = ((n_sel - lo < kSdListCap) ? n_sel - lo : kSdListCap) * KT;
-    const int64_t n_stages = (n_items + NSPLIT - 1) / NSPLIT;
-    int64_t issued = 0;
+    const int n_items = (int)((n_sel - lo < kSdListCap) ? n_sel - lo : kSdListCap) * KT;
+    const int n_stages = (n_items + NSPLIT - 1) / NSPLIT;
+    int issued = 0;
     for (; issued < DEPTH - 1 && issued < n_stages; ++issued) issue(issued, n_items);
-    for (int64_t n = 0; n < n_stages; ++n) {
+    for (int n = 0; n < n_stages; ++n) {
       wait_stages<LOADS, DEPTH - 2>(issued - n - 1);  // this wave's copies of stage n landed
       lds_barrier();  // everyone's copies of stage n landed; stage n - 1 has been read
       if (issued < n_stages) {
@@ -1119,7 +1120,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       if (active) compute(n, n_items);
     }
   }
-  if (NSPLIT > 1) {  // add the partial sums of the waves that share a tile, in split order
+  if (NSPLIT > 1 && n_sel > 0) {  // add the split sums of the waves sharing a tile, in order
     floatx4(*red)[16][64] = reinterpret_cast<floatx4(*)[16][64]>(ring);
     __syncthreads();  // the ring is free
     if (split > 0) {
