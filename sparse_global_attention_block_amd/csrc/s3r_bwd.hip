@@ -786,6 +786,32 @@ constexpr int kSdListCap = 1024;      // selecting query blocks listed at a time
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Two fp16 values -> the same two values rounded to bf16 (nearest even).
+__device__ __forceinline__ uint32_t f16x2_to_bf16x2(uint32_t w) {
+  return bf16_bits(in_to_float<true>(w & 0xFFFFu)) |
+         ((uint32_t)bf16_bits(in_to_float<true>(w >> 16)) << 16);
+}
+
+// Row images in LDS. 16-byte chunk c of a 1 KB record sits in slot tau(c), tau(16 g' + i) =
+// 16 g' + (i ^ 12 (g' & 1)) (an involution): measured with the LDS bank-conflict counter on
+// gfx950, both the transposed reads below and the 16-byte row-operand reads (lane l takes slot
+// tau(l)) are then free of conflicts (the plain layout conflicts on the transposed reads, and
+// XOR 4 or 8 alone on one of the two).
+__device__ __forceinline__ int chunk_slot(int c) { return c ^ (12 * ((c >> 4) & 1)); }
+
+// ds_read_b64_tr_b16 (gfx950): lane i of each 16-lane group receives column i of the four
+// 16-element rows that the group's lanes address (lanes 4j..4j+3 give row j, four elements
+// each). On a row image it yields a transposed operand: lane (n, g) gets, for query rows
+// 4g + j of a 16-row half, the element of dim n of a 16-dim group. Byte offset of this lane
+// in a record pair (mt, half): tr_lane_offset(lane) + 1024 (2 half + mt / 2) + 512 (mt % 2).
+// (It delivers about half the LDS bandwidth of a 16-byte read, 110 against 200 bytes per
+// clock per CU, measured; cmp_dkv, whose LDS pipe is busy, keeps building its transposed
+// images with 2-byte stores while staging: with these reads it was 20 % slower.)
+__device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, hi = (lane & 3) >> 1;
+  return (uint32_t)((16 * hi + ((4 * g + j) ^ (12 * hi))) * 16 + 8 * (lane & 1));
+}
+
 // 4-byte global->LDS copy per lane: lane l's 4 bytes at src land at dst + 4 l (dst the same
 // for every lane). Out of line of the kernel template for the same reason as copy16_to_lds.
 __device__ __forceinline__ void copy4_to_lds(const void* src, void* dst) {
@@ -803,12 +829,6 @@ __device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
     if (lane >= d) x += y;
   }
   return x;
-}
-
-// Two fp16 values -> the same two values rounded to bf16 (nearest even).
-__device__ __forceinline__ uint32_t f16x2_to_bf16x2(uint32_t w) {
-  return bf16_bits(in_to_float<true>(w & 0xFFFFu)) |
-         ((uint32_t)bf16_bits(in_to_float<true>(w >> 16)) << 16);
 }
 
 // Waits until at most p stages of L copies each are still in flight (p <= P).
@@ -921,18 +941,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const unsigned char* qtl = a.qtiles + (int64_t)h * a.n_ktiles * kQImgBytes;
   const float* qs = a.qs + (int64_t)h * a.T * 8;
   const uint32_t ring_lds = lds_address(ring);
-  // LDS layout of a tile. Records: 16-byte chunk c of a record sits in slot tau(c), with
-  // tau(16 g' + i) = 16 g' + (i ^ 8 (g' & 1)) (an involution; the copying lane l fetches chunk
-  // tau(l)), so that the 32 lanes of a half-wave in a transposed read hit 16 distinct bank
-  // groups (rows 0..7 of dim chunks g' and g' + 1 would otherwise share them); the row reads
-  // stay conflict-free. Scalars: field-major, [L_sel, g1, g1 dout . O_sel, unused][32 rows].
-  const int tau_lane = lane ^ (8 * ((lane >> 4) & 1));
-  // transposed reads: lane 16g + 4j + q addresses query row i = 4g + j, dims 4q..4q+3 of a
-  // 16-dim group, i.e. chunk 16 g' + i with g' = 2 (mt & 1) + (q >> 1); the (mt, half) part of
-  // the address is the immediate offset
-  const int tq_hi = (lane & 3) >> 1;
-  const uint32_t tr_lane =
-      (16 * tq_hi + ((4 * g + ((lane >> 2) & 3)) ^ (8 * tq_hi))) * 16 + 8 * (lane & 1);
+  // LDS layout of a tile: the row images with their chunks permuted (chunk_slot; the copying
+  // lane l fetches chunk chunk_slot(l)), then the scalars field-major, [L_sel, g1,
+  // g1 dout . O_sel, unused][32 rows]; transposed reads at tr_lane_offset.
+  const int tau_lane = chunk_slot(lane);
+  const uint32_t tr_lane = tr_lane_offset(lane);
   const uint32_t qs_lane = 8192 + 16 * g;  // rows 4g..4g+3 of a field
 
   // item i of the list: query tile i % KT of block list[i / KT] (for B = 16 the 32-row tile
