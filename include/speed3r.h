@@ -118,8 +118,8 @@ int64_t speed3r_num_selected(const s3r_params* p);
 int64_t speed3r_score_row_stride(const s3r_params* p);
 
 /* Bytes of workspace the per-stage entry points need (packed tiles of the pooled keys and
- * values, of the group keys of the bound pass, and of the raw keys and values). 0 if p is
- * invalid. */
+ * values, of the group keys of the bound pass, and of the raw keys and values, plus the
+ * blocks' f32 column sums [H][Nb][128] that pooling reads). 0 if p is invalid. */
 size_t speed3r_tiles_workspace_size(const s3r_params* p);
 
 /* Bytes of workspace speed3r_sparse_attn_fwd needs: the tiles plus LSE [H][T] f32, O_cmp
@@ -155,9 +155,11 @@ s3r_status speed3r_sparse_attn_fwd(const s3r_params* p, const void* q, const voi
  * speed3r_pool filled. */
 
 /* Compression branch, pooling (summary "Methodologie" 1, average pooling of blocks): fills the
- * workspace tiles from k and v. k_mean / v_mean (optional, f32 [H][Nb][64]) receive the block
- * means themselves: sum in f32 then an IEEE division by the block's token count. Also writes
- * the group keys that speed3r_cmp_lse_bound reads. */
+ * workspace tiles from k and v (k and v are read once: the raw tiles and each block's column
+ * sums come from one pass). k_mean / v_mean (optional, f32 [H][Nb][64]) receive the block means
+ * themselves: a sum in f32 (rows added in order within each 32-row tile, then the tiles of the
+ * block in order) then an IEEE division by the block's token count. Also writes the group keys
+ * that speed3r_cmp_lse_bound reads. */
 s3r_status speed3r_pool(const s3r_params* p, const void* k, const void* v, void* workspace,
                         size_t workspace_bytes, float* k_mean, float* v_mean,
                         hipStream_t stream);

@@ -44,7 +44,7 @@ struct Dims {
 
 // Workspace regions, in this order, each 256-byte aligned.
 struct Layout {
-  size_t pooled, groups, raw, lse, o_cmp, score, sel, redo, tiles_end, end;
+  size_t pooled, groups, raw, bsum, lse, o_cmp, score, sel, redo, tiles_end, end;
 };
 
 bool valid_stride(int64_t s) { return s >= 0 && (s % 8) == 0; }
@@ -111,6 +111,8 @@ Layout layout(const Dims& d) {
   off += align256((size_t)d.H * d.n_gtiles * kPooledTileBytes);
   L.raw = off;
   off += align256((size_t)d.H * d.n_ktiles * kRawTileBytes);
+  L.bsum = off;  // the blocks' column sums, from packing to pooling
+  off += align256((size_t)d.H * d.Nb * 128 * sizeof(float));
   L.tiles_end = off;
   L.lse = off;
   off += align256((size_t)d.H * d.T * sizeof(float));
@@ -143,6 +145,7 @@ PoolArgs pool_args(const s3r_params* p, const Dims& d, const void* k, const void
   a.T = d.T; a.Nb = d.Nb; a.n_tiles = d.n_ctiles; a.H = d.H; a.B = d.B; a.half = d.half;
   a.key_mult = d.scale * kLog2e;
   a.v_mult = d.half ? 1.0f : kVMultBf16;
+  a.bsum = (const float*)((unsigned char*)ws + L.bsum);
   a.k_mean = k_mean; a.v_mean = v_mean;
   a.tiles = (unsigned char*)ws + L.pooled;
   a.group_tiles = d.n_gtiles > 0 ? (unsigned char*)ws + L.groups : nullptr;
@@ -150,14 +153,16 @@ PoolArgs pool_args(const s3r_params* p, const Dims& d, const void* k, const void
   return a;
 }
 
+// bsum: where the blocks' column sums for pooling go (null: raw tiles only)
 PackArgs pack_args(const s3r_params* p, const Dims& d, const void* k, const void* v,
-                   unsigned char* tiles) {
+                   unsigned char* tiles, float* bsum) {
   PackArgs a;
   a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.k_st = p->k_stride_t; a.k_sh = p->k_stride_h; a.v_st = p->v_stride_t; a.v_sh = p->v_stride_h;
   a.T = d.T; a.n_tiles = d.n_ktiles; a.H = d.H; a.half = d.half;
   a.v_mult = d.half ? 1.0f : kVMultBf16;
   a.tiles = tiles;
+  a.bsum = bsum; a.Nb = d.Nb; a.B = d.B;
   return a;
 }
 
@@ -286,10 +291,10 @@ s3r_status run_forward(const s3r_params* p, const Dims& d, const Layout& L, cons
   int32_t* sel = sel_idx ? sel_idx : (int32_t*)(ws + L.sel);
   float* k_mean = train ? (float*)(ws + train->k_mean) : nullptr;
   float* v_mean = train ? (float*)(ws + train->v_mean) : nullptr;
-  if ((st = hip_status(launch_pool(pool_args(p, d, k, v, ws, L, k_mean, v_mean), stream))) !=
-      S3R_OK)
-    return st;
-  if ((st = hip_status(launch_pack(pack_args(p, d, k, v, ws + L.raw), stream))) != S3R_OK)
+  if ((st = hip_status(launch_pack(pack_args(p, d, k, v, ws + L.raw, (float*)(ws + L.bsum)),
+                                     stream))) != S3R_OK ||
+      (st = hip_status(launch_pool(pool_args(p, d, k, v, ws, L, k_mean, v_mean), stream))) !=
+          S3R_OK)
     return st;
   CmpArgs c = cmp_args(p, d, q, ws, L);
   c.o_cmp = o_cmp;
@@ -466,10 +471,10 @@ s3r_status speed3r_pool(const s3r_params* p, const void* k, const void* v, void*
     return S3R_ERR_INVALID_ARG;
   const Layout L = layout(d);
   if ((st = check_ws(workspace, workspace_bytes, L.tiles_end)) != S3R_OK) return st;
-  st = hip_status(launch_pool(pool_args(p, d, k, v, workspace, L, k_mean, v_mean), stream));
+  unsigned char* ws = (unsigned char*)workspace;
+  st = hip_status(launch_pack(pack_args(p, d, k, v, ws + L.raw, (float*)(ws + L.bsum)), stream));
   if (st != S3R_OK) return st;
-  return hip_status(
-      launch_pack(pack_args(p, d, k, v, (unsigned char*)workspace + L.raw), stream));
+  return hip_status(launch_pool(pool_args(p, d, k, v, workspace, L, k_mean, v_mean), stream));
 }
 
 s3r_status speed3r_cmp_lse(const s3r_params* p, const void* q, const void* workspace,
@@ -776,7 +781,8 @@ s3r_status speed3r_dense_attn_fwd(const s3r_params* p, const void* q, const void
   const size_t need = align256((size_t)d.H * d.n_ktiles * kRawTileBytes);
   if ((st = check_ws(workspace, workspace_bytes, need)) != S3R_OK) return st;
   unsigned char* raw = (unsigned char*)workspace;
-  if ((st = hip_status(launch_pack(pack_args(p, d, k, v, raw), stream))) != S3R_OK) return st;
+  if ((st = hip_status(launch_pack(pack_args(p, d, k, v, raw, nullptr), stream))) != S3R_OK)
+    return st;
   AttnArgs a = attn_args(p, d, q, raw);
   a.out = (uint16_t*)out;
   return hip_status(launch_dense(a, stream));

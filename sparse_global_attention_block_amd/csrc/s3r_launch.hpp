@@ -16,6 +16,8 @@ struct PoolArgs {
   float key_mult;          // scale * log2(e), folded into the packed pooled keys
   float v_mult;            // power of two the pooled values are multiplied by before their
                            // fp16 records are written (kept in fp16 range; see v_unscale)
+  const float* bsum;       // [H][Nb][128] f32 column sums of each block's k (64) and v (64)
+                           // rows, written by the packing kernel
   float* k_mean; float* v_mean;  // optional f32 [H][Nb][64]
   unsigned char* tiles;    // [H][n_tiles][12 KB]
   unsigned char* group_tiles;  // optional [H][n_gtiles][12 KB] (K records only): key g is the
@@ -30,6 +32,9 @@ struct PackArgs {
   int32_t half;            // inputs are fp16 (else bf16)
   float v_mult;            // power of two applied to v before its fp16 V^T records
   unsigned char* tiles;    // [H][n_tiles][8 KB]
+  float* bsum;             // optional [H][Nb][128]: per block of B tokens, the f32 column sums
+  int64_t Nb;              // of its k rows (dims 0..63) and v rows (64..127), for pooling
+  int32_t B;
 };
 
 struct CmpArgs {

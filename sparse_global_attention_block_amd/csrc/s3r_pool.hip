@@ -2,20 +2,21 @@
 //
 // Pooling follows the compression branch of the Speed3R technical summary (gist.science,
 // "Methodologie" section 1): each contiguous block of B tokens of the keys and values is
-// replaced by its mean. Both kernels stream q/k/v-shaped bf16 tensors once and are bound by
-// HBM bandwidth.
+// replaced by its mean. The packing kernel streams k and v once (raw tiles plus the blocks'
+// column sums) and is bound by HBM bandwidth; pooling then reads only the sums.
 #include "s3r_common.hpp"
 #include "s3r_launch.hpp"
 
 namespace s3r {
 
 // One work-group per (head, tile of 32 consecutive blocks). Thread (slot m = tid/8, dim group
-// d8 = tid%8) sums block 32*tile + m over its tokens, 8 dims of k and of v at a time, in f32,
-// then divides by the block's token count (IEEE division). Writes the f32 means (optional)
-// and one pooled tile: the mean keys scaled by key_mult = scale*log2(e) as a hi + lo pair in the
-// input type (hi = round(x), lo = round(x - hi); bf16 or fp16), and the mean values times
-// v_mult (a power of two) as fp16 V^T records. Optionally also the group keys (means of 8 consecutive scaled pooled keys) of
-// the bound pass, in the K records of group tiles.
+// d8 = tid%8) takes block 32*tile + m: the f32 column sums of its k and v rows (written by the
+// packing kernel, which reads k and v once for both), divided by the block's token count
+// (IEEE division). Writes the f32 means (optional) and one pooled tile: the mean keys scaled
+// by key_mult = scale*log2(e) as a hi + lo pair in the input type (hi = round(x), lo =
+// round(x - hi); bf16 or fp16), and the mean values times v_mult (a power of two) as fp16 V^T
+// records. Optionally also the group keys (means of 8 consecutive scaled pooled keys) of the
+// bound pass, in the K records of group tiles.
 template <bool kHalf>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[kPooledTileBytes];
@@ -27,28 +28,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   float ks[8], vs[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { ks[e] = 0.f; vs[e] = 0.f; }
-  int64_t n = 0;
   if (j < a.Nb) {
     const int64_t t0 = j * a.B;
-    const int64_t t1 = (t0 + a.B < a.T) ? t0 + a.B : a.T;
-    n = t1 - t0;
-    const u16* kp = a.k + t0 * a.k_st + (int64_t)h * a.k_sh + d8 * 8;
-    const u16* vp = a.v + t0 * a.v_st + (int64_t)h * a.v_sh + d8 * 8;
-    for (int64_t t = 0; t < n; ++t) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(kp + t * a.k_st);
-      const uint4 vv = *reinterpret_cast<const uint4*>(vp + t * a.v_st);
-      float kx[8], vx[8];
-      unpack8<kHalf>(kk, kx);
-      unpack8<kHalf>(vv, vx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ks[e] += kx[e];
-        vs[e] += vx[e];
-      }
-    }
+    const int64_t n = ((t0 + a.B < a.T) ? t0 + a.B : a.T) - t0;
+    const float4* bs = reinterpret_cast<const float4*>(a.bsum + ((int64_t)h * a.Nb + j) * 128);
+    const float4 k0 = bs[2 * d8], k1 = bs[2 * d8 + 1], v0 = bs[16 + 2 * d8], v1 = bs[17 + 2 * d8];
+    const float kx[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const float vx[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     const float fn = (float)n;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { ks[e] = ks[e] / fn; vs[e] = vs[e] / fn; }
+    for (int e = 0; e < 8; ++e) { ks[e] = kx[e] / fn; vs[e] = vx[e] / fn; }
     if (a.k_mean) {
       float4* km = reinterpret_cast<float4*>(a.k_mean + ((int64_t)h * a.Nb + j) * kD + d8 * 8);
       km[0] = make_float4(ks[0], ks[1], ks[2], ks[3]);
@@ -129,13 +118,20 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 // V^T record sit at slot l ^ ((l >> 3) & 7): every lane of one 2-byte store writes the same
 // dim modulo 8, which the plain layout puts in 2 of the 32 banks; the copy out reads through
 // the same swizzle (a permutation inside aligned groups of 8 slots, free of conflicts).
+// With bsum set, the same read of k and v also yields the pooling sums: each thread puts its
+// 8 + 8 values in an LDS row of the tile (rows padded to 129 floats: conflict-free both ways),
+// and thread c of the first 128 (of 256 for B = 16, one per half tile) adds column c over the
+// tile's rows of its block in row order, and over the tiles of a block in tile order
+// (kPackTiles * 32 = 128 tokens is a whole number of blocks).
 constexpr int kPackTiles = 4;
 template <bool kHalf>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[4 * kRecBytes];
+  __shared__ float red[kTileKeys][129];
   const int tid = threadIdx.x;
   const int m = tid >> 3, d8 = tid & 7;
   const int h = blockIdx.y;
+  float run = 0.f;  // (bsum, B >= 32, tid < 128) running sum of column tid over the block
   for (int it = 0; it < kPackTiles; ++it) {
     const int64_t tile = (int64_t)blockIdx.x * kPackTiles + it;
     if (tile >= a.n_tiles) break;
@@ -157,10 +153,42 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       // exact for fp16 inputs (v_mult = 1) and for bf16 values of magnitude 2^-6..2^24
       vt[(rec * 64 + (lane ^ ((lane >> 3) & 7))) * 8 + slot] = f16_bits(vx[e] * a.v_mult);
     }
+    if (a.bsum) {
+      float kx[8];
+      unpack8<kHalf>(kk, kx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        red[m][d8 * 8 + e] = kx[e];
+        red[m][64 + d8 * 8 + e] = vx[e];
+      }
+    }
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(out + 4 * kRecBytes);
     const int l = tid & 63;
     dst[tid] = reinterpret_cast<const uint4*>(stage)[(tid & ~63) | (l ^ ((l >> 3) & 7))];
+    if (a.bsum) {
+      if (a.B >= kTileKeys) {
+        if (tid < 128) {
+          float s = 0.f;
+#pragma unroll 8
+          for (int r = 0; r < kTileKeys; ++r) s += red[r][tid];
+          run += s;
+          // the block ends with this tile
+          if ((tile + 1) * kTileKeys % a.B == 0 || tile + 1 == a.n_tiles) {
+            const int64_t blk = tile * kTileKeys / a.B;
+            a.bsum[((int64_t)h * a.Nb + blk) * 128 + tid] = run;
+            run = 0.f;
+          }
+        }
+      } else {  // B = 16: two blocks per tile
+        const int half = tid >> 7, c = tid & 127;
+        float s = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < 16; ++r) s += red[16 * half + r][c];
+        const int64_t blk = 2 * tile + half;
+        if (blk < a.Nb) a.bsum[((int64_t)h * a.Nb + blk) * 128 + c] = s;
+      }
+    }
     __syncthreads();
   }
 }
