@@ -94,10 +94,10 @@ def work_of(w: W.Workload, T: int, Nb: int, topk: int):
     k_eff = forced + own + min(topk, Nb - forced - own)
     sel_keys = sum(min(T, (j + 1) * B) - j * B for j in range(min(k_eff, Nb)))  # ~ k*B
     return {
-        # reads k and v once (2 x 128 B per token-head), writes 12 KB per 32 pooled tokens
-        "pool": {"bytes": th * 256 + H * math.ceil(Nb / 32) * 12288, "bound": "hbm"},
-        # reads k and v, writes them back as packed tiles
-        "pack": {"bytes": th * 256 * 2, "bound": "hbm"},
+        # the pool stage (packing kernel, then pooling from the blocks' column sums): reads k
+        # and v once (2 x 128 B per token-head), writes them back as packed raw tiles and
+        # writes 12 KB per 32 pooled tokens
+        "pool": {"bytes": th * 256 * 2 + H * math.ceil(Nb / 32) * 12288, "bound": "hbm"},
         # logits q.Kc over all pooled keys: 2D per (token, head, block); the kernel multiplies
         # by the hi and the lo part of every pooled key (4D)
         "cmp_lse": {"flops": 2 * D * th * Nb, "flops_exec": 4 * D * th * Nb, "bound": "mfma"},
@@ -209,10 +209,7 @@ def stage_kernels(w, x, topk, reps, single, ceil, T, Nb):
     work = work_of(w, T, Nb, topk)
     kernels = {}
     for name, ms_k in stage_ms.items():
-        wk = work[name]
-        if name == "pool":  # pool stage = pool kernel + pack kernel
-            wk = {"bytes": work["pool"]["bytes"] + work["pack"]["bytes"], "bound": "hbm"}
-        kernels[name] = rate(name, ms_k, wk, ceil)
+        kernels[name] = rate(name, ms_k, work[name], ceil)
     del st
     torch.cuda.empty_cache()
     return kernels, redone
