@@ -44,6 +44,12 @@ CASES = {
                                        own=True), 3 * 1374, {}),
     "tiny_f3_own": (dataclasses.replace(W.WORKLOADS["tiny"], name="tiny_f3_own", forced=3,
                                         own=True), None, {}),
+    # the first 2 key blocks are chosen by every one of more than 1024 query blocks, so the
+    # dk/dv kernel lists their selecting blocks in several chunks
+    "b16_chunked": (dataclasses.replace(_tiny_s, name="b16_chunked", H=1, block=16, topk=2,
+                                        forced=2), 1100 * 16 + 5, {}),
+    "b64_chunked": (dataclasses.replace(_tiny_s, name="b64_chunked", H=1, block=64, topk=2,
+                                        forced=2), 1030 * 64 + 17, {}),
     # a second block of a single token, and a single token
     "t17": (dataclasses.replace(_tiny_s, name="t17", H=2, block=16, topk=1), 17, {}),
     # one token: both softmaxes have a single key, so dq and dk vanish in exact arithmetic
