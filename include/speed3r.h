@@ -125,7 +125,7 @@ size_t speed3r_tiles_workspace_size(const s3r_params* p);
 /* Bytes of workspace speed3r_sparse_attn_fwd needs: the tiles plus LSE [H][T] f32, O_cmp
  * [T][H][64] f32, the selected indices, the redo flags when the forward pass runs the single
  * compression pass and, only when the selection cannot be folded into the compression pass
- * (B = 128 or more than 64 chosen blocks), the score matrix [H][Nb][ld] f32. About 11.5 GB
+ * (B = 128 or more than 64 chosen blocks), the score matrix [H][Nb][ld] f32. About 11.7 GB
  * at T = 1,374,000, H = 16, B = 64, k = 16. 0 if p is invalid. */
 size_t speed3r_workspace_size(const s3r_params* p);
 
@@ -288,7 +288,7 @@ s3r_status speed3r_sparse_attn_fwd_train(const s3r_params* p, const void* q, con
 /* Bytes of scratch speed3r_sparse_attn_bwd needs: operand tiles of q, dout, k, v and the
  * block means, per-token scalars, the pooled gradients, a [H][Nb][ceil(Nb/32)] selection
  * bitmap, per-token gate gradients and four partial sums of the pooled gradients (about
- * 19.7 GB at T = 1,374,000, H = 16, B = 64). */
+ * 14.0 GB at T = 1,374,000, H = 16, B = 64). */
 size_t speed3r_bwd_workspace_size(const s3r_params* p);
 
 /* Gradients of the sparse forward pass. q, k, v, gates and p must be those of the
