@@ -55,7 +55,7 @@ def test_size_queries():
     assert all(a < b for a, b in zip(sizes, sizes[1:])), "workspace must grow with T"
     assert S.tiles_workspace_size(p) < S.workspace_size(p)
     assert S.dense_workspace_size(p) > 0
-    # 1000 views x 1374 tokens, 16 heads, B = 64, k = 16: about 11.5 GB
+    # 1000 views x 1374 tokens, 16 heads, B = 64, k = 16: about 11.7 GB
     big = params(T=1_374_000, H=16, B=64, k=16)
     assert 10e9 < S.workspace_size(big) < 13e9
     big128 = params(T=1_374_000, H=16, B=128, k=16)
