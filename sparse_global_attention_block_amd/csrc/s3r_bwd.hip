@@ -818,19 +818,6 @@ __device__ __forceinline__ void copy4_to_lds(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
 // Waits until at most p stages of L copies each are still in flight (p <= P).
 template <int L, int P>
 __device__ __forceinline__ void wait_stages(int64_t p) {

@@ -244,6 +244,21 @@ __device__ __forceinline__ void wait_lds() {  // every LDS (and scalar-memory) o
   asm volatile("" ::: "memory");
 }
 
+// inclusive prefix sum over the lanes of a wave
+__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// LDS byte address of a __shared__ object (for inline asm)
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Direct global->LDS copy of 16 bytes per lane: lane l's 16 bytes at src land at dst + 16 l
 // (dst the same for every lane of the wave). Counts on vmcnt like a load. (Kept out of line of
 // kernel templates: there the host pass of hipcc rejects the builtin and silently drops the
