@@ -234,7 +234,28 @@ __device__ __forceinline__ bool sel_advance(const AttnArgs& a, const int32_t* ro
 
 constexpr int kSelSlots = 2;  // tiles in flight per wave (the vmcnt waits below assume 2)
 
-template <int NT, bool kHalf>
+// The eight 1 KB records of a tile slot (this lane's 16 bytes of each), read in one asm block
+// that waits for its own reads. Written as plain loads, the reads would be ordered behind
+// every global->LDS copy in flight (the compiler cannot tell that those fill other slots).
+__device__ __forceinline__ void read_tile8(uint32_t addr, bf16x8 (&r)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(addr)
+      : "memory");
+}
+
+
+template <int NT, bool kHalf, bool kPre = false>
 __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   __shared__ uint4 ring[4][kSelSlots][kRawTileBytes / 16];  // 16 KB per wave
   // wave-uniform as far as the compiler can see: the LDS copy destinations (M0), the item and
@@ -277,6 +298,66 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
 
   Flash<NT, kHalf> f;
   f.init();
+  if constexpr (kPre) {
+    // The row's step schedule, built once (rows of at most 64 entries and 128 tile steps):
+    // lane e holds entry e, which counts if its block is valid and differs from the last
+    // valid entry before it (the walk's rule: a block repeated right away counts once); its
+    // tiles become steps incl - c .. incl - 1, scattered through this wave's second slot
+    // (no copy has been issued yet) and read back two steps per lane, s and s + 64.
+    const int nb = (int)a.Nb, tt = (int)a.T;
+    const int j = (lane < a.k_eff) ? row[lane] : -1;
+    const bool valid = (unsigned)j < (unsigned)nb;
+    const uint64_t below = __ballot(valid) & ((1ull << lane) - 1);
+    const int pl = below ? 63 - __builtin_clzll(below) : lane;
+    const int jp = __shfl(j, pl);
+    const bool taken = valid && (pl == lane || jp != j);
+    const int lo = valid ? j * a.B : 0;
+    const int hi = (lo + a.B < tt) ? lo + a.B : tt;
+    const int ts = lo / kTileKeys;
+    const int c = taken ? (hi - 1) / kTileKeys + 1 - ts : 0;
+    const int incl = wave_inclusive_sum(c, lane);
+    const int n = __builtin_amdgcn_readlane(incl, 63);
+    uint2* sc = reinterpret_cast<uint2*>(ring[wave][1]);
+#pragma unroll
+    for (int x = 0; x < 128 / kTileKeys; ++x) {  // (B <= 128: at most 4 tiles per block)
+      if (x < c) {
+        const int t0 = (ts + x) * kTileKeys;
+        const int rl = (lo > t0) ? lo - t0 : 0;
+        const int rh = (hi < t0 + kTileKeys) ? hi - t0 : kTileKeys;
+        sc[incl - c + x] = make_uint2((uint32_t)(ts + x), (uint32_t)(rl | (rh << 8)));
+      }
+    }
+    const uint2 m0 = sc[lane], m1 = sc[64 + lane];
+    const int s_tile0 = (int)m0.x, s_range0 = (int)m0.y;
+    const int s_tile1 = (int)m1.x, s_range1 = (int)m1.y;
+    auto tile_of = [&](int t) {
+      return t < 64 ? __builtin_amdgcn_readlane(s_tile0, t)
+                    : __builtin_amdgcn_readlane(s_tile1, t - 64);
+    };
+    const uint32_t ring_lds = lds_address(ring[wave][0]);
+    if (n > 0) tile_to_lds(tiles + (int64_t)tile_of(0) * kRawTileBytes, ring[wave][0], lane);
+    if (n > 1) tile_to_lds(tiles + (int64_t)tile_of(1) * kRawTileBytes, ring[wave][1], lane);
+    if (n == 0) fetch_ocmp(q0);
+    for (int t = 0; t < n; ++t) {
+      const int slot = t & 1;
+      // tile t has landed once at most tile t + 1's copies are pending
+      if (t + 1 < n) wait_vmem<8>();
+      else wait_vmem<0>();
+      bf16x8 cur[8];
+      read_tile8(ring_lds + slot * kRawTileBytes + 16 * lane, cur);
+      if (t + 2 < n) {
+        // (the slot is free: read_tile8 waited for its reads)
+        tile_to_lds(tiles + (int64_t)tile_of(t + 2) * kRawTileBytes, ring[wave][slot], lane);
+      } else if (t + 1 == n) {
+        int64_t qq = q0;
+        asm volatile("" : "+s"(qq));
+        fetch_ocmp(qq);  // last tile: both slots are free once it is read
+      }
+      const int range = t < 64 ? __builtin_amdgcn_readlane(s_range0, t)
+                               : __builtin_amdgcn_readlane(s_range1, t - 64);
+      f.step(cur, qb, range & 0xFF, range >> 8, a.logit_mult, g);
+    }
+  } else {
   // cons: the tile being computed; prod: the next tile to request (kSelSlots ahead)
   SelIter cons{0, 0, sel_chunk(a, row, 0, lane), -1, 0, 0, 0, 0};
   bool cvalid = sel_next_block(a, row, lane, cons);
@@ -323,6 +404,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
     cons = nx;
     cvalid = nvalid;
   }
+  }
   wait_vmem<0>();  // O_cmp has landed
 
   float inv[NT];
@@ -349,275 +431,6 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
       w.y = float_to_in<kHalf>(g_cmp * oc.z + g_sel * s2) |
             ((uint32_t)float_to_in<kHalf>(g_cmp * oc.w + g_sel * s3) << 16);
       *reinterpret_cast<uint2*>(a.out + base) = w;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// Selection branch for B >= 64 (token indices below 2^31): one work-group of two waves per
-// (head, query block, 64-query part); wave w holds queries 32 w .. 32 w + 31 of the part (two
-// column tiles). Both waves walk the same selection row and share a ring of kSel2Ring tile
-// slots: wave w copies records 4 w .. 4 w + 3 of every tile (wave 0 the K records, wave 1 the
-// V^T records) and one barrier per tile publishes both halves. Per wave this needs half the
-// registers and a third less LDS than one wave per query block with a ring of its own, so
-// three waves share each SIMD instead of two, and the gathered tiles' latency is covered by
-// the other waves' tile steps.
-// ---------------------------------------------------------------------------------------
-constexpr int kSel2Ring = 3;   // tile slots per work-group: two tiles in flight, one computed
-constexpr int kSel2Ahead = kSel2Ring - 1;
-
-// Walks a selection row block by block, like SelIter, in 32-bit token arithmetic.
-struct Sel2Walk {
-  int idx;        // next position in the selection row
-  int base;       // first entry held in chunk
-  int32_t chunk;  // lane l: row[base + l] (-1 past the end)
-  int prev;       // last block taken
-  int tile, tile_end;
-  int lo, hi;     // token range of the current block
-};
-
-__device__ __forceinline__ bool sel2_next_block(const AttnArgs& a, const int32_t* row, int lane,
-                                                Sel2Walk& w) {
-  const int nb = (int)a.Nb, tt = (int)a.T;
-  while (w.idx < a.k_eff) {
-    if (w.idx >= w.base + 64) {
-      w.base += 64;
-      w.chunk = sel_chunk(a, row, w.base, lane);
-      wait_vmem<0>();  // here, so that the common path carries no pending load
-      asm volatile("" : "+v"(w.chunk));  // (later reads depend on this, not on the load)
-    }
-    const int j = __builtin_amdgcn_readlane(w.chunk, w.idx - w.base);
-    ++w.idx;
-    if ((unsigned)j >= (unsigned)nb || j == w.prev) continue;
-    w.prev = j;
-    w.lo = j * a.B;
-    w.hi = (w.lo + a.B < tt) ? w.lo + a.B : tt;
-    w.tile = w.lo / kTileKeys;
-    w.tile_end = (w.hi - 1) / kTileKeys + 1;
-    return true;
-  }
-  return false;
-}
-
-// The walk's next tile: its index and the range [lo, hi) of its keys inside the block, packed
-// as lo | hi << 8 (false once the row is exhausted).
-__device__ __forceinline__ bool sel2_next_tile(const AttnArgs& a, const int32_t* row, int lane,
-                                               Sel2Walk& w, bool first, int& tile, int& range) {
-  if (first || w.tile + 1 >= w.tile_end) {
-    if (!sel2_next_block(a, row, lane, w)) return false;
-  } else {
-    ++w.tile;
-  }
-  tile = w.tile;
-  const int t0 = w.tile * kTileKeys;
-  const int lo = (w.lo > t0) ? w.lo - t0 : 0;
-  const int hi = (w.hi < t0 + kTileKeys) ? w.hi - t0 : kTileKeys;
-  range = lo | (hi << 8);
-  return true;
-}
-
-// The eight 1 KB records of a tile slot (this lane's 16 bytes of each), read in one asm block
-// that waits for its own reads. Written as plain loads, the reads would be ordered behind
-// every global->LDS copy in flight (the compiler cannot tell that those fill other slots).
-__device__ __forceinline__ void read_tile8(uint32_t addr, bf16x8 (&r)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %8 offset:4096\n\t"
-      "ds_read_b128 %5, %8 offset:5120\n\t"
-      "ds_read_b128 %6, %8 offset:6144\n\t"
-      "ds_read_b128 %7, %8 offset:7168\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(addr)
-      : "memory");
-}
-
-// Work-group barrier with no memory fence. The loop below waits itself for what the barrier
-// must order (its own copies of the tile being published, and its reads of the slot about to
-// be refilled, which wait for themselves); a release fence on LDS would also wait for the
-// copies still in flight into the other slots.
-__device__ __forceinline__ void slot_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// kPre (rows of at most 64 tile steps): the step schedule is computed once, one step per lane
-// (tile index, and key range lo | hi << 8), and each step reads its entries with readlane;
-// otherwise the row is walked block by block as the steps are issued.
-template <bool kHalf, bool kPre>
-__global__ __launch_bounds__(128, 3) void sel2_kernel(AttnArgs a) {
-  constexpr int NT = 2;
-  constexpr int kTileU4 = kRawTileBytes / 16;
-  __shared__ uint4 ring[kSel2Ring][kTileU4];  // 24 KB
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int g = lane >> 4, li = lane & 15;
-  const int parts = a.B / 64;
-  const int64_t n_items = (int64_t)a.H * a.Nb * parts;
-  const int64_t item = xcd_logical_id(blockIdx.x, n_items);
-  if (item >= n_items) return;  // the whole work-group
-  const int part = (int)(item % parts);
-  const int64_t hi_ = item / parts;
-  const int h = (int)(hi_ / a.Nb);
-  const int64_t i = hi_ % a.Nb;
-  const int64_t q0 = i * a.B + 64 * part + 32 * wave;
-
-  bf16x8 qb[NT][2];
-  load_q<NT>(a, h, q0, g, li, qb);
-  const int32_t* row = a.sel + ((int64_t)h * a.Nb + i) * a.k_eff;
-  const unsigned char* tiles =
-      a.tiles + (int64_t)h * a.n_tiles * kRawTileBytes + (4 * wave) * kRecBytes + 16 * lane;
-
-  // this wave's four records of tile `tile` into slot `slot`
-  auto copy = [&](int tile, int slot) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      copy16_to_lds(tiles + (int64_t)tile * kRawTileBytes + x * kRecBytes,
-                    &ring[slot][(4 * wave + x) * 64]);
-  };
-  // O_cmp of this wave's queries for the gated epilogue, into a slot no tile uses any more:
-  // record nt * 4 + mt, lane li + 16 g = query 16 nt + li, dims 16 mt + 4 g .. + 3. Rows past
-  // the end read the last row (not used).
-  auto fetch_ocmp = [&](int slot) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      int64_t t = q0 + 16 * nt + li;
-      t = t < a.T ? t : a.T - 1;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        copy16_to_lds(a.o_cmp + (t * a.H + h) * kD + 16 * mt + 4 * g,
-                      &ring[slot][64 * (nt * 4 + mt)]);
-    }
-  };
-  static_assert(NT * 4 * kRecBytes <= kRawTileBytes, "O_cmp fits one slot");
-
-  const uint32_t ring_lds = lds_address(ring);
-  Flash<NT, kHalf> f;
-  f.init();
-  int oslot = wave;  // slot of this wave's O_cmp
-  if constexpr (kPre) {
-    // Lane e holds row entry e; an entry is taken if its block is valid and differs from the
-    // last valid entry before it (the walk's rule: a block repeated right away counts once).
-    const int nb = (int)a.Nb, tt = (int)a.T;
-    const int j = (lane < a.k_eff) ? row[lane] : -1;
-    const bool valid = (unsigned)j < (unsigned)nb;
-    const uint64_t below = __ballot(valid) & ((1ull << lane) - 1);
-    const int pl = below ? 63 - __builtin_clzll(below) : lane;
-    const int jp = __shfl(j, pl);
-    const bool taken = valid && (pl == lane || jp != j);
-    const int lo = valid ? j * a.B : 0;
-    const int hi = (lo + a.B < tt) ? lo + a.B : tt;
-    const int ts = lo / kTileKeys;
-    const int c = taken ? (hi - 1) / kTileKeys + 1 - ts : 0;
-    const int incl = wave_inclusive_sum(c, lane);
-    const int n = __builtin_amdgcn_readlane(incl, 63);
-    // entry e's tiles become steps incl - c .. incl - 1: scattered through this wave's part
-    // of the last slot (no copy has been issued yet), then read back one step per lane
-    uint2* sc = reinterpret_cast<uint2*>(&ring[kSel2Ring - 1][wave * 64]);
-#pragma unroll
-    for (int x = 0; x < 128 / kTileKeys; ++x) {  // (B <= 128: at most 4 tiles per block)
-      if (x < c) {
-        const int t0 = (ts + x) * kTileKeys;
-        const int rl = (lo > t0) ? lo - t0 : 0;
-        const int rh = (hi < t0 + kTileKeys) ? hi - t0 : kTileKeys;
-        sc[incl - c + x] = make_uint2((uint32_t)(ts + x), (uint32_t)(rl | (rh << 8)));
-      }
-    }
-    const uint2 mine = sc[lane];
-    const int s_tile = (int)mine.x, s_range = (int)mine.y;
-    if (n > 0) copy(__builtin_amdgcn_readlane(s_tile, 0), 0);
-    if (n > 1) copy(__builtin_amdgcn_readlane(s_tile, 1), 1);
-    if (n == 0) fetch_ocmp(oslot);  // no tiles: every slot is free
-    int slot = 0;
-    for (int t = 0; t < n; ++t) {
-      // tile t has landed (this wave's half) once at most tile t + 1's copies are pending
-      if (t + 1 < n) wait_vmem<4>();
-      else wait_vmem<0>();
-      slot_barrier();  // both halves of tile t are visible; both waves are done with t - 1
-      bf16x8 cur[8];
-      read_tile8(ring_lds + slot * kRawTileBytes + 16 * lane, cur);
-      const int free1 = (slot + 1 == kSel2Ring) ? 0 : slot + 1;    // tile t + 1's slot
-      const int free2 = (free1 + 1 == kSel2Ring) ? 0 : free1 + 1;  // tile t - 1's slot
-      if (t + 2 < n) {
-        copy(__builtin_amdgcn_readlane(s_tile, t + 2), free2);
-      } else if (t + 1 == n) {
-        oslot = (wave == 0) ? free1 : free2;  // last tile: the other two slots are free
-        fetch_ocmp(oslot);
-      }
-      const int range = __builtin_amdgcn_readlane(s_range, t);
-      f.step(cur, qb, range & 0xFF, range >> 8, a.logit_mult, g);
-      slot = free1;
-    }
-  } else {
-  // tiles t, t + 1, t + 2 of the walk: index and key range (d0 is computed, d1 and d2 in flight)
-  Sel2Walk w{0, 0, sel_chunk(a, row, 0, lane), -1, 0, 0, 0, 0};
-  wait_vmem<0>();
-  asm volatile("" : "+v"(w.chunk));  // (later reads depend on this, not on the load)
-  int t0i = 0, t0r = 0, t1i = 0, t1r = 0, t2i = 0, t2r = 0;
-  bool v0 = sel2_next_tile(a, row, lane, w, true, t0i, t0r);
-  bool v1 = v0 && sel2_next_tile(a, row, lane, w, false, t1i, t1r);
-  int issued = 0;
-  if (v0) { copy(t0i, 0); ++issued; }
-  if (v1) { copy(t1i, 1); ++issued; }
-  if (!v0) fetch_ocmp(oslot);  // no tiles: every slot is free
-  int slot = 0;
-  for (int t = 0; v0; ++t) {
-    // tile t has landed (this wave's half) once at most the copies issued after it are pending
-    if (issued > t + 1) wait_vmem<4>();
-    else wait_vmem<0>();
-    slot_barrier();  // both halves of tile t are visible; both waves are done with tile t - 1
-    bf16x8 cur[8];
-    read_tile8(ring_lds + slot * kRawTileBytes + 16 * lane, cur);
-    const int free1 = (slot + 1 == kSel2Ring) ? 0 : slot + 1;  // tile t + 1's slot
-    const int free2 = (free1 + 1 == kSel2Ring) ? 0 : free1 + 1;  // tile t - 1's slot
-    bool v2 = false;
-    if (v1) {
-      v2 = sel2_next_tile(a, row, lane, w, false, t2i, t2r);
-      if (v2) {
-        copy(t2i, free2);  // tile t - 1's slot, read by both waves before the barrier
-        ++issued;
-      }
-    } else {
-      // last tile: the other two slots are free (tile t - 1's was read before the barrier,
-      // and no tile follows into tile t + 1's)
-      oslot = (wave == 0) ? free1 : free2;
-      fetch_ocmp(oslot);
-    }
-    f.step(cur, qb, t0r & 0xFF, t0r >> 8, a.logit_mult, g);
-    t0r = t1r; v0 = v1;
-    t1i = t2i; t1r = t2r; v1 = v2;
-    slot = free1;
-  }
-  }
-  wait_vmem<0>();  // O_cmp has landed (each wave reads only its own copy)
-  const uint4* cmp_lds = ring[oslot];
-
-  float inv[NT];
-  f.finish(inv, a.v_unscale);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int64_t t = q0 + 16 * nt + li;
-    if (t >= a.T || 16 * nt + li + 32 * wave + 64 * part >= a.B) continue;
-    if (a.lse_sel && g == 0)  // saved for the backward pass
-      a.lse_sel[(int64_t)h * a.T + t] =
-          (f.l[nt][0] > 0.f) ? f.m[nt] + __log2f(f.l[nt][0]) : INFINITY;
-    const float* gp = a.gates + t * a.gate_st + (int64_t)h * 2;
-    const float g_cmp = gp[0], g_sel = gp[1];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int64_t base = (t * a.H + h) * kD + 16 * mt + 4 * g;
-      const float4 oc = __builtin_bit_cast(float4, cmp_lds[64 * (nt * 4 + mt) + lane]);
-      const float s0 = f.o[mt][nt][0] * inv[nt], s1 = f.o[mt][nt][1] * inv[nt];
-      const float s2 = f.o[mt][nt][2] * inv[nt], s3 = f.o[mt][nt][3] * inv[nt];
-      if (a.o_sel) *reinterpret_cast<float4*>(a.o_sel + base) = make_float4(s0, s1, s2, s3);
-      uint2 wv;
-      wv.x = float_to_in<kHalf>(g_cmp * oc.x + g_sel * s0) |
-             ((uint32_t)float_to_in<kHalf>(g_cmp * oc.y + g_sel * s1) << 16);
-      wv.y = float_to_in<kHalf>(g_cmp * oc.z + g_sel * s2) |
-             ((uint32_t)float_to_in<kHalf>(g_cmp * oc.w + g_sel * s3) << 16);
-      *reinterpret_cast<uint2*>(a.out + base) = wv;
     }
   }
 }
@@ -689,36 +502,31 @@ __global__ __launch_bounds__(256) void dense_kernel(AttnArgs a) {
 }
 
 hipError_t launch_sel(const AttnArgs& a, hipStream_t s) {
-  if (a.B >= 64 && a.T + a.B < ((int64_t)1 << 31)) {
-    const int64_t n_items = (int64_t)a.H * a.Nb * (a.B / 64);
-    const dim3 g3((unsigned)(((n_items + 7) / 8) * 8)), b3(128);
-    if ((int64_t)a.k_eff * (a.B / kTileKeys) <= 64) {  // every row fits one step per lane
-      if (a.half) hipLaunchKernelGGL((sel2_kernel<true, true>), g3, b3, 0, s, a);
-      else hipLaunchKernelGGL((sel2_kernel<false, true>), g3, b3, 0, s, a);
-    } else {
-      if (a.half) hipLaunchKernelGGL((sel2_kernel<true, false>), g3, b3, 0, s, a);
-      else hipLaunchKernelGGL((sel2_kernel<false, false>), g3, b3, 0, s, a);
-    }
-    return hipGetLastError();
-  }
   const int parts = (a.B > 64) ? a.B / 64 : 1;
   const int64_t n_items = (int64_t)a.H * a.Nb * parts;
   const int64_t n_wg = (n_items + 3) / 4;
   const dim3 g3((unsigned)(((n_wg + 7) / 8) * 8)), b3(256);
+  // the step schedule in registers: rows of at most 64 entries and 128 tile steps, token
+  // indices below 2^31
+  const int tiles_per_block = a.B > kTileKeys ? a.B / kTileKeys : 1;
+  const bool pre = a.k_eff <= 64 && (int64_t)a.k_eff * tiles_per_block <= 128 &&
+                   a.T + a.B < ((int64_t)1 << 31);
+#define S3R_SEL(NT)                                                                        \
+  do {                                                                                      \
+    if (pre) {                                                                              \
+      if (a.half) hipLaunchKernelGGL((sel_kernel<NT, true, true>), g3, b3, 0, s, a);        \
+      else hipLaunchKernelGGL((sel_kernel<NT, false, true>), g3, b3, 0, s, a);              \
+    } else {                                                                                \
+      if (a.half) hipLaunchKernelGGL((sel_kernel<NT, true, false>), g3, b3, 0, s, a);       \
+      else hipLaunchKernelGGL((sel_kernel<NT, false, false>), g3, b3, 0, s, a);             \
+    }                                                                                       \
+  } while (0)
   switch (a.B) {
-    case 16:
-      if (a.half) hipLaunchKernelGGL((sel_kernel<1, true>), g3, b3, 0, s, a);
-      else hipLaunchKernelGGL((sel_kernel<1, false>), g3, b3, 0, s, a);
-      break;
-    case 32:
-      if (a.half) hipLaunchKernelGGL((sel_kernel<2, true>), g3, b3, 0, s, a);
-      else hipLaunchKernelGGL((sel_kernel<2, false>), g3, b3, 0, s, a);
-      break;
-    default:
-      if (a.half) hipLaunchKernelGGL((sel_kernel<4, true>), g3, b3, 0, s, a);
-      else hipLaunchKernelGGL((sel_kernel<4, false>), g3, b3, 0, s, a);
-      break;
+    case 16: S3R_SEL(1); break;
+    case 32: S3R_SEL(2); break;
+    default: S3R_SEL(4); break;
   }
+#undef S3R_SEL
   return hipGetLastError();
 }
 
