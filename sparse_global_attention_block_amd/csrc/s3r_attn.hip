@@ -182,7 +182,9 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int h, int64_t q0, int
 // gathered from all over the key sequence, so each costs a full memory latency: the wave
 // keeps two tiles in flight, copied from global memory straight into two LDS slots of its own
 // (no registers held while in flight), and computes on a third, read from its slot into
-// registers just before the slot is refilled.
+// registers just before the slot is refilled. Rows of at most 64 entries and 128 tile steps
+// (kPre) get their step schedule built once at the start, one step per lane, and each step
+// reads its tile with readlane; longer rows are walked block by block (SelIter).
 // ---------------------------------------------------------------------------------------
 // Walks a selection row block by block and tile by tile. The row is held 64 entries at a time
 // in one register (lane l: entry base + l) and read with readlane, so that walking it issues
@@ -330,6 +332,7 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
     const uint2 m0 = sc[lane], m1 = sc[64 + lane];
     const int s_tile0 = (int)m0.x, s_range0 = (int)m0.y;
     const int s_tile1 = (int)m1.x, s_range1 = (int)m1.y;
+    wait_lds();  // both reads are done before tile 1 is copied over the scratch
     auto tile_of = [&](int t) {
       return t < 64 ? __builtin_amdgcn_readlane(s_tile0, t)
                     : __builtin_amdgcn_readlane(s_tile1, t - 64);
