@@ -236,27 +236,6 @@ __device__ __forceinline__ bool sel_advance(const AttnArgs& a, const int32_t* ro
 
 constexpr int kSelSlots = 2;  // tiles in flight per wave (the vmcnt waits below assume 2)
 
-// The eight 1 KB records of a tile slot (this lane's 16 bytes of each), read in one asm block
-// that waits for its own reads. Written as plain loads, the reads would be ordered behind
-// every global->LDS copy in flight (the compiler cannot tell that those fill other slots).
-__device__ __forceinline__ void read_tile8(uint32_t addr, bf16x8 (&r)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %8 offset:4096\n\t"
-      "ds_read_b128 %5, %8 offset:5120\n\t"
-      "ds_read_b128 %6, %8 offset:6144\n\t"
-      "ds_read_b128 %7, %8 offset:7168\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(addr)
-      : "memory");
-}
-
-
 template <int NT, bool kHalf, bool kPre = false>
 __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
   __shared__ uint4 ring[4][kSelSlots][kRawTileBytes / 16];  // 16 KB per wave
@@ -337,7 +316,6 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
       return t < 64 ? __builtin_amdgcn_readlane(s_tile0, t)
                     : __builtin_amdgcn_readlane(s_tile1, t - 64);
     };
-    const uint32_t ring_lds = lds_address(ring[wave][0]);
     if (n > 0) tile_to_lds(tiles + (int64_t)tile_of(0) * kRawTileBytes, ring[wave][0], lane);
     if (n > 1) tile_to_lds(tiles + (int64_t)tile_of(1) * kRawTileBytes, ring[wave][1], lane);
     if (n == 0) fetch_ocmp(q0);
@@ -346,10 +324,13 @@ __global__ __launch_bounds__(256) void sel_kernel(AttnArgs a) {
       // tile t has landed once at most tile t + 1's copies are pending
       if (t + 1 < n) wait_vmem<8>();
       else wait_vmem<0>();
+      // (after the explicit wait above the compiler orders these reads behind nothing else)
       bf16x8 cur[8];
-      read_tile8(ring_lds + slot * kRawTileBytes + 16 * lane, cur);
+      const bf16x8* L = reinterpret_cast<const bf16x8*>(ring[wave][slot]);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) cur[x] = L[x * 64 + lane];
       if (t + 2 < n) {
-        // (the slot is free: read_tile8 waited for its reads)
+        wait_lds();  // the slot is read before the next tile overwrites it
         tile_to_lds(tiles + (int64_t)tile_of(t + 2) * kRawTileBytes, ring[wave][slot], lane);
       } else if (t + 1 == n) {
         int64_t qq = q0;
