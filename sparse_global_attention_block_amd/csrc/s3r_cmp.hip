@@ -55,8 +55,9 @@ constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 // kBound with kFused (and kTopk): the single pass (above). kBound without kFused: the bound
 // pass, pass 1 over the group keys on their hi parts alone (half the MFMAs and half the
 // records): its result need not be exact, only low enough, which the single pass checks.
-// kDeep: tiles in flight for the exact reruns after the single pass, where a few lone
-// work-groups sweep all tiles and the latency of each copy, not the chip's throughput, decides.
+// kDeep: tiles in flight for the exact reruns after the single pass, where few work-groups
+// (at 1000 views, 16 heads: about 16 of 343,500 waves flagged at k = 16, 3% at k = 32) sweep
+// all tiles and the latency of each copy, not the chip's throughput, decides.
 // kScoresOnly (rerun of pass 2 with the running top-k where only the single pass's selection
 // was not proven: its O_cmp stands): no V^T records, no P.V, no O_cmp write.
 template <bool kFused, int kQB, int kWaves, bool kTopk = false, bool kHalf = false,
@@ -83,12 +84,22 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
 
   const int64_t n_qtiles = (a.T + kQueries - 1) / kQueries;
   const int64_t total = (int64_t)a.H * n_qtiles;
-  const int64_t logical = xcd_logical_id(blockIdx.x, total);
+  // (reruns: logical id = block id, so that the dispatcher deals the flagged work-groups,
+  // which cluster where block scores are close, round-robin over the XCDs, not onto a few)
+  const int64_t logical = kDeep ? (int64_t)blockIdx.x : xcd_logical_id(blockIdx.x, total);
   if (logical >= total) return;
+  // (scores-only rerun) a wave whose own selection the single pass proved only copies its
+  // share of each tile: no logits, no list, no write (its rows stand)
+  bool idle = false;
   if (a.redo_in) {  // exact rerun of the work-groups the single pass flagged
     const int4 f = *reinterpret_cast<const int4*>(a.redo_in + 4 * logical);
     const int any = f.x | f.y | f.z | f.w;
     if ((any & a.redo_mask) == 0 || (any & a.redo_skip) != 0) return;
+    if constexpr (kScoresOnly) {
+      const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+      const int mine = w == 0 ? f.x : (w == 1 ? f.y : (w == 2 ? f.z : f.w));
+      idle = (mine & a.redo_mask) == 0;
+    }
   }
   const int h = (int)(logical / n_qtiles);
   const int64_t qt = logical % n_qtiles;
@@ -479,17 +490,20 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   for (int64_t tau = 0; tau + 1 < n; ++tau) {
     copy(tau + kAhead < n ? tau + kAhead : n - 1, (int)((tau + kAhead) % kRing));
     const uint4* L = lds[(int)(tau % kRing)];
-    qk(L, acc);
-    process(tau, L, acc, false);
+    if (!(kScoresOnly && idle)) {
+      qk(L, acc);
+      process(tau, L, acc, false);
+    }
     wait_vmem<(kAhead - 1) * kRecsPerWave>();
     lds_barrier();
   }
-  {
+  if (!(kScoresOnly && idle)) {
     const uint4* L = lds[(int)((n - 1) % kRing)];
     qk(L, acc);
     process(n - 1, L, acc, true);
   }
   wait_vmem<0>();  // no copy outlives the work-group
+  if (kScoresOnly && idle) return;
 
   if constexpr (!kFused) {
     // combine the four lane groups of each query: offsets and partial sums
