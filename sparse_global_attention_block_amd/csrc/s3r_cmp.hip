@@ -31,8 +31,10 @@
 // One sweep accumulates O_cmp * Z_t and Z_t = sum_j u_tj, and per key block the upper bound
 // sum_t u_tj of its score; a running list keeps the 64 blocks of largest bound. At the end
 // L_t = L'_t + log2 Z_t, O_cmp = O / Z, and the listed blocks are rescored exactly (their
-// logits recomputed on the same MFMA sequence) and ranked. A wave whose Z_t leave [1, 2^15] or
-// whose list cannot prove the top k (its last bound not below the k-th score) sets a redo flag;
+// logits recomputed on the same MFMA sequence) and ranked. Since P_tj = u_tj / Z_t, an unlisted
+// block's score is at most its bound over the query block's smallest Z_t. A wave whose Z_t
+// leave [1, 2^15] or whose list cannot prove the top k (its last bound, over that Z_t, not
+// below the k-th score) sets a redo flag;
 // the exact passes rerun only on the flagged work-groups (kDeep, kScoresOnly), so the outputs
 // are those of the two passes up to rounding.
 #include "s3r_common.hpp"
@@ -398,8 +400,9 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
   // the blocks' pooled keys are gathered 16 at a time into this wave's LDS records R and meet
   // the resident queries in the same MFMA sequence as in the pass, so every logit is the
   // pass's own. The k best by (score desc, index asc) are kept if the largest upper bound of
-  // a block outside the list stays below the k-th score; otherwise `fail` is set.
-  auto rescore = [&](int qi, const float (&L2)[4], uint4* R, bool& fail) {
+  // a block outside the list, over the query block's smallest Z_t, stays below the k-th
+  // score; otherwise `fail` is set. zq: Z_t of this lane's queries (+inf past the end).
+  auto rescore = [&](int qi, const float (&L2)[4], const float (&zq)[4], uint4* R, bool& fail) {
     // (a list short of entries, from non-finite bounds, has also failed the Z check)
     const int64_t qblk = (q0 + 16 * qi * kNtPerQB) / a.B;
     if (qblk >= a.Nb) return;
@@ -471,9 +474,21 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     // reduction), 6 * 2^-11 < 2^-8 in all, and the at most 136 roundings of values below 2^-14
     // add at most 2^-25 each, < 2^-17 in all (fp16 subnormals are kept: the kernels run with
     // f16 denormals on, the compiler's default; flushing them would cost up to 2^-14 each).
+    // So a block's sum of weights sum_t w_tj is at most its bound * (1 + 2^-8) + 2^-17, and
+    // its exact score sum_t 2^(c_tj - L_t) = sum_t w_tj / Z_t is at most that sum over the
+    // smallest Z_t of the query block's queries (the bound itself carries every Z_t >= 1).
+    // The f32 roundings of the scores, of log2 Z_t and of this division add far less than
+    // 2^-10 relative (for exponents below 2^10 in magnitude), the room 2^-8 leaves over
+    // 6 * 2^-11.
+    float zmin = zq[qi * kNtPerQB];
+#pragma unroll
+    for (int nt = qi * kNtPerQB + 1; nt < (qi + 1) * kNtPerQB; ++nt) zmin = fminf(zmin, zq[nt]);
+#pragma unroll
+    for (int sh = 1; sh < 16; sh *= 2) zmin = fminf(zmin, __shfl_xor(zmin, sh));
+    zmin = fminf(fmaxf(zmin, 1.0f), 0x1p15f);  // (outside [1, 2^15] the Z check fails anyway)
     const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
     const float rmax = nc <= Kc ? -1.0f : th_v[qi];
-    fail |= !(at != 0 && (rmax < 0.f || rmax * (1.0f + 0x1p-8f) + 0x1p-17f < sk));
+    fail |= !(at != 0 && (rmax < 0.f || (rmax * (1.0f + 0x1p-8f) + 0x1p-17f) / zmin < sk));
     tk_j[qi] = __builtin_amdgcn_ds_permute(4 * rank, j);  // entry of exact rank e to lane e
   };
 
@@ -534,13 +549,14 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       // rerun); one whose selection is not proven fails with bit 0 (only the second reruns:
       // its L_t are exact).
       bool zfail = false, fail = false;
-      float L2[4];
+      float L2[4], zq[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float z = zpart[wave][lane][nt];
         z += __shfl_xor(z, 16);
         z += __shfl_xor(z, 32);
         const int64_t t = q0 + 16 * nt + li;
+        zq[nt] = t < a.T ? z : INFINITY;
         zfail |= t < a.T && !(z >= 1.0f && z <= 0x1p15f);
         L2[nt] = (t < a.T && z > 0.f) ? off[nt] + __log2f(z) : INFINITY;
         zinv[nt] = z > 0.f ? a.v_unscale / z : 0.f;
@@ -550,7 +566,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
       static_assert(kRing * kRecs * 64 / kWaves >= 4 * 64, "four records per wave");
       uint4* R = &lds[0][0] + wave * (kRing * kRecs * 64 / kWaves);
 #pragma unroll
-      for (int qi = 0; qi < kQB; ++qi) rescore(qi, L2, R, fail);
+      for (int qi = 0; qi < kQB; ++qi) rescore(qi, L2, zq, R, fail);
       const int flag = (__any(zfail) ? 2 : 0) | (__any(fail) ? 1 : 0);
       if (lane == 0) a.redo_out[4 * logical + wave] = flag;
     }
