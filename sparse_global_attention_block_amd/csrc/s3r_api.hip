@@ -90,12 +90,12 @@ s3r_status check_params(const s3r_params* p, Dims* d) {
   d->n_redo = (int64_t)d->H * ((d->T + 255) / 256) * 4;
   d->single_ok = d->fold_topk && d->Nb_g >= 1;
   // automatic: the single pass where its list of 64 bound-ranked candidates holds every
-  // candidate or at least 2k of them. At 1000 views (21,469 blocks) its check fails on 0.005 %
-  // of the waves for k = 16, 3 % for k = 32 (still 47 ms faster than two passes), 18 % for
-  // k = 40 (even) and 52 % for k = 48 (54 ms slower).
+  // candidate or at least 4k/3 of them (k <= 48). At 1000 views (21,469 blocks) its check
+  // fails on no wave for k = 16, 0.2 % for k = 32, 3 % for k = 40 (62 ms faster than two
+  // passes), 23 % for k = 48 (32 ms faster) and 74 % for k = 56 (20 ms slower).
   d->single = d->single_ok && (p->cmp_mode == S3R_CMP_SINGLE ||
                                (p->cmp_mode == S3R_CMP_AUTO &&
-                                (2 * most <= kFusedTopkMaxK || d->Nb - d->forced <= 64)));
+                                (4 * most <= 3 * kFusedTopkMaxK || d->Nb - d->forced <= 64)));
   // the separate top-k kernel's exact tie search indexes a row with 16 bits and the score
   // matrix grows as Nb^2; the folded selection has no limit
   if (!d->fold_topk && d->Nb > kMaxBlocks) return S3R_ERR_UNSUPPORTED;

@@ -205,7 +205,7 @@ def dense_workspace_size(p: Params) -> int:
 def runs_single(p: Params) -> bool:
     """Whether the forward pass with these params runs the single compression pass: CMP_SINGLE,
     or CMP_AUTO where the single pass applies (B <= 64, at most 64 chosen blocks, Nb >= 8) and
-    k <= 32 or at most 64 candidate blocks (the rule the library applies, include/speed3r.h)."""
+    k <= 48 or at most 64 candidate blocks (the rule the library applies, include/speed3r.h)."""
     Nb = num_blocks(p)
     if Nb < 0:
         raise ValueError("invalid params")
@@ -214,7 +214,7 @@ def runs_single(p: Params) -> bool:
     ok = p.block <= 64 and most <= 64 and Nb >= 8
     if p.cmp_mode == CMP_SINGLE:
         return ok
-    return ok and p.cmp_mode == CMP_AUTO and (2 * most <= 64 or Nb - forced <= 64)
+    return ok and p.cmp_mode == CMP_AUTO and (4 * most <= 3 * 64 or Nb - forced <= 64)
 
 
 def _need(cond: bool, msg: str):

@@ -272,11 +272,11 @@ def test_single_pass_limits():
     # the forward workspace holds the redo flags only when the single pass runs
     two = S.workspace_size(params(T=1_374_000, H=16, B=64, k=16, mode=S.CMP_TWO_PASS))
     assert S.workspace_size(big_p) == two + S.redo_flag_count(big_p) * 4
-    # automatic mode: the single pass for k <= 32 or when every candidate fits the list of 64
-    assert S.workspace_size(params(T=1_374_000, H=16, B=64, k=33)) == S.workspace_size(
-        params(T=1_374_000, H=16, B=64, k=33, mode=S.CMP_TWO_PASS))
-    assert S.workspace_size(params(T=1_374_000, H=16, B=64, k=32)) > S.workspace_size(
-        params(T=1_374_000, H=16, B=64, k=32, mode=S.CMP_TWO_PASS))
+    # automatic mode: the single pass for k <= 48 or when every candidate fits the list of 64
+    assert S.workspace_size(params(T=1_374_000, H=16, B=64, k=49)) == S.workspace_size(
+        params(T=1_374_000, H=16, B=64, k=49, mode=S.CMP_TWO_PASS))
+    assert S.workspace_size(params(T=1_374_000, H=16, B=64, k=48)) > S.workspace_size(
+        params(T=1_374_000, H=16, B=64, k=48, mode=S.CMP_TWO_PASS))
     assert S.workspace_size(params(T=60 * 64, B=64, k=40)) > S.workspace_size(
         params(T=60 * 64, B=64, k=40, mode=S.CMP_TWO_PASS))
 
@@ -314,6 +314,7 @@ def test_training_entry_points_validate_before_launching():
 
 @pytest.mark.parametrize("T,B,k,F,own", [
     (1_374_000, 64, 16, 0, 0), (1_374_000, 64, 32, 0, 0), (1_374_000, 64, 33, 22, 1),
+    (1_374_000, 64, 48, 0, 0), (1_374_000, 64, 49, 0, 0), (1_374_000, 64, 49, 2, 1),
     (60 * 64, 64, 30, 0, 0), (7 * 16, 16, 4, 0, 0), (8 * 16, 16, 4, 0, 0), (4096, 128, 4, 0, 0),
     (100 * 64, 64, 65, 0, 0), (100 * 64, 64, 30, 40, 0), (1000, 32, 5, 3, 1),
 ])
