@@ -511,6 +511,9 @@ def run_table(args, dev):
             return f"{kk[key]:.0f} ({kk['frac']:.0%})"
         return f"{kk['achieved']:.0f} ({kk['frac']:.0%} / {kk['frac_executed']:.0%})"
 
+    def opt(v):  # a figure only some configurations have (the dense comparator's)
+        return "—" if v is None else f"{v:.1f}"
+
     lines = ["| config | T | k | t_sparse (ms) | tokens/s | pool+pack GB/s (%HBM) | "
              "cmp TF/s (%MFMA alg / exec) | sel TF/s (%MFMA alg / exec) | t_dense (ms) | "
              "x vs dense | rows checked / identical sel / exact rule | max-abs / mean-abs |",
@@ -521,8 +524,7 @@ def run_table(args, dev):
         lines.append(
             f"| {r['workload']} | {r['T']:,} | {r['topk']} | {r['ms']:.3f} | "
             f"{r['tokens_per_s']:.3e} | {g(r, 'pool')} | {g(r, cmp)} | {g(r, 'sel')} | "
-            f"{r.get('dense_ms', float('nan')):.1f} | "
-            f"{r.get('x_vs_dense', float('nan')):.1f} | {p['rows']} / "
+            f"{opt(r.get('dense_ms'))} | {opt(r.get('x_vs_dense'))} | {p['rows']} / "
             f"{p['rows_same_selection']:.1%} / {p['rows_exact_rule']:.1%} | "
             f"{p['out_max_abs']:.2e} / {p['out_mean_abs']:.2e} |")
     log("\n".join(lines))
