@@ -110,6 +110,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("v100", 100, 1374, 5, 16, 64, 16, "structured", seed=100, special_mult=3.0),
     Workload("v1000_k16", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000, special_mult=3.0),
     Workload("v1000_k32", 1000, 1374, 5, 16, 64, 32, "structured", seed=1000, special_mult=3.0),
+    # k = 48: the largest k for which the automatic mode takes the single compression pass
+    Workload("v1000_k48", 1000, 1374, 5, 16, 64, 48, "structured", seed=1000, special_mult=3.0),
     # same as v1000_k16, with the 22 key blocks that cover the first (reference) view attended
     # by every query block in addition to its top-16
     Workload("v1000_k16_ref", 1000, 1374, 5, 16, 64, 16, "structured", seed=1000,

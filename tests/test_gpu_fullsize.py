@@ -2,7 +2,8 @@
 through speed3r_sparse_attn_fwd exactly as the benchmark launches it. The oracle recomputes a
 sample of (head, query block) rows one by one, stratified: the first block, the short last
 block, blocks holding a view's special tokens (the heavy-hitter keys) and random blocks. At
-1000 views, k = 16 and k = 32, 512 rows over 4 heads."""
+1000 views, k = 16 and k = 32, 512 rows over 4 heads; k = 48 (where the automatic mode still
+takes the single compression pass, with reruns), 56 rows over 2 heads."""
 import numpy as np
 import pytest
 import torch
@@ -34,6 +35,7 @@ FULLSIZE = {
     "v100": ((0, 15), 6, 2),
     "v1000_k16": ((0, 5, 10, 15), 94, 32),
     "v1000_k32": ((0, 5, 10, 15), 94, 32),
+    "v1000_k48": ((0, 15), 20, 6),
     "v1000_k16_ref": ((0, 15), 6, 2),
     "v1000_k16_ref_own": ((0, 15), 6, 2),
     "v1000_k16_fp16": ((0, 7, 15), 20, 6),
