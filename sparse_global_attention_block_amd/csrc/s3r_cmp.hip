@@ -58,7 +58,7 @@ constexpr int kFusedAhead = 1;  // tiles in flight, pass 2
 // pass, pass 1 over the group keys on their hi parts alone (half the MFMAs and half the
 // records): its result need not be exact, only low enough, which the single pass checks.
 // kDeep: tiles in flight for the exact reruns after the single pass, where few work-groups
-// (at 1000 views, 16 heads: about 16 of 343,500 waves flagged at k = 16, 3% at k = 32) sweep
+// (at 1000 views, 16 heads: none of 343,500 waves flagged at k = 16, 0.2 % at k = 32) sweep
 // all tiles and the latency of each copy, not the chip's throughput, decides.
 // kScoresOnly (rerun of pass 2 with the running top-k where only the single pass's selection
 // was not proven: its O_cmp stands): no V^T records, no P.V, no O_cmp write.
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     // f16 denormals on, the compiler's default; flushing them would cost up to 2^-14 each).
     // So a block's sum of weights sum_t w_tj is at most its bound * (1 + 2^-8) + 2^-17, and
     // its exact score sum_t 2^(c_tj - L_t) = sum_t w_tj / Z_t is at most that sum over the
-    // smallest Z_t of the query block's queries (the bound itself carries every Z_t >= 1).
+    // smallest Z_t of the query block's queries.
     // The f32 roundings of the scores, of log2 Z_t and of this division add far less than
     // 2^-10 relative (for exponents below 2^10 in magnitude), the room 2^-8 leaves over
     // 6 * 2^-11.
@@ -485,7 +485,8 @@ __global__ __launch_bounds__(64 * kWaves, kFused ? 3 : 4) void cmp_kernel(CmpArg
     for (int nt = qi * kNtPerQB + 1; nt < (qi + 1) * kNtPerQB; ++nt) zmin = fminf(zmin, zq[nt]);
 #pragma unroll
     for (int sh = 1; sh < 16; sh *= 2) zmin = fminf(zmin, __shfl_xor(zmin, sh));
-    zmin = fminf(fmaxf(zmin, 1.0f), 0x1p15f);  // (outside [1, 2^15] the Z check fails anyway)
+    // (a Z_t outside [1, 2^15] fails the Z check, whose full rerun replaces this wave's results)
+    zmin = fminf(fmaxf(zmin, 1.0f), 0x1p15f);
     const int64_t nc = a.Nb - a.forced - (own ? 1 : 0);
     const float rmax = nc <= Kc ? -1.0f : th_v[qi];
     fail |= !(at != 0 && (rmax < 0.f || (rmax * (1.0f + 0x1p-8f) + 0x1p-17f) / zmin < sk));
