@@ -43,6 +43,10 @@ CASES = {
     # so more query blocks fail the check, and work-groups rerun with some waves idle
     "v14_k32": (dataclasses.replace(_v8, name="v14_k32", H=2, topk=32), 14 * 1374),
     "v14_k48": (dataclasses.replace(_v8, name="v14_k48", H=2, topk=48), 14 * 1374),
+    # large k with several query blocks per wave (each with its own smallest Z_t, and reruns
+    # of waves that hold four or two query blocks)
+    "b16_k40": (dataclasses.replace(_tiny_s, name="b16_k40", H=1, block=16, topk=40), 3000),
+    "b32_k48": (dataclasses.replace(_tiny_s, name="b32_k48", H=2, block=32, topk=48), 3000),
     # exactly one group of 8 blocks
     "one_group": (dataclasses.replace(_tiny_s, name="one_group", H=2, block=64, topk=3), 8 * 64),
 }
@@ -198,7 +202,7 @@ def test_uneven_bound(name):
     print(f"[{name}] waves redone: {int((host(st.redo) != 0).sum())}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["v14", "v14_k32", "b32_ragged"])
+@pytest.mark.parametrize("name", ["v14", "v14_k32", "b32_ragged", "b32_k48"])
 def test_rerun_with_proven_waves_in_the_work_group(name):
     """Work-groups where only some waves failed the selection check. The bound is lowered by
     6 for every other query of waves 0 and 2 of every work-group of 256 queries: the Z_t of
